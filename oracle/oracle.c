@@ -1,0 +1,422 @@
+/*
+ * oracle.c -- plain, slow CPU reference of the routed-expert path of one MoE layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link, load or
+ * call this file.  It exists so that tests, the smoke check and the CPU-baseline leg of
+ * the benchmark can check the GPU library against an independent implementation.  It
+ * shares no code, header, table or helper with the HIP library.
+ *
+ * Every step is the plain definition of what the path computes, written as loops in the
+ * order the source pages state them.  Floating point is accumulated in double; the two
+ * rounding points that the bf16 path has (the SwiGLU activation and the expert output,
+ * plus the final combined output) round the double result to bf16, nearest-even.
+ *
+ * Sources (the pages' titles and the parts used):
+ *   [MF]   "MegaFlux: Skew-Resilient MoE Megakernels via Pipelined Expert Replication":
+ *          §1 (router picks k experts, outputs combined by routing weights),
+ *          §2.1 (FC1 -> FC2 SwiGLU experts; the final top-k sum is its own launch),
+ *          §3.1 (blocks of at most beta rows; stable order inside each expert),
+ *          §4.1 (beta = 128, SwiGLU, FP32 accumulation with BF16 outputs; k distinct experts),
+ *          App. A.2 (assignments ordered by source and (token, top-k position); ids, positions
+ *          and weights kept for the combine), App. B.2 (routed work is conserved).
+ *   [MEP]  "MoonEP routing flow -- live": the per-rank surplus over capacity S*K, and the
+ *          greedy balance (hungriest receiver refilled in one shot from the biggest donor,
+ *          donor may overshoot, moves realised by slicing the donor's biggest experts).
+ *   [RN]   Daily Papers listing, the abstract on top-k renormalisation in fine-grained MoEs
+ *          (probabilities of the selected experts are renormalised).
+ *
+ * Parity status per function is stated in each header comment ("pinned by" lists the
+ * CPU tests that tie the function to something other than itself).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_ERR_ARG 1
+#define ORACLE_ERR_DATA 2
+
+/* ---------------------------------------------------------------- bf16 helpers --- */
+
+/* bf16 is the upper half of an IEEE binary32; widening is exact. */
+static double bf16_bits_to_double(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Round a double to the nearest bf16 value, ties to even, straight from the definition:
+ * bf16 keeps 8 significant bits.  Writing v = m * 2^e with 0.5 <= |m| < 1, the nearest
+ * value is nearbyint(m * 2^8) * 2^(e-8) (nearbyint rounds ties to even in the default
+ * rounding mode).  Valid for |v| in the normal binary32 range, which is all the path
+ * produces; zero keeps its sign.  Pinned by: test_oracle_pins.py::test_bf16_rounding. */
+uint16_t oracle_double_to_bf16(double v) {
+    if (v == 0.0) return signbit(v) ? 0x8000u : 0x0000u;
+    int e;
+    double m = frexp(v, &e);
+    double r = ldexp(nearbyint(ldexp(m, 8)), e - 8);
+    float f = (float)r; /* exact: r has at most 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
+/* Element i of an array of dtype dt (0 = float32, 1 = bf16), widened to double. */
+static double load_elem(const void* p, int64_t i, int dt) {
+    if (dt == 1) return bf16_bits_to_double(((const uint16_t*)p)[i]);
+    return (double)((const float*)p)[i];
+}
+
+/* Store a double into element i of an array of dtype dt, rounding to nearest-even.
+ * (double -> float conversion in C rounds to nearest-even.) */
+static void store_elem(void* p, int64_t i, int dt, double v) {
+    if (dt == 1)
+        ((uint16_t*)p)[i] = oracle_double_to_bf16(v);
+    else
+        ((float*)p)[i] = (float)v;
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------------ route --- */
+
+/* Router top-k and routing weights.  [MF §1]: each token is sent to k experts and their
+ * outputs are mixed with routing weights; [MF §4.1]: the k experts of a token are distinct;
+ * [RN]: the probabilities of the picked experts are renormalised over the picks.
+ *
+ * For token t the experts are ranked by the key (larger logit first, then smaller expert
+ * id); ids[t][0..K) are the first K in that order (slot 0 = the largest).  Weights are the
+ * softmax of the logits: renormalize != 0 -> over the K picks, else over all E experts.
+ * The maximum logit is subtracted before exp (it cancels in the ratio).  counts[e] is the
+ * number of (t, k) with ids[t][k] == e.
+ * Pinned by: full stable sort per row (ids), torch.softmax in float64 (weights), sums. */
+int oracle_route(const float* logits, int T, int E, int K, int renormalize,
+                 int32_t* ids, float* w, int32_t* counts) {
+    if (T < 1 || E < 1 || K < 1 || K > E) return ORACLE_ERR_ARG;
+    int bad = 0;
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        const float* row = logits + (int64_t)t * E;
+        unsigned char* taken = (unsigned char*)calloc((size_t)E, 1);
+        if (!taken) { bad = 1; continue; }
+        /* K selection passes; a strict '>' keeps the lower id on equal logits */
+        for (int k = 0; k < K; ++k) {
+            int best = -1;
+            for (int e = 0; e < E; ++e) {
+                if (taken[e]) continue;
+                if (best < 0 || row[e] > row[best]) best = e;
+            }
+            taken[best] = 1;
+            ids[(int64_t)t * K + k] = best;
+        }
+        free(taken);
+        double m = (double)row[ids[(int64_t)t * K]];
+        double denom = 0.0;
+        if (renormalize) {
+            for (int k = 0; k < K; ++k) denom += exp((double)row[ids[(int64_t)t * K + k]] - m);
+        } else {
+            for (int e = 0; e < E; ++e) denom += exp((double)row[e] - m);
+        }
+        for (int k = 0; k < K; ++k)
+            w[(int64_t)t * K + k] = (float)(exp((double)row[ids[(int64_t)t * K + k]] - m) / denom);
+    }
+    if (bad) return ORACLE_ERR_DATA;
+    for (int e = 0; e < E; ++e) counts[e] = 0;
+    for (int64_t i = 0; i < (int64_t)T * K; ++i) counts[ids[i]] += 1;
+    return ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------------- permute --- */
+
+/* Local index of global expert e in the set { begin + j*stride : 0 <= j < E_loc }, or -1. */
+static int local_index(int e, int begin, int stride, int E_loc) {
+    int d = e - begin;
+    if (d < 0 || d % stride != 0) return -1;
+    int l = d / stride;
+    return l < E_loc ? l : -1;
+}
+
+/* Tile-aligned expert offsets: off[0] = 0, off[l+1] = off[l] + ceil(n_l / beta) * beta,
+ * so every expert's segment starts on a multiple of beta.  [MF §3.1]: an expert's rows are
+ * cut into blocks of at most beta rows.  Returns the padded total. */
+static int64_t padded_offsets(const int32_t* counts, int begin, int stride, int E_loc, int beta,
+                              int32_t* off) {
+    off[0] = 0;
+    for (int l = 0; l < E_loc; ++l) {
+        int64_t n = counts[begin + l * stride];
+        int64_t padded = (n + beta - 1) / beta * beta;
+        off[l + 1] = (int32_t)(off[l] + padded);
+    }
+    return off[E_loc];
+}
+
+/* Dispatch permutation.  [MF §3.1, App. A.2]: inside each expert the routed assignments
+ * keep a stable, deterministic order by source and (token, top-k position); with tokens
+ * laid out source-major that is the flat index i = t*K + k ascending.  Entry i routed to
+ * local expert l gets the next free row of l's segment; entry_pos[i] is that row (-1 when
+ * the expert is not local), row_token[row] = t (-1 on padding rows), and row `row` of xp is
+ * a copy of row t of x (row_bytes bytes each; x/xp may be NULL to skip the copy).
+ * Returns ORACLE_ERR_DATA if counts disagree with ids.
+ * Pinned by: Python sorted() over (expert, i); bijection and multiset checks. */
+int oracle_permute(const int32_t* ids, const int32_t* counts, int T, int K, int E,
+                   int begin, int stride, int E_loc, int beta,
+                   const void* x, int64_t row_bytes,
+                   int32_t* offsets, int32_t* entry_pos, int32_t* row_token, void* xp,
+                   int64_t max_rows) {
+    if (T < 1 || K < 1 || E < 1 || E_loc < 1 || stride < 1 || beta < 1) return ORACLE_ERR_ARG;
+    if (begin < 0 || begin + (int64_t)(E_loc - 1) * stride >= E) return ORACLE_ERR_ARG;
+    int64_t rows_pad = padded_offsets(counts, begin, stride, E_loc, beta, offsets);
+    if (rows_pad > max_rows) return ORACLE_ERR_ARG;
+    for (int64_t p = 0; p < rows_pad; ++p) row_token[p] = -1;
+    int32_t* cursor = (int32_t*)malloc(sizeof(int32_t) * (size_t)E_loc);
+    if (!cursor) return ORACLE_ERR_DATA;
+    for (int l = 0; l < E_loc; ++l) cursor[l] = offsets[l];
+    for (int64_t i = 0; i < (int64_t)T * K; ++i) {
+        int l = local_index(ids[i], begin, stride, E_loc);
+        if (l < 0) {
+            entry_pos[i] = -1;
+            continue;
+        }
+        int32_t p = cursor[l]++;
+        int t = (int)(i / K);
+        entry_pos[i] = p;
+        row_token[p] = t;
+        if (x && xp)
+            memcpy((char*)xp + (int64_t)p * row_bytes, (const char*)x + (int64_t)t * row_bytes,
+                   (size_t)row_bytes);
+    }
+    int rc = ORACLE_OK;
+    for (int l = 0; l < E_loc; ++l)
+        if (cursor[l] != offsets[l] + counts[begin + l * stride]) rc = ORACLE_ERR_DATA;
+    free(cursor);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------- plan --- */
+
+/* Skew-balancing plan over P logical partitions ("ranks"), which are data, not devices.
+ *
+ * [MEP]: each rank owns a contiguous group of G = E_loc / P experts; its surplus is the sum
+ * of its experts' entries minus its capacity S*K, the number of entries it computes after
+ * balancing.  Capacity here: C_r = floor(N/P) + (r < N mod P), which is S*K whenever P | N.
+ * The greedy repeats, while some rank is below capacity:
+ *   receiver = the rank with the lowest surplus (the hungriest), lowest id on ties;
+ *   donor    = the rank with the highest surplus (the biggest donor), lowest id on ties;
+ *   the receiver is refilled in one move by need = -surplus(receiver) entries: its surplus
+ *   becomes 0, the donor's drops by need (it may go below zero and be refilled later);
+ *   the move is realised by slicing the donor's own experts, biggest remaining count first
+ *   (lowest id on ties), taking min(remaining, need) from each until need is covered; each
+ *   slice (donor, receiver, expert, rows) is one entry of `moves`.
+ * What no move took stays with the owner.  q[l*P + r] = entries of local expert l computed
+ * by rank r.  [MF §3.1, App. A.2]: the plan keeps every selection and weight; rows are cut
+ * into blocks of at most beta rows in the expert's stable order.  The ranks that compute
+ * expert l take consecutive ranges of its segment in ascending rank order; the table lists
+ * blocks rank by rank, then expert by expert: (rank, expert, first row, rows).
+ * Pinned by: exact capacity and conservation invariants, move-count bound, hand-worked
+ * golden plans, and an exhaustive sweep of small count vectors against brute-force
+ * properties. */
+int oracle_plan(const int32_t* counts, int E, int begin, int stride, int E_loc, int P, int beta,
+                int32_t* q, int32_t* moves, int32_t* n_moves, int max_moves,
+                int32_t* blocks, int32_t* n_blocks, int max_blocks) {
+    if (E_loc < 1 || P < 1 || E_loc % P != 0 || beta < 1 || stride < 1) return ORACLE_ERR_ARG;
+    if (begin < 0 || begin + (int64_t)(E_loc - 1) * stride >= E) return ORACLE_ERR_ARG;
+    const int G = E_loc / P;
+    int64_t* n = (int64_t*)calloc((size_t)E_loc, sizeof(int64_t));
+    int64_t* rem = (int64_t*)calloc((size_t)E_loc, sizeof(int64_t));
+    int64_t* d = (int64_t*)calloc((size_t)P, sizeof(int64_t));
+    int32_t* off = (int32_t*)calloc((size_t)E_loc + 1, sizeof(int32_t));
+    int rc = ORACLE_OK;
+    if (!n || !rem || !d || !off) { rc = ORACLE_ERR_DATA; goto done; }
+
+    int64_t N = 0;
+    for (int l = 0; l < E_loc; ++l) {
+        n[l] = counts[begin + l * stride];
+        rem[l] = n[l];
+        N += n[l];
+    }
+    for (int r = 0; r < P; ++r) {
+        int64_t cap = N / P + (r < N % P ? 1 : 0);
+        int64_t load = 0;
+        for (int l = r * G; l < (r + 1) * G; ++l) load += n[l];
+        d[r] = load - cap;
+    }
+    for (int64_t i = 0; i < (int64_t)E_loc * P; ++i) q[i] = 0;
+
+    int nm = 0;
+    for (;;) {
+        int recv = 0, donor = 0;
+        for (int r = 1; r < P; ++r) {
+            if (d[r] < d[recv]) recv = r;
+            if (d[r] > d[donor]) donor = r;
+        }
+        if (d[recv] >= 0) break;
+        int64_t need = -d[recv];
+        d[donor] -= need;
+        d[recv] = 0;
+        while (need > 0) {
+            int best = -1;
+            for (int l = donor * G; l < (donor + 1) * G; ++l)
+                if (rem[l] > 0 && (best < 0 || rem[l] > rem[best])) best = l;
+            if (best < 0 || nm >= max_moves) { rc = ORACLE_ERR_DATA; goto done; }
+            int64_t take = rem[best] < need ? rem[best] : need;
+            q[(int64_t)best * P + recv] += (int32_t)take;
+            rem[best] -= take;
+            need -= take;
+            moves[4 * nm + 0] = donor;
+            moves[4 * nm + 1] = recv;
+            moves[4 * nm + 2] = best;
+            moves[4 * nm + 3] = (int32_t)take;
+            ++nm;
+        }
+    }
+    for (int l = 0; l < E_loc; ++l) q[(int64_t)l * P + l / G] += (int32_t)rem[l];
+    *n_moves = nm;
+
+    padded_offsets(counts, begin, stride, E_loc, beta, off);
+    int nb = 0;
+    for (int r = 0; r < P; ++r) {
+        for (int l = 0; l < E_loc; ++l) {
+            int64_t take = q[(int64_t)l * P + r];
+            if (take <= 0) continue;
+            int64_t first = off[l];
+            for (int r2 = 0; r2 < r; ++r2) first += q[(int64_t)l * P + r2];
+            for (int64_t j = 0; j * beta < take; ++j) {
+                if (nb >= max_blocks) { rc = ORACLE_ERR_DATA; goto done; }
+                int64_t rows = take - j * beta < beta ? take - j * beta : beta;
+                blocks[4 * nb + 0] = r;
+                blocks[4 * nb + 1] = l;
+                blocks[4 * nb + 2] = (int32_t)(first + j * beta);
+                blocks[4 * nb + 3] = (int32_t)rows;
+                ++nb;
+            }
+        }
+    }
+    *n_blocks = nb;
+done:
+    free(n);
+    free(rem);
+    free(d);
+    free(off);
+    return rc;
+}
+
+/* ------------------------------------------------------------------- expert FFN --- */
+
+/* SwiGLU expert FFN for a list of rows.  [MF §2.1, §4.1]: FC1 produces gate and up
+ * projections, the activation is SiLU(gate) * up, FC2 projects back to H; accumulation is
+ * in high precision and outputs are BF16.
+ *
+ * Row j of the list is row rows[j] of xp ([*, H]); it uses local expert row_expert[j]:
+ *   W1 is [E_loc, 2I, H] (rows 0..I-1 gate, I..2I-1 up), W2 is [E_loc, H, I].
+ *   g_i = sum_h xp[p][h] * W1[l][i][h],  u_i = sum_h xp[p][h] * W1[l][I+i][h]   (double)
+ *   act[j][i] = round(g_i / (1 + exp(-g_i)) * u_i)
+ *   yp[j][h]  = round(sum_i act[j][i] * W2[l][h][i])                            (double)
+ * round = bf16 nearest-even when dt == 1, float32 when dt == 0.  act is [n, I], yp [n, H].
+ * Pinned by: E=1, K=1 against a dense SwiGLU written with torch.matmul in float64. */
+int oracle_ffn_rows(const void* xp, int dt, int H, int I, const void* w1, const void* w2,
+                    const int32_t* rows, const int32_t* row_expert, int n, void* act, void* yp) {
+    if (H < 1 || I < 1 || n < 0 || (dt != 0 && dt != 1)) return ORACLE_ERR_ARG;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int j = 0; j < n; ++j) {
+        int64_t p = rows[j];
+        int64_t l = row_expert[j];
+        double* a = (double*)malloc(sizeof(double) * (size_t)I);
+        if (!a) { bad = 1; continue; }
+        const int64_t w1_base = l * 2 * (int64_t)I * H;
+        for (int i = 0; i < I; ++i) {
+            double g = 0.0, u = 0.0;
+            for (int h = 0; h < H; ++h) {
+                double xv = load_elem(xp, p * H + h, dt);
+                g += xv * load_elem(w1, w1_base + (int64_t)i * H + h, dt);
+                u += xv * load_elem(w1, w1_base + (int64_t)(I + i) * H + h, dt);
+            }
+            double v = g / (1.0 + exp(-g)) * u;
+            store_elem(act, (int64_t)j * I + i, dt, v);
+            a[i] = load_elem(act, (int64_t)j * I + i, dt); /* FC2 consumes the stored value */
+        }
+        const int64_t w2_base = l * (int64_t)H * I;
+        for (int h = 0; h < H; ++h) {
+            double y = 0.0;
+            for (int i = 0; i < I; ++i) y += a[i] * load_elem(w2, w2_base + (int64_t)h * I + i, dt);
+            store_elem(yp, (int64_t)j * H + h, dt, y);
+        }
+        free(a);
+    }
+    return bad ? ORACLE_ERR_DATA : ORACLE_OK;
+}
+
+/* The FFN over a block table: every row of every block (rank, expert, first, rows) is
+ * computed with that block's expert, results written at the same row of act [*, I] and
+ * yp [*, H] (full-size arrays indexed by permuted row). */
+int oracle_ffn_blocks(const void* xp, int dt, int H, int I, const void* w1, const void* w2,
+                      const int32_t* blocks, int n_blocks, void* act, void* yp) {
+    int64_t total = 0;
+    for (int b = 0; b < n_blocks; ++b) total += blocks[4 * b + 3];
+    int32_t* rows = (int32_t*)malloc(sizeof(int32_t) * (size_t)(total > 0 ? total : 1));
+    int32_t* ex = (int32_t*)malloc(sizeof(int32_t) * (size_t)(total > 0 ? total : 1));
+    size_t es = dt == 1 ? 2 : 4;
+    void* a = malloc(es * (size_t)(total > 0 ? total : 1) * (size_t)I);
+    void* y = malloc(es * (size_t)(total > 0 ? total : 1) * (size_t)H);
+    int rc = ORACLE_OK;
+    if (!rows || !ex || !a || !y) { rc = ORACLE_ERR_DATA; goto done; }
+    int64_t j = 0;
+    for (int b = 0; b < n_blocks; ++b)
+        for (int m = 0; m < blocks[4 * b + 3]; ++m) {
+            rows[j] = blocks[4 * b + 2] + m;
+            ex[j] = blocks[4 * b + 1];
+            ++j;
+        }
+    rc = oracle_ffn_rows(xp, dt, H, I, w1, w2, rows, ex, (int)total, a, y);
+    if (rc != ORACLE_OK) goto done;
+    for (int64_t k = 0; k < total; ++k) {
+        memcpy((char*)act + (int64_t)rows[k] * I * es, (char*)a + k * I * es, (size_t)I * es);
+        memcpy((char*)yp + (int64_t)rows[k] * H * es, (char*)y + k * H * es, (size_t)H * es);
+    }
+done:
+    free(rows);
+    free(ex);
+    free(a);
+    free(y);
+    return rc;
+}
+
+/* ---------------------------------------------------------------------- combine --- */
+
+/* Routing-weight combine.  [MF §1]: expert outputs are mixed with the routing weights;
+ * [MF §2.1]: the top-k sum is a separate step; [MF App. A.2]: token ids, top-k positions
+ * and weights are kept for it.
+ *   out[t][h] = round( sum over k = 0..K-1 with entry_pos[t*K+k] >= 0 of
+ *                      w[t][k] * yp[entry_pos[t*K+k]][h] )      (double, k ascending)
+ * A token with no local entry gets 0.  round as in oracle_ffn_rows.
+ * Pinned by: K = 1 reproduces the expert row; no local entry gives 0; equal-logit K = E
+ * gives the mean of all experts' outputs. */
+int oracle_combine(const void* yp, int dt, const float* w, const int32_t* entry_pos, int T, int H,
+                   int K, void* out) {
+    if (T < 1 || H < 1 || K < 1 || (dt != 0 && dt != 1)) return ORACLE_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        for (int h = 0; h < H; ++h) {
+            double s = 0.0;
+            for (int k = 0; k < K; ++k) {
+                int64_t p = entry_pos[(int64_t)t * K + k];
+                if (p < 0) continue;
+                s += (double)w[(int64_t)t * K + k] * load_elem(yp, p * H + h, dt);
+            }
+            store_elem(out, (int64_t)t * H + h, dt, s);
+        }
+    }
+    return ORACLE_OK;
+}

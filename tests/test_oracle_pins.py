@@ -1,0 +1,383 @@
+"""Pins that tie the CPU oracle to what the pages and the mathematics fix (no GPU).
+
+Each test checks the oracle against something other than itself: a library routine on a
+special case (stable sort, torch.softmax / torch.matmul in float64), a closed form, an
+invariant the pages state, or a plan worked out by hand (tests/golden/plan_cases.json).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from mixture_experts_routed_router_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ------------------------------------------------------------------ bf16 rounding ---
+
+def test_bf16_rounding(oracle_mod):
+    rng = np.random.default_rng(0)
+    # float32-representable values: the nearest-even bf16 equals torch's float -> bf16 cast
+    v = (rng.standard_normal(20000) * np.exp(rng.uniform(-20, 20, 20000))).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle_mod.double_to_bf16(float(a)) for a in v], np.uint16)
+    assert np.array_equal(got, ref)
+    # exact ties go to the even significand
+    assert oracle_mod.double_to_bf16(1.0 + 2.0 ** -8) == 0x3F80          # -> 1.0
+    assert oracle_mod.double_to_bf16(1.0 + 3 * 2.0 ** -8) == 0x3F82      # -> 1 + 2^-6
+    assert oracle_mod.double_to_bf16(-(1.0 + 2.0 ** -8)) == 0xBF80
+    # just above a tie rounds up (a float32 detour would round to the tie, then down)
+    assert oracle_mod.double_to_bf16(1.0 + 2.0 ** -8 + 2.0 ** -40) == 0x3F81
+    assert oracle_mod.double_to_bf16(0.0) == 0 and oracle_mod.double_to_bf16(-0.0) == 0x8000
+
+
+# ------------------------------------------------------------------------- route ---
+
+def _route_reference_ids(L: np.ndarray, K: int) -> np.ndarray:
+    # full stable sort of each row by descending logit: equal logits keep ascending id
+    return np.argsort(-L, axis=1, kind="stable")[:, :K].astype(np.int32)
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "olmoe_shaped", "qwen3_30b_a3b_shaped",
+                                  "gpt_oss_120b_decode"])
+def test_route_matches_full_sort_and_softmax(oracle_mod, name):
+    w = inputs.WORKLOADS[name]
+    for skew in w.skews:
+        L = inputs.make_logits(w, skew)
+        ids, wt, counts = oracle_mod.route(L, w.K)
+        assert np.array_equal(ids, _route_reference_ids(L, w.K))
+        picked = torch.from_numpy(np.take_along_axis(L, ids, 1).astype(np.float64))
+        ref_w = torch.softmax(picked, dim=1).numpy()
+        assert np.max(np.abs(wt - ref_w)) <= 1e-7
+        assert np.allclose(wt.astype(np.float64).sum(1), 1.0, atol=1e-6)
+        assert np.all(np.diff(wt, axis=1) <= 0)  # slot 0 is the largest weight
+        assert np.array_equal(counts, np.bincount(ids.ravel(), minlength=w.E))
+        assert counts.sum() == w.T * w.K
+        # k distinct experts per token
+        assert all(len(set(r)) == w.K for r in ids[:512].tolist())
+
+
+def test_route_no_renormalize_is_full_softmax(oracle_mod):
+    w = inputs.WORKLOADS["tiny_f32"]
+    L = inputs.make_logits(w, 1.0)
+    ids, wt, _ = oracle_mod.route(L, w.K, renormalize=False)
+    full = torch.softmax(torch.from_numpy(L.astype(np.float64)), dim=1).numpy()
+    assert np.max(np.abs(wt - np.take_along_axis(full, ids, 1))) <= 1e-7
+
+
+def test_route_ties_and_k1(oracle_mod):
+    L = np.zeros((3, 6), np.float32)
+    L[1] = [1, 2, 2, 0, 2, 1]
+    L[2] = [-1, -1, -1, -1, -1, 5]
+    ids, wt, counts = oracle_mod.route(L, 3)
+    assert ids.tolist() == [[0, 1, 2], [1, 2, 4], [5, 0, 1]]
+    assert np.allclose(wt[0], 1 / 3) and np.allclose(wt[1], 1 / 3)
+    ids1, w1, _ = oracle_mod.route(L, 1)
+    assert ids1.ravel().tolist() == [0, 1, 5] and np.all(w1 == 1.0)
+    # K = E picks every expert
+    idsE, wE, _ = oracle_mod.route(L, 6)
+    assert sorted(idsE[1].tolist()) == list(range(6))
+
+
+def test_hot4_share(oracle_mod):
+    w = inputs.WORKLOADS["qwen3_30b_a3b_shaped"]
+    _, _, counts = oracle_mod.route(inputs.make_logits(w, "hot4"), w.K)
+    share = counts[:4].sum() / counts.sum()
+    assert share >= 0.40, share
+
+
+def test_deepseek_share_local_entries(oracle_mod):
+    w = inputs.WORKLOADS["deepseek_v3_share"]
+    for skew in w.skews:
+        _, _, counts = oracle_mod.route(inputs.make_logits(w, skew), w.K)
+        local = counts[w.expert_begin::w.expert_stride][: w.n_local].sum()
+        # about T * K / 8 entries land on this GPU's 32 of 256 experts
+        assert 0.8 * w.T < local < 1.25 * w.T, local
+
+
+# ----------------------------------------------------------------------- permute ---
+
+def _check_permutation(ids, counts, E, begin, stride, E_loc, beta, offsets, entry_pos,
+                       row_token, xp=None, x=None):
+    T, K = ids.shape
+    flat = ids.ravel()
+
+    def loc(e):
+        d = e - begin
+        return d // stride if d >= 0 and d % stride == 0 and d // stride < E_loc else -1
+
+    n = [int(counts[begin + l * stride]) for l in range(E_loc)]
+    # offsets: start on multiples of beta, each segment holds its expert with < beta padding
+    assert offsets[0] == 0
+    for l in range(E_loc):
+        seg = offsets[l + 1] - offsets[l]
+        assert offsets[l] % beta == 0 and n[l] <= seg < n[l] + beta and seg % beta == 0
+    # stable expert-major order by flat index, computed independently with sorted()
+    local_entries = [i for i in range(T * K) if loc(int(flat[i])) >= 0]
+    order = sorted(local_entries, key=lambda i: (loc(int(flat[i])), i))
+    expected = np.full(T * K, -1, np.int64)
+    seen = {}
+    for i in order:
+        l = loc(int(flat[i]))
+        expected[i] = offsets[l] + seen.get(l, 0)
+        seen[l] = seen.get(l, 0) + 1
+    assert np.array_equal(entry_pos.astype(np.int64), expected)
+    # bijection between valid rows and local entries; padding rows are -1
+    valid = np.nonzero(row_token >= 0)[0]
+    assert len(valid) == len(local_entries) == sum(n)
+    assert np.array_equal(np.sort(entry_pos[entry_pos >= 0]), valid)
+    for i in local_entries:
+        assert row_token[entry_pos[i]] == i // K
+    if xp is not None:
+        tok = row_token[valid]
+        assert np.array_equal(xp[valid], x[tok])
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "olmoe_shaped", "deepseek_v3_share"])
+def test_permute_independent_sort(oracle_mod, name):
+    w = inputs.WORKLOADS[name]
+    skew = w.skews[-1]
+    L = inputs.make_logits(w, skew)
+    if w.T > 4096:  # keep the pure-Python check small: first 4096 tokens
+        L = L[:4096]
+    ids, _, counts = oracle_mod.route(L, w.K)
+    x = None
+    if w.H * L.shape[0] <= 1 << 24:
+        x = inputs.as_oracle_array(inputs.make_x(w))[: L.shape[0]]
+    offs, ep, rt, xp = oracle_mod.permute(ids, counts, w.E, w.expert_begin, w.expert_stride,
+                                          w.n_local, w.beta, x)
+    _check_permutation(ids, counts, w.E, w.expert_begin, w.expert_stride, w.n_local, w.beta,
+                       offs, ep, rt, xp, x)
+
+
+def test_permute_small_beta_and_subset(oracle_mod):
+    rng = np.random.default_rng(5)
+    T, E, K = 37, 12, 3
+    L = rng.standard_normal((T, E)).astype(np.float32)
+    ids, _, counts = oracle_mod.route(L, K)
+    x = rng.standard_normal((T, 5)).astype(np.float32)
+    for begin, stride, E_loc, beta in [(0, 1, 12, 1), (0, 1, 12, 4), (1, 3, 4, 2), (11, 1, 1, 16)]:
+        offs, ep, rt, xp = oracle_mod.permute(ids, counts, E, begin, stride, E_loc, beta, x)
+        _check_permutation(ids, counts, E, begin, stride, E_loc, beta, offs, ep, rt, xp, x)
+
+
+def test_permute_rejects_inconsistent_counts(oracle_mod):
+    ids = np.array([[0, 1], [1, 2]], np.int32)
+    bad = np.array([1, 1, 1], np.int32)  # expert 1 is picked twice
+    with pytest.raises(RuntimeError):
+        oracle_mod.permute(ids, bad, 3, 0, 1, 3, 4)
+
+
+# -------------------------------------------------------------------------- plan ---
+
+def _check_plan(counts, E, begin, stride, E_loc, P, beta, q, moves, blocks):
+    n = np.array([counts[begin + l * stride] for l in range(E_loc)], np.int64)
+    N = int(n.sum())
+    G = E_loc // P
+    cap = np.array([N // P + (1 if r < N % P else 0) for r in range(P)])
+    # selections preserved: every expert's entries are all assigned
+    assert np.array_equal(q.sum(1), n)
+    # every rank computes exactly its capacity (S*K when P divides N)
+    assert np.array_equal(q.sum(0), cap)
+    # the lower bound ceil(N/P) on the busiest rank is met
+    assert q.sum(0).max() == -(-N // P)
+    assert np.all(q >= 0)
+    # moves: donors slice only their own experts; <= P-1 rank-level moves
+    rank_moves = []
+    for d, r, l, take in moves.tolist():
+        assert l // G == d and take > 0 and d != r
+        if not rank_moves or rank_moves[-1] != (d, r):
+            rank_moves.append((d, r))
+    assert len(rank_moves) <= max(P - 1, 0)
+    receivers = {r for _, r in rank_moves}
+    for l in range(E_loc):
+        for r in range(P):
+            if q[l, r] > 0 and r != l // G:
+                assert r in receivers
+    # moved rows add up
+    moved = np.zeros_like(q)
+    for d, r, l, take in moves.tolist():
+        moved[l, r] += take
+    for l in range(E_loc):
+        for r in range(P):
+            if r != l // G:
+                assert moved[l, r] == q[l, r]
+    # blocks: <= beta rows, inside the expert's segment, cover it once, rank totals = q
+    off = np.concatenate([[0], np.cumsum((n + beta - 1) // beta * beta)])
+    covered = np.zeros(int(off[-1]), np.int64)
+    per_rank = np.zeros((E_loc, P), np.int64)
+    partial = {}
+    for r, l, b0, m in blocks.tolist():
+        assert 1 <= m <= beta
+        assert off[l] <= b0 and b0 + m <= off[l] + n[l]
+        covered[b0:b0 + m] += 1
+        per_rank[l, r] += m
+        if m < beta:
+            partial[(l, r)] = partial.get((l, r), 0) + 1
+    assert np.array_equal(per_rank, q)
+    for l in range(E_loc):
+        assert np.all(covered[off[l]:off[l] + n[l]] == 1)
+    assert all(v == 1 for v in partial.values())  # <= 1 partial block per (expert, rank)
+    assert sum(m for *_, m in blocks.tolist()) == N
+
+
+def test_plan_golden_hand_worked(oracle_mod):
+    cases = json.load(open(os.path.join(GOLDEN, "plan_cases.json")))["cases"]
+    for c in cases:
+        cnt = np.array(c["counts"], np.int32)
+        q, moves, blocks = oracle_mod.plan(cnt, len(cnt), 0, 1, len(cnt), c["P"], c["beta"])
+        assert q.tolist() == c["q"], c["name"]
+        assert moves.tolist() == c["moves"], c["name"]
+        assert blocks.tolist() == c["blocks"], c["name"]
+        _check_plan(cnt, len(cnt), 0, 1, len(cnt), c["P"], c["beta"], q, moves, blocks)
+
+
+@pytest.mark.parametrize("name", list(inputs.WORKLOADS))
+def test_plan_invariants_all_workloads(oracle_mod, name):
+    w = inputs.WORKLOADS[name]
+    for skew in w.skews:
+        _, _, counts = oracle_mod.route(inputs.make_logits(w, skew), w.K)
+        q, moves, blocks = oracle_mod.plan(counts, w.E, w.expert_begin, w.expert_stride,
+                                           w.n_local, w.P, w.beta)
+        _check_plan(counts, w.E, w.expert_begin, w.expert_stride, w.n_local, w.P, w.beta,
+                    q, moves, blocks)
+        if w.T % w.P == 0 and w.n_local == w.E:
+            # every logical rank receives exactly S*K entries, S = T / P
+            assert np.all(q.sum(0) == (w.T // w.P) * w.K)
+
+
+@pytest.mark.parametrize("P,G,cmax", [(2, 2, 4), (3, 2, 3), (4, 2, 3), (3, 1, 6), (4, 1, 5)])
+def test_plan_exhaustive_small(oracle_mod, P, G, cmax):
+    import itertools
+    E = P * G
+    for cnt in itertools.product(range(cmax + 1), repeat=E):
+        c = np.array(cnt, np.int32)
+        q, moves, blocks = oracle_mod.plan(c, E, 0, 1, E, P, 2)
+        _check_plan(c, E, 0, 1, E, P, 2, q, moves, blocks)
+
+
+# --------------------------------------------------------------------------- ffn ---
+
+def _swiglu_f64(x, w1, w2, I):
+    g = x @ w1[:I].T
+    u = x @ w1[I:].T
+    return g / (1 + torch.exp(-g)) * u
+
+
+def _ulp_bf16(v):
+    # spacing of bf16 values around |v| (normal range): 2^(floor(log2|v|) - 7)
+    return np.exp2(np.floor(np.log2(np.abs(v))) - 7)
+
+
+def test_ffn_single_expert_is_dense_swiglu_bf16(oracle_mod):
+    """E = 1, K = 1: the path reduces to one dense SwiGLU FFN (torch.matmul in float64);
+    the oracle's act and yp must be the nearest bf16 values of the float64 results."""
+    rng = np.random.default_rng(1)
+    T, H, I = 24, 64, 96
+    bf = lambda a: torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16)
+    x = bf(rng.standard_normal((T, H)))
+    W1 = bf(rng.standard_normal((1, 2 * I, H)) * 0.1)
+    W2 = bf(rng.standard_normal((1, H, I)) * 0.1)
+    rows = np.arange(T, dtype=np.int32)
+    act, yp = oracle_mod.ffn_rows(inputs.as_oracle_array(x), inputs.as_oracle_array(W1),
+                                  inputs.as_oracle_array(W2), rows, np.zeros(T, np.int32))
+    ref_act = _swiglu_f64(x.double(), W1[0].double(), W2[0].double(), I).numpy()
+    got_act = oracle_mod.bf16_to_f64(act)
+    assert np.all(np.abs(got_act - ref_act) <= 0.5 * _ulp_bf16(ref_act) * (1 + 1e-9) + 1e-300)
+    ref_y = (torch.from_numpy(got_act) @ W2[0].double().T).numpy()
+    got_y = oracle_mod.bf16_to_f64(yp)
+    assert np.all(np.abs(got_y - ref_y) <= 0.5 * _ulp_bf16(ref_y) * (1 + 1e-9) + 1e-300)
+
+
+def test_ffn_single_expert_is_dense_swiglu_f32(oracle_mod):
+    rng = np.random.default_rng(2)
+    T, H, I = 16, 32, 48
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    W1 = (rng.standard_normal((1, 2 * I, H)) * 0.1).astype(np.float32)
+    W2 = (rng.standard_normal((1, H, I)) * 0.1).astype(np.float32)
+    act, yp = oracle_mod.ffn_rows(x, W1, W2, np.arange(T, dtype=np.int32), np.zeros(T, np.int32))
+    ref_act = _swiglu_f64(torch.from_numpy(x).double(), torch.from_numpy(W1[0]).double(),
+                          torch.from_numpy(W2[0]).double(), I).numpy()
+    assert np.max(np.abs(act - ref_act) / np.abs(ref_act)) <= 2 ** -24 * 1.0001
+    ref_y = act.astype(np.float64) @ W2[0].astype(np.float64).T
+    assert np.max(np.abs(yp - ref_y) / np.abs(ref_y)) <= 2 ** -24 * 1.0001
+
+
+def _full_chain(oracle_mod, L, x, W1, W2, K, E, begin, stride, E_loc, P, beta):
+    ids, wt, counts = oracle_mod.route(L, K)
+    offs, ep, rt, xp = oracle_mod.permute(ids, counts, E, begin, stride, E_loc, beta, x)
+    q, moves, blocks = oracle_mod.plan(counts, E, begin, stride, E_loc, P, beta)
+    act, yp = oracle_mod.ffn_blocks(xp, W1, W2, blocks)
+    out = oracle_mod.combine(yp, wt, ep, L.shape[0], K)
+    return ids, wt, out
+
+
+def test_chain_k1_selects_the_right_expert(oracle_mod):
+    """K = 1, E = 6: each token's output is exactly its expert's dense SwiGLU (weight 1);
+    a wrong expert index, gate/up swap or transposed weight fails this."""
+    rng = np.random.default_rng(3)
+    T, H, I, E = 40, 32, 48, 6
+    L = rng.standard_normal((T, E)).astype(np.float32)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    W1 = (rng.standard_normal((E, 2 * I, H)) * 0.2).astype(np.float32)
+    W2 = (rng.standard_normal((E, H, I)) * 0.2).astype(np.float32)
+    ids, wt, out = _full_chain(oracle_mod, L, x, W1, W2, 1, E, 0, 1, E, 3, 4)
+    assert np.all(wt == 1.0)
+    for t in range(T):
+        e = int(ids[t, 0])
+        ref = _swiglu_f64(torch.from_numpy(x[t:t + 1]).double(), torch.from_numpy(W1[e]).double(),
+                          None, I)
+        ref = (ref @ torch.from_numpy(W2[e]).double().T).numpy()[0]
+        # act is stored as float32 before FC2, so compare against the row's scale
+        assert np.max(np.abs(out[t] - ref)) <= 1e-6 * np.max(np.abs(ref))
+
+
+def test_chain_equal_logits_all_experts_is_mean(oracle_mod):
+    """K = E with equal logits: weights are 1/E and the output is the mean of all experts."""
+    rng = np.random.default_rng(4)
+    T, H, I, E = 12, 16, 24, 4
+    L = np.zeros((T, E), np.float32)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    W1 = (rng.standard_normal((E, 2 * I, H)) * 0.3).astype(np.float32)
+    W2 = (rng.standard_normal((E, H, I)) * 0.3).astype(np.float32)
+    ids, wt, out = _full_chain(oracle_mod, L, x, W1, W2, E, E, 0, 1, E, 2, 8)
+    assert np.all(wt == np.float32(0.25))
+    ref = 0
+    for e in range(E):
+        a = _swiglu_f64(torch.from_numpy(x).double(), torch.from_numpy(W1[e]).double(), None, I)
+        ref = ref + (a @ torch.from_numpy(W2[e]).double().T).numpy() / E
+    assert np.max(np.abs(out - ref)) < 1e-5 * np.max(np.abs(ref))
+
+
+def test_chain_token_permutation_invariance(oracle_mod):
+    w = inputs.WORKLOADS["tiny_f32"]
+    L = inputs.make_logits(w, 1.0)
+    x = inputs.as_oracle_array(inputs.make_x(w))
+    W1, W2 = (inputs.as_oracle_array(t) for t in inputs.make_weights(w))
+    args = (w.K, w.E, 0, 1, w.E, w.P, 16)
+    _, _, out = _full_chain(oracle_mod, L, x, W1, W2, *args)
+    perm = np.random.default_rng(6).permutation(w.T)
+    _, _, out_p = _full_chain(oracle_mod, np.ascontiguousarray(L[perm]),
+                              np.ascontiguousarray(x[perm]), W1, W2, *args)
+    assert np.max(np.abs(out_p - out[perm])) <= 1e-6 * np.max(np.abs(out))
+
+
+# ----------------------------------------------------------------------- combine ---
+
+def test_combine_k1_and_nonlocal(oracle_mod):
+    rng = np.random.default_rng(7)
+    yp = inputs.as_oracle_array(torch.from_numpy(rng.standard_normal((6, 8)).astype(np.float32))
+                                .to(torch.bfloat16))
+    # K = 1 with weight 1 reproduces the row bit for bit
+    out = oracle_mod.combine(yp, np.ones((3, 1), np.float32), np.array([4, 0, 2], np.int32), 3, 1)
+    assert np.array_equal(out, yp[[4, 0, 2]])
+    # a token whose entries are all non-local gets zero; partial locality sums the rest
+    w = np.array([[0.75, 0.25], [0.5, 0.5]], np.float32)
+    out = oracle_mod.combine(yp, w, np.array([-1, -1, 1, -1], np.int32), 2, 2)
+    assert np.all(oracle_mod.bf16_to_f64(out[0]) == 0)
+    ref = 0.5 * oracle_mod.bf16_to_f64(yp[1])
+    assert np.array_equal(oracle_mod.bf16_to_f64(out[1]), ref)  # exact: scaling by 1/2
