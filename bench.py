@@ -1,0 +1,234 @@
+"""Benchmark of the routed-expert path of one MoE layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--skew S]
+
+One step = route -> permute -> plan -> expert FFN (FC1, FC2) -> combine over one batch of
+seeded synthetic input already resident in HBM.  Prints ONE JSON line: whole-path tokens/s,
+the grouped GEMM's TFLOP/s, the dominant kernel (FC1, the gate/up GEMM with fused SwiGLU)
+against the bf16 MFMA peak, per-call times, and the CPU oracle timed on a bounded sample of
+the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "routed-expert layer tokens/s + grouped-GEMM TFLOP/s (% MFMA peak) vs skew"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="olmoe_shaped")
+    ap.add_argument("--skew", default=None, help="Zipf exponent or 'hot4' (default: middle skew)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (tokens)")
+    ap.add_argument("--all-skews", action="store_true", help="also time every skew of the workload")
+    return ap.parse_args()
+
+
+def pick_skew(w, s):
+    if s is None:
+        return w.skews[len(w.skews) // 2]
+    if s == "hot4":
+        return s
+    for cand in w.skews:
+        if not isinstance(cand, str) and abs(cand - float(s)) < 1e-9:
+            return cand
+    raise SystemExit(f"skew {s} is not one of {w.skews} for {w.name}")
+
+
+class Step:
+    """The path's calls on one stream, with optional HIP events between them."""
+
+    CALLS = ("route", "permute", "plan", "fc1", "fc2", "combine")
+
+    def __init__(self, layer, logits, x, W1, W2):
+        self.layer, self.logits, self.x, self.W1, self.W2 = layer, logits, x, W1, W2
+
+    def run(self, events=None):
+        L = self.layer
+        rec = (lambda i: events[i].record()) if events is not None else (lambda i: None)
+        rec(0)
+        L.route(self.logits)
+        rec(1)
+        L.permute(self.x)
+        rec(2)
+        L.plan()
+        rec(3)
+        L.expert_ffn_fc1(self.W1)
+        rec(4)
+        L.expert_ffn_fc2(self.W2)
+        rec(5)
+        L.combine()
+        rec(6)
+
+
+def time_steps(step, steps, warmup, torch):
+    for _ in range(warmup):
+        step.run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step.run()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    # per-call durations: HIP events on the stream the kernels are launched on
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
+    for i in range(steps):
+        step.run(ev[i])
+    torch.cuda.synchronize()
+    per = {c: sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)) / steps * 1e3
+           for j, c in enumerate(Step.CALLS)}
+    return wall, per
+
+
+def ffn_traffic(workload: str):
+    """HBM bytes per FC1 launch from committed rocprofv3 counter runs, if they were taken on
+    the current FC1 kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"fc1_{workload}_traffic.json")
+    src = os.path.join(ROOT, "mixture_experts_routed_router_amd", "csrc", "ffn.hip")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("ffn_hip_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, skew, T_s):
+    """The CPU oracle, as it stands, over the first T_s tokens of the same batch (whole path)."""
+    import numpy as np
+    sys.path.insert(0, os.path.join(ROOT, "oracle"))
+    import oracle
+    from mixture_experts_routed_router_amd import inputs
+
+    logits = inputs.make_logits(w, skew)[:T_s].copy()
+    x = inputs.as_oracle_array(inputs.make_x(w)[:T_s].contiguous())
+    W1, W2 = (inputs.as_oracle_array(t) for t in inputs.make_weights(w, threads=16))
+    oracle.build()
+    t0 = time.perf_counter()
+    ids, wt, counts = oracle.route(logits, w.K)
+    _, ep, _, xp = oracle.permute(ids, counts, w.E, w.expert_begin, w.expert_stride, w.n_local,
+                                  w.beta, x)
+    _, _, blocks = oracle.plan(counts, w.E, w.expert_begin, w.expert_stride, w.n_local, w.P,
+                               w.beta)
+    _, yp = oracle.ffn_blocks(xp, W1, W2, blocks)
+    oracle.combine(yp, wt, ep, T_s, w.K)
+    dt = time.perf_counter() - t0
+    return {"value": round(T_s / dt, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"first {T_s} tokens of the same batch, whole path (route, permute, plan, "
+                      f"FFN, combine), float64 plain C, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mixture_experts_routed_router_amd import binding, inputs
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = inputs.WORKLOADS[args.workload]
+    skew = pick_skew(w, args.skew)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    W1, W2 = inputs.make_weights(w, threads=16)
+    W1, W2 = W1.to(dev), W2.to(dev)
+    x = inputs.make_x(w).to(dev)
+    layer = binding.RoutedExperts(w.T, w.H, w.E, w.K, w.I, w.P, dtype=dt, E_loc=w.n_local,
+                                  expert_begin=w.expert_begin, expert_stride=w.expert_stride,
+                                  block_m=w.beta)
+
+    def measure(sk, steps, warmup):
+        logits = torch.from_numpy(inputs.make_logits(w, sk)).to(dev)
+        step = Step(layer, logits, x, W1, W2)
+        wall, per = time_steps(step, steps, warmup, torch)
+        counts = layer.counts.cpu()
+        N = int(counts[w.expert_begin::w.expert_stride][: w.n_local].sum())
+        nb = int(layer.n_blocks.item())
+        return wall, per, N, nb, counts
+
+    wall, per, N, nb, counts = measure(skew, args.steps, args.warmup)
+    flops_fc1 = 4.0 * w.H * w.I * N
+    flops_ffn = 6.0 * w.H * w.I * N
+    fc1_s = per["fc1"] * 1e-6
+    ffn_s = (per["fc1"] + per["fc2"]) * 1e-6
+    achieved = flops_fc1 / fc1_s / 1e12
+    loc = counts[w.expert_begin::w.expert_stride][: w.n_local].double()
+    maxvio = float(loc.max() / loc.mean() - 1.0)
+    rows_pad = int(layer.offsets[-1].item())
+    eb = 2 if dt == torch.bfloat16 else 4
+    permute_bytes = (w.T + N) * w.H * eb + 4 * (w.T * w.K + rows_pad)
+    combine_bytes = (N + w.T) * w.H * eb + 8 * w.T * w.K
+    traffic = ffn_traffic(w.name)
+
+    line = {
+        "metric": METRIC,
+        "value": round(w.T / wall, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if dt == torch.bfloat16 else "f32",
+        "data": "synthetic (seeded Zipf-skewed router logits, N(0,1) activations, "
+                "N(0,0.02^2) expert weights)",
+        "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "E_loc": w.n_local,
+                   "K": w.K, "I": w.I, "P": w.P, "block_m": w.beta,
+                   "skew": w.skew_label(skew), "local_entries": N, "blocks": nb,
+                   "maxvio": round(maxvio, 3), "parallelism": "single GPU"},
+        "gemm_tflops": round(flops_ffn / ffn_s / 1e12, 1),
+        "gemm_frac_of_peak": round(flops_ffn / ffn_s / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "per_call_us": {k: round(v, 2) for k, v in per.items()},
+        "permute_gbs": round(permute_bytes / (per["permute"] * 1e-6) / 1e9, 1),
+        "combine_gbs": round(combine_bytes / (per["combine"] * 1e-6) / 1e9, 1),
+        "roofline": {"kernel": "moe_expert_ffn_fc1 (gate/up grouped GEMM + SwiGLU)",
+                     "bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+    }
+    if args.all_skews:
+        by = []
+        for sk in w.skews:
+            wl, pr, n_, nb_, _ = measure(sk, max(5, args.steps // 2), 2)
+            f = 6.0 * w.H * w.I * n_
+            by.append({"skew": w.skew_label(sk), "tokens_per_s": round(w.T / wl, 1),
+                       "ms_per_step": round(wl * 1e3, 4),
+                       "gemm_tflops": round(f / ((pr["fc1"] + pr["fc2"]) * 1e-6) / 1e12, 1)})
+        line["by_skew"] = by
+    if not args.no_cpu_baseline:
+        T_s = args.cpu_tokens or {"tiny_f32": 64, "olmoe_shaped": 1024,
+                                  "qwen3_30b_a3b_shaped": 1024, "gpt_oss_120b_shaped": 256,
+                                  "gpt_oss_120b_decode": 64, "deepseek_v3_share": 1024}[w.name]
+        T_s = max(w.P, T_s // w.P * w.P)
+        del layer
+        torch.cuda.empty_cache()
+        line["cpu_baseline"] = cpu_baseline(w, skew, T_s)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,286 @@
+"""Python binding of libmoe: one function per C-ABI call, same names, argument marshalling only.
+
+Every function takes torch CUDA tensors (device memory) and passes their data pointers and
+the current HIP stream to the C call; all computation happens in the HIP kernels of
+libmoe.so.  There is no fallback: if the library is missing, or a call returns an error,
+a ``MoeError`` is raised.
+
+``RoutedExperts`` holds every buffer of the path, allocated once at the static bounds the
+library reports (no allocation per call), and runs the five calls in order on one stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+_lib = None
+
+MOE_F32, MOE_BF16 = 0, 1
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape or dtype", 3: "kernel launch failed"}
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int
+_i64 = ctypes.c_int64
+
+# name -> (restype, argtypes); mirrors include/moe.h
+_SIGNATURES = {
+    "moe_status_string": (ctypes.c_char_p, [_i32]),
+    "moe_max_rows": (_i64, [_i32, _i32, _i32, _i32]),
+    "moe_max_blocks": (ctypes.c_int32, [_i32, _i32, _i32, _i32, _i32]),
+    "moe_max_moves": (ctypes.c_int32, [_i32, _i32]),
+    "moe_permute_workspace_elems": (_i64, [_i32, _i32]),
+    "moe_route": (_i32, [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "moe_permute": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
+                           _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp]),
+    "moe_plan": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _vp, _vp,
+                        _i32, _vp, _vp]),
+    "moe_expert_ffn": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _vp,
+                              _i64, _vp]),
+    "moe_expert_ffn_fc1": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _i64,
+                                  _vp]),
+    "moe_expert_ffn_fc2": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _i64,
+                                  _vp]),
+    "moe_combine": (_i32, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
+}
+
+
+class MoeError(RuntimeError):
+    pass
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """The loaded libmoe (ctypes).  torch is imported first so that the library binds to the
+    HIP runtime torch already loaded (one runtime per process, shared streams)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise MoeError(f"{_LIB_PATH} is not built; run `python -m "
+                           "mixture_experts_routed_router_amd.build` (hipcc, gfx950)")
+        handle = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(status: int, call: str):
+    if status != 0:
+        raise MoeError(f"{call}: {_STATUS.get(status, status)}")
+
+
+def _ptr(t, dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise MoeError(f"{name} must be a CUDA tensor")
+    if not t.is_contiguous():
+        raise MoeError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise MoeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype == torch.float32:
+        return MOE_F32
+    raise MoeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+# ----------------------------------------------------------------------- bounds ---
+
+def moe_max_rows(T: int, K: int, E_loc: int, block_m: int) -> int:
+    return int(lib().moe_max_rows(T, K, E_loc, block_m))
+
+
+def moe_max_blocks(T: int, K: int, E_loc: int, P: int, block_m: int) -> int:
+    return int(lib().moe_max_blocks(T, K, E_loc, P, block_m))
+
+
+def moe_max_moves(E_loc: int, P: int) -> int:
+    return int(lib().moe_max_moves(E_loc, P))
+
+
+def moe_permute_workspace_elems(T: int, E_loc: int) -> int:
+    return int(lib().moe_permute_workspace_elems(T, E_loc))
+
+
+# ------------------------------------------------------------------------ calls ---
+
+def moe_route(logits, K, topk_ids, topk_w, expert_counts, renormalize=True, stream=None):
+    T, E = logits.shape
+    _check(lib().moe_route(_ptr(logits, torch.float32, "logits"), T, E, K, int(bool(renormalize)),
+                           _ptr(topk_ids, torch.int32, "topk_ids"),
+                           _ptr(topk_w, torch.float32, "topk_w"),
+                           _ptr(expert_counts, torch.int32, "expert_counts"), _stream(stream)),
+           "moe_route")
+
+
+def moe_permute(x, topk_ids, expert_counts, E, expert_begin, expert_stride, E_loc, block_m,
+                expert_offsets, entry_pos, row_token, xp, workspace, stream=None):
+    T, H = x.shape
+    K = topk_ids.shape[1]
+    _check(lib().moe_permute(_ptr(x, None, "x"), _dt(x), T, H, K, E,
+                             _ptr(topk_ids, torch.int32, "topk_ids"),
+                             _ptr(expert_counts, torch.int32, "expert_counts"),
+                             expert_begin, expert_stride, E_loc, block_m,
+                             _ptr(expert_offsets, torch.int32, "expert_offsets"),
+                             _ptr(entry_pos, torch.int32, "entry_pos"),
+                             _ptr(row_token, torch.int32, "row_token"),
+                             _ptr(xp, x.dtype, "xp"), xp.shape[0],
+                             _ptr(workspace, torch.int32, "workspace"), workspace.numel(),
+                             _stream(stream)),
+           "moe_permute")
+
+
+def moe_plan(expert_counts, E, expert_begin, expert_stride, E_loc, P, block_m, q, moves,
+             n_moves, blocks, n_blocks, err_word=None, stream=None):
+    _check(lib().moe_plan(_ptr(expert_counts, torch.int32, "expert_counts"), E, expert_begin,
+                          expert_stride, E_loc, P, block_m, _ptr(q, torch.int32, "q"),
+                          _ptr(moves, torch.int32, "moves"), _ptr(n_moves, torch.int32, "n_moves"),
+                          moves.shape[0], _ptr(blocks, torch.int32, "blocks"),
+                          _ptr(n_blocks, torch.int32, "n_blocks"), blocks.shape[0],
+                          _ptr(err_word, torch.int32, "err_word"), _stream(stream)),
+           "moe_plan")
+
+
+def moe_expert_ffn(xp, w1, w2, blocks, n_blocks, act, yp, stream=None):
+    E_loc, two_I, H = w1.shape
+    I = two_I // 2
+    if xp.shape[1] != H or w2.shape != (E_loc, H, I) or act.shape[1] != I or yp.shape[1] != H:
+        raise MoeError("moe_expert_ffn: inconsistent shapes")
+    if act.shape[0] < xp.shape[0] or yp.shape[0] < xp.shape[0]:
+        raise MoeError("moe_expert_ffn: act/yp have fewer rows than xp")
+    dt = _dt(xp)
+    _check(lib().moe_expert_ffn(_ptr(xp, xp.dtype, "xp"), _ptr(w1, xp.dtype, "w1"),
+                                _ptr(w2, xp.dtype, "w2"), dt, H, I, E_loc,
+                                _ptr(blocks, torch.int32, "blocks"),
+                                _ptr(n_blocks, torch.int32, "n_blocks"), blocks.shape[0],
+                                _ptr(act, xp.dtype, "act"), _ptr(yp, xp.dtype, "yp"),
+                                xp.shape[0], _stream(stream)),
+           "moe_expert_ffn")
+
+
+def moe_expert_ffn_fc1(xp, w1, blocks, n_blocks, act, stream=None):
+    E_loc, two_I, H = w1.shape
+    I = two_I // 2
+    if xp.shape[1] != H or act.shape[1] != I or act.shape[0] < xp.shape[0]:
+        raise MoeError("moe_expert_ffn_fc1: inconsistent shapes")
+    _check(lib().moe_expert_ffn_fc1(_ptr(xp, xp.dtype, "xp"), _ptr(w1, xp.dtype, "w1"), _dt(xp),
+                                    H, I, E_loc, _ptr(blocks, torch.int32, "blocks"),
+                                    _ptr(n_blocks, torch.int32, "n_blocks"), blocks.shape[0],
+                                    _ptr(act, xp.dtype, "act"), xp.shape[0], _stream(stream)),
+           "moe_expert_ffn_fc1")
+
+
+def moe_expert_ffn_fc2(act, w2, blocks, n_blocks, yp, stream=None):
+    E_loc, H, I = w2.shape
+    if act.shape[1] != I or yp.shape[1] != H or yp.shape[0] < act.shape[0]:
+        raise MoeError("moe_expert_ffn_fc2: inconsistent shapes")
+    _check(lib().moe_expert_ffn_fc2(_ptr(act, act.dtype, "act"), _ptr(w2, act.dtype, "w2"),
+                                    _dt(act), H, I, E_loc, _ptr(blocks, torch.int32, "blocks"),
+                                    _ptr(n_blocks, torch.int32, "n_blocks"), blocks.shape[0],
+                                    _ptr(yp, act.dtype, "yp"), act.shape[0], _stream(stream)),
+           "moe_expert_ffn_fc2")
+
+
+def moe_combine(yp, topk_w, entry_pos, out, stream=None):
+    T, K = topk_w.shape
+    H = yp.shape[1]
+    if out.shape != (T, H) or entry_pos.numel() != T * K:
+        raise MoeError("moe_combine: inconsistent shapes")
+    _check(lib().moe_combine(_ptr(yp, None, "yp"), _dt(yp), _ptr(topk_w, torch.float32, "topk_w"),
+                             _ptr(entry_pos, torch.int32, "entry_pos"), T, H, K,
+                             _ptr(out, yp.dtype, "out"), _stream(stream)),
+           "moe_combine")
+
+
+# ------------------------------------------------------------- whole layer path ---
+
+class RoutedExperts:
+    """Static buffers for one layer shape and the five calls in order.
+
+    Buffers are sized once from the library's static bounds (T, K, E_loc, P, block_m), so a
+    forward pass allocates nothing.  Weights are device tensors W1 [E_loc, 2I, H],
+    W2 [E_loc, H, I] in the activation dtype.
+    """
+
+    def __init__(self, T, H, E, K, I, P, dtype=torch.bfloat16, E_loc=None, expert_begin=0,
+                 expert_stride=1, block_m=128, renormalize=True, device="cuda"):
+        self.T, self.H, self.E, self.K, self.I, self.P = T, H, E, K, I, P
+        self.E_loc = E_loc or E
+        self.begin, self.stride, self.block_m = expert_begin, expert_stride, block_m
+        self.renormalize = renormalize
+        self.dtype = dtype
+        i32 = dict(dtype=torch.int32, device=device)
+        self.max_rows = moe_max_rows(T, K, self.E_loc, block_m)
+        self.max_blocks = moe_max_blocks(T, K, self.E_loc, P, block_m)
+        self.max_moves = moe_max_moves(self.E_loc, P)
+        if min(self.max_rows, self.max_blocks, self.max_moves) < 0:
+            raise MoeError("invalid layer shape")
+        self.topk_ids = torch.empty((T, K), **i32)
+        self.topk_w = torch.empty((T, K), dtype=torch.float32, device=device)
+        self.counts = torch.empty((E,), **i32)
+        self.offsets = torch.empty((self.E_loc + 1,), **i32)
+        self.entry_pos = torch.empty((T * K,), **i32)
+        self.row_token = torch.empty((self.max_rows,), **i32)
+        self.workspace = torch.empty((moe_permute_workspace_elems(T, self.E_loc),), **i32)
+        self.xp = torch.empty((self.max_rows, H), dtype=dtype, device=device)
+        self.q = torch.empty((self.E_loc, P), **i32)
+        self.moves = torch.empty((self.max_moves, 4), **i32)
+        self.n_moves = torch.empty((1,), **i32)
+        self.blocks = torch.empty((self.max_blocks, 4), **i32)
+        self.n_blocks = torch.empty((1,), **i32)
+        self.err_word = torch.empty((1,), **i32)
+        self.act = torch.empty((self.max_rows, I), dtype=dtype, device=device)
+        self.yp = torch.empty((self.max_rows, H), dtype=dtype, device=device)
+        self.out = torch.empty((T, H), dtype=dtype, device=device)
+
+    def route(self, logits, stream=None):
+        moe_route(logits, self.K, self.topk_ids, self.topk_w, self.counts, self.renormalize, stream)
+
+    def permute(self, x, stream=None):
+        moe_permute(x, self.topk_ids, self.counts, self.E, self.begin, self.stride, self.E_loc,
+                    self.block_m, self.offsets, self.entry_pos, self.row_token, self.xp,
+                    self.workspace, stream)
+
+    def plan(self, stream=None):
+        moe_plan(self.counts, self.E, self.begin, self.stride, self.E_loc, self.P, self.block_m,
+                 self.q, self.moves, self.n_moves, self.blocks, self.n_blocks, self.err_word,
+                 stream)
+
+    def expert_ffn(self, w1, w2, stream=None):
+        moe_expert_ffn(self.xp, w1, w2, self.blocks, self.n_blocks, self.act, self.yp, stream)
+
+    def expert_ffn_fc1(self, w1, stream=None):
+        moe_expert_ffn_fc1(self.xp, w1, self.blocks, self.n_blocks, self.act, stream)
+
+    def expert_ffn_fc2(self, w2, stream=None):
+        moe_expert_ffn_fc2(self.act, w2, self.blocks, self.n_blocks, self.yp, stream)
+
+    def combine(self, stream=None):
+        moe_combine(self.yp, self.topk_w, self.entry_pos, self.out, stream)
+
+    def forward(self, logits, x, w1, w2, stream=None):
+        """route -> permute -> plan -> expert FFN -> combine; returns the static `out`."""
+        self.route(logits, stream)
+        self.permute(x, stream)
+        self.plan(stream)
+        self.expert_ffn(w1, w2, stream)
+        self.combine(stream)
+        return self.out

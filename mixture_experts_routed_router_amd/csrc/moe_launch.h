@@ -1,0 +1,34 @@
+// moe_launch.h -- internal launchers of libmoe (one per step), called by the C ABI in abi.hip
+// after the host-side argument checks.  Not part of the public interface.
+#pragma once
+
+#include "moe_device.h"
+
+#define MOE_PERMUTE_CHUNK 16  // tokens per permutation chunk
+#define MOE_MAX_K 16          // largest top-k
+
+hipError_t moe_launch_route(const float* logits, int T, int E, int K, int renormalize,
+                            int32_t* topk_ids, float* topk_w, int32_t* counts,
+                            hipStream_t stream);
+
+hipError_t moe_launch_permute(const void* x, int64_t row_bytes, int T, int K,
+                              const int32_t* ids, const int32_t* counts, int begin, int stride,
+                              int E_loc, int beta, int32_t* offsets, int32_t* entry_pos,
+                              int32_t* row_token, void* xp, int32_t* ws, hipStream_t stream);
+
+hipError_t moe_launch_plan(const int32_t* counts, int begin, int stride, int E_loc, int P,
+                           int beta, int32_t* q, int32_t* moves, int32_t* n_moves,
+                           int max_moves, int32_t* blocks, int32_t* n_blocks, int max_blocks,
+                           int32_t* err_word, hipStream_t stream);
+
+hipError_t moe_launch_ffn_fc1(const void* xp, const void* w1, moe_dtype_t dt, int H, int I,
+                              const int32_t* blocks, const int32_t* n_blocks, int max_blocks,
+                              void* act, int64_t max_rows, hipStream_t stream);
+
+hipError_t moe_launch_ffn_fc2(const void* act, const void* w2, moe_dtype_t dt, int H, int I,
+                              const int32_t* blocks, const int32_t* n_blocks, int max_blocks,
+                              void* yp, int64_t max_rows, hipStream_t stream);
+
+hipError_t moe_launch_combine(const void* yp, moe_dtype_t dt, const float* w,
+                              const int32_t* entry_pos, int T, int H, int K, void* out,
+                              hipStream_t stream);

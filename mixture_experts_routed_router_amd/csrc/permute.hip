@@ -1,0 +1,176 @@
+// permute.hip -- dispatch permutation into beta-aligned expert segments (moe_permute).
+//
+// MegaFlux §3.1 / App. A.2: inside each expert the routed assignments keep a stable order by
+// source and (token, top-k slot), i.e. the flat entry index t*K + k, and the rows are cut into
+// blocks of at most beta rows; each expert's segment therefore starts on a multiple of beta.
+//
+// Three launches, all without order-dependent atomics:
+//   hist    per chunk of 16 tokens, the number of entries of each local expert (LDS counts);
+//   scan    one workgroup per local expert: the padded segment start, an exclusive scan of
+//           the expert's chunk counts (so each chunk knows where its rows begin), and -1 in
+//           row_token for the segment's padding rows;
+//   scatter one workgroup per chunk: an entry's rank inside the chunk is the number of
+//           earlier tokens of the chunk that picked the same expert, read off a 16-bit token
+//           mask per expert (a token's K experts are distinct, so each (token, expert) pair
+//           is one entry); then every token row of x is read once and written to each of its
+//           local rows of xp with 16-byte accesses (HBM-bound part).
+#include "moe_launch.h"
+
+namespace {
+
+constexpr int kChunk = MOE_PERMUTE_CHUNK;  // tokens per chunk
+constexpr int kThreads = 256;
+
+// Block: 256 tokens = 16 chunks.  ws[c * E_loc + l] = entries of local expert l in chunk c.
+__global__ void __launch_bounds__(kThreads)
+permute_hist_kernel(const int32_t* __restrict__ ids, int T, int K, int begin, int stride,
+                    int E_loc, int n_chunks, int32_t* __restrict__ ws) {
+    __shared__ int h[kThreads / kChunk][256];
+    const int tid = threadIdx.x;
+    for (int i = tid; i < (kThreads / kChunk) * E_loc; i += kThreads) h[i / E_loc][i % E_loc] = 0;
+    __syncthreads();
+    const int t = blockIdx.x * kThreads + tid;
+    if (t < T) {
+        for (int k = 0; k < K; ++k) {
+            int l = moe_local_index(ids[(size_t)t * K + k], begin, stride, E_loc);
+            if (l >= 0) atomicAdd(&h[tid / kChunk][l], 1);
+        }
+    }
+    __syncthreads();
+    const int c0 = blockIdx.x * (kThreads / kChunk);
+    for (int i = tid; i < (kThreads / kChunk) * E_loc; i += kThreads) {
+        int c = c0 + i / E_loc;
+        if (c < n_chunks) ws[(size_t)c * E_loc + i % E_loc] = h[i / E_loc][i % E_loc];
+    }
+}
+
+// Block l: segment start of local expert l, exclusive scan of its chunk counts (in place),
+// padding rows of its segment marked -1.
+__global__ void __launch_bounds__(kThreads)
+permute_scan_kernel(const int32_t* __restrict__ counts, int begin, int stride, int E_loc,
+                    int beta, int n_chunks, int32_t* __restrict__ ws,
+                    int32_t* __restrict__ offsets, int32_t* __restrict__ row_token) {
+    __shared__ int part[kThreads];
+    const int l = blockIdx.x;
+    const int tid = threadIdx.x;
+
+    // padded start of segment l = sum over j < l of ceil(n_j / beta) * beta
+    int s = 0;
+    for (int j = tid; j < l; j += kThreads) {
+        int n = counts[begin + j * stride];
+        s += (n + beta - 1) / beta * beta;
+    }
+    part[tid] = s;
+    __syncthreads();
+    for (int w = kThreads / 2; w > 0; w >>= 1) {
+        if (tid < w) part[tid] += part[tid + w];
+        __syncthreads();
+    }
+    const int off = part[0];
+    const int n_l = counts[begin + l * stride];
+    const int seg = (n_l + beta - 1) / beta * beta;
+    if (tid == 0) {
+        offsets[l] = off;
+        if (l == E_loc - 1) offsets[E_loc] = off + seg;
+    }
+    __syncthreads();
+
+    // exclusive scan over chunks of ws[c][l]; thread tid owns a contiguous run of chunks
+    const int per = (n_chunks + kThreads - 1) / kThreads;
+    const int c_begin = min(n_chunks, tid * per);
+    const int c_end = min(n_chunks, c_begin + per);
+    int run = 0;
+    for (int c = c_begin; c < c_end; ++c) run += ws[(size_t)c * E_loc + l];
+    part[tid] = run;
+    __syncthreads();
+    // Hillis-Steele inclusive scan of the per-thread sums
+    for (int d = 1; d < kThreads; d <<= 1) {
+        int add = tid >= d ? part[tid - d] : 0;
+        __syncthreads();
+        part[tid] += add;
+        __syncthreads();
+    }
+    int base = part[tid] - run;
+    for (int c = c_begin; c < c_end; ++c) {
+        int v = ws[(size_t)c * E_loc + l];
+        ws[(size_t)c * E_loc + l] = base;
+        base += v;
+    }
+    for (int p = off + n_l + tid; p < off + seg; p += kThreads) row_token[p] = -1;
+}
+
+// Block c: rows of the entries of tokens [16c, 16c + 16), then the row copy.
+__global__ void __launch_bounds__(kThreads)
+permute_scatter_kernel(const uint8_t* __restrict__ x, int64_t row_bytes,
+                       const int32_t* __restrict__ ids, int T, int K, int begin, int stride,
+                       int E_loc, const int32_t* __restrict__ ws,
+                       const int32_t* __restrict__ offsets, int32_t* __restrict__ entry_pos,
+                       int32_t* __restrict__ row_token, uint8_t* __restrict__ xp) {
+    __shared__ uint32_t mask[256];
+    __shared__ int base[256];
+    __shared__ int pos_s[kChunk * MOE_MAX_K];
+    const int c = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int t0 = c * kChunk;
+    for (int l = tid; l < E_loc; l += kThreads) {
+        mask[l] = 0u;
+        base[l] = offsets[l] + ws[(size_t)c * E_loc + l];
+    }
+    __syncthreads();
+
+    // one thread per entry (token j of the chunk, slot k)
+    const int j = tid / K;
+    const int k = tid - j * K;
+    const int t = t0 + j;
+    const bool has_entry = j < kChunk && t < T;
+    int l = -1;
+    if (has_entry) {
+        l = moe_local_index(ids[(size_t)t * K + k], begin, stride, E_loc);
+        if (l >= 0) atomicOr(&mask[l], 1u << j);
+    }
+    __syncthreads();
+    if (has_entry) {
+        int p = -1;
+        if (l >= 0) {
+            p = base[l] + __popc(mask[l] & ((1u << j) - 1u));
+            row_token[p] = t;
+        }
+        entry_pos[(size_t)t * K + k] = p;
+        pos_s[j * K + k] = p;
+    }
+    __syncthreads();
+
+    // row copy: each wave moves whole token rows, 16 bytes per lane per step
+    const int lane = moe_lane_id();
+    const int wave = tid / MOE_WAVE;
+    const int nt = min(kChunk, T - t0);
+    for (int jj = wave; jj < nt; jj += kThreads / MOE_WAVE) {
+        const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)(t0 + jj) * row_bytes);
+        const int n16 = (int)(row_bytes / 16);
+#pragma unroll 4
+        for (int i = lane; i < n16; i += MOE_WAVE) {
+            uint4 v = src[i];
+            for (int kk = 0; kk < K; ++kk) {
+                int p = pos_s[jj * K + kk];
+                if (p >= 0) reinterpret_cast<uint4*>(xp + (size_t)p * row_bytes)[i] = v;
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t moe_launch_permute(const void* x, int64_t row_bytes, int T, int K,
+                              const int32_t* ids, const int32_t* counts, int begin, int stride,
+                              int E_loc, int beta, int32_t* offsets, int32_t* entry_pos,
+                              int32_t* row_token, void* xp, int32_t* ws, hipStream_t stream) {
+    const int n_chunks = (T + kChunk - 1) / kChunk;
+    permute_hist_kernel<<<(T + kThreads - 1) / kThreads, kThreads, 0, stream>>>(
+        ids, T, K, begin, stride, E_loc, n_chunks, ws);
+    permute_scan_kernel<<<E_loc, kThreads, 0, stream>>>(counts, begin, stride, E_loc, beta,
+                                                         n_chunks, ws, offsets, row_token);
+    permute_scatter_kernel<<<n_chunks, kThreads, 0, stream>>>(
+        static_cast<const uint8_t*>(x), row_bytes, ids, T, K, begin, stride, E_loc, ws, offsets,
+        entry_pos, row_token, static_cast<uint8_t*>(xp));
+    return hipGetLastError();
+}

@@ -1,0 +1,166 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same seeded
+inputs.  Bit-exact for ids, counts, offsets, permutation, plan and block table; routing
+weights within 1e-6; act / yp / out within a relative Frobenius error of 5e-3 (bf16, float32
+accumulation) or 1e-5 (float32 layer)."""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mixture_experts_routed_router_amd import inputs
+from parity_helpers import (check_index_parity, check_xp, host, oracle_index, random_case,
+                            rel_frob, row_experts, run_gpu, sample_rows, to_f64, workload_case)
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(msg):
+    print(f"\n[parity] {msg}", flush=True)
+
+
+def _full_check(c, layer, ref):
+    """Every output against the oracle on every row (small layers)."""
+    check_index_parity(layer, ref)
+    x = inputs.as_oracle_array(c.x)
+    _, _, _, xp = oracle.permute(ref.ids, ref.counts, c.E, c.begin, c.stride, c.n_local,
+                                 c.block_m, x)
+    valid = ref.row_token >= 0
+    assert np.array_equal(host(layer.xp)[: len(valid)][valid], xp[valid]), "xp"
+    W1, W2 = inputs.as_oracle_array(c.W1), inputs.as_oracle_array(c.W2)
+    act, yp = oracle.ffn_blocks(xp, W1, W2, ref.blocks)
+    g_act = host(layer.act)[: len(valid)][valid]
+    g_yp = host(layer.yp)[: len(valid)][valid]
+    e_act = rel_frob(to_f64(g_act), to_f64(act[valid]))
+    e_yp = rel_frob(to_f64(g_yp), to_f64(yp[valid]))
+    assert e_act <= c.tol, f"act rel err {e_act}"
+    assert e_yp <= c.tol, f"yp rel err {e_yp}"
+    # combine on the GPU's own yp, then the whole chain on the oracle's yp
+    out_same_yp = oracle.combine(host(layer.yp)[: len(valid)], host(layer.topk_w), ref.entry_pos,
+                                 c.T, c.K)
+    out_chain = oracle.combine(yp, ref.w, ref.entry_pos, c.T, c.K)
+    g_out = to_f64(host(layer.out))
+    e_comb = rel_frob(g_out, to_f64(out_same_yp))
+    e_chain = rel_frob(g_out, to_f64(out_chain))
+    assert e_comb <= c.tol, f"combine rel err {e_comb}"
+    assert e_chain <= c.tol, f"end-to-end rel err {e_chain}"
+    return dict(act=e_act, yp=e_yp, combine=e_comb, chain=e_chain)
+
+
+# --------------------------------------------------------------- small layers: full ---
+
+def test_tiny_f32_full():
+    c = workload_case("tiny_f32", 1.0)
+    _announce("tiny_f32 s=1")
+    errs = _full_check(c, run_gpu(c), oracle_index(c))
+    print(errs)
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("ragged", dict(seed=1, T=37, H=128, E=12, K=3, I=192, P=4, block_m=32)),
+    ("single_token", dict(seed=2, T=1, H=64, E=8, K=2, I=64, P=2)),
+    ("k1", dict(seed=3, T=200, H=128, E=8, K=1, I=128, P=4, block_m=16)),
+    ("subset_local", dict(seed=4, T=300, H=128, E=16, K=3, I=128, P=2, E_loc=4, begin=1,
+                          stride=3, block_m=64)),
+    ("hot_experts", dict(seed=5, T=700, H=64, E=8, K=2, I=64, P=4,
+                         logit_bias=[30, 29, 0, 0, 0, 0, 0, 0])),
+    ("tall_blocks", dict(seed=6, T=600, H=128, E=4, K=2, I=128, P=2, block_m=256)),
+    ("no_renorm", dict(seed=7, T=96, H=64, E=16, K=4, I=64, P=4, renormalize=False)),
+    ("wide_k", dict(seed=8, T=80, H=64, E=256, K=16, I=64, P=16, block_m=16)),
+    ("f32_ragged", dict(seed=9, T=50, H=32, E=6, K=2, I=48, P=3, dtype=torch.float32,
+                        block_m=16)),
+])
+def test_small_layers_full(name, kw):
+    c = random_case(**kw)
+    _announce(f"small {name} {kw}")
+    print(_full_check(c, run_gpu(c), oracle_index(c)))
+
+
+def test_equal_logits_ties():
+    """All-equal logits: every token picks experts 0..K-1 (lowest ids), weights 1/K."""
+    c = random_case(seed=10, T=64, H=64, E=8, K=3, I=64, P=4)
+    c.logits[:] = 0.0
+    layer = run_gpu(c)
+    ref = oracle_index(c)
+    assert np.all(ref.ids == np.arange(3)[None, :])
+    _full_check(c, layer, ref)
+
+
+def test_olmoe_first_tokens_full():
+    c = workload_case("olmoe_shaped", 1.2, T=512)
+    _announce("olmoe_shaped s=1.2, first 512 tokens, every row")
+    print(_full_check(c, run_gpu(c), oracle_index(c)))
+
+
+def test_repeat_runs_are_bit_identical():
+    """Race check: the whole path twice on the same inputs gives the same bits everywhere."""
+    c = workload_case("qwen3_30b_a3b_shaped", 1.5, T=2048)
+    a = run_gpu(c)
+    b = run_gpu(c)
+    for name in ("topk_ids", "topk_w", "counts", "offsets", "entry_pos", "q", "moves", "blocks",
+                 "out"):
+        assert torch.equal(getattr(a, name), getattr(b, name)), name
+    rows = int(host(a.offsets)[-1])
+    for name in ("row_token", "xp", "act", "yp"):
+        assert torch.equal(getattr(a, name)[:rows], getattr(b, name)[:rows]), name
+
+
+# ------------------------------------------------------ full-size layers: sampled ---
+
+FULL = [(n, s) for n in ("olmoe_shaped", "qwen3_30b_a3b_shaped", "gpt_oss_120b_shaped",
+                         "gpt_oss_120b_decode", "deepseek_v3_share")
+        for s in inputs.WORKLOADS[n].skews]
+
+_weights_cache = {}
+
+
+def _weights(name):
+    w = inputs.WORKLOADS[name]
+    key = (w.seed_id, w.H, w.I, w.n_local)
+    if key not in _weights_cache:
+        _weights_cache.clear()
+        gc.collect()
+        _weights_cache[key] = inputs.make_weights(w, threads=16)
+    return _weights_cache[key]
+
+
+@pytest.mark.parametrize("name,skew", FULL)
+def test_full_size_sampled(name, skew):
+    """At the full layer size: index outputs bit-exact on every entry; act / yp on sampled
+    rows and out on sampled tokens against the oracle, which computes those one by one."""
+    _announce(f"full {name} skew={skew}")
+    c = workload_case(name, skew, weights=_weights(name))
+    layer = run_gpu(c)
+    ref = oracle_index(c)
+    check_index_parity(layer, ref)
+    check_xp(layer, c, ref)
+
+    # sampled tokens (with at least one local entry) + sampled rows
+    rng = np.random.default_rng(1)
+    ep = ref.entry_pos.reshape(c.T, c.K)
+    has_local = np.nonzero((ep >= 0).any(1))[0]
+    toks = np.sort(rng.choice(has_local, size=min(16, len(has_local)), replace=False))
+    tok_rows = ep[toks][ep[toks] >= 0]
+    rows = np.unique(np.concatenate([sample_rows(ref, 48), tok_rows]))
+    ex = row_experts(ref.blocks, rows)
+    x_rows = inputs.as_oracle_array(c.x)[ref.row_token[rows]]
+    act, yp = oracle.ffn_rows(x_rows, inputs.as_oracle_array(c.W1), inputs.as_oracle_array(c.W2),
+                              np.arange(len(rows), dtype=np.int32), ex.astype(np.int32))
+    rows_t = torch.from_numpy(rows).to(layer.act.device)
+    e_act = rel_frob(to_f64(host(layer.act[rows_t])), to_f64(act))
+    e_yp = rel_frob(to_f64(host(layer.yp[rows_t])), to_f64(yp))
+    # end to end on the sampled tokens: oracle combine over the oracle's yp rows
+    remap = {int(r): j for j, r in enumerate(rows)}
+    ep_t = np.array([[remap[int(p)] if p >= 0 else -1 for p in ep[t]] for t in toks], np.int32)
+    out_ref = oracle.combine(yp, ref.w[toks], ep_t, len(toks), c.K)
+    toks_t = torch.from_numpy(toks).to(layer.out.device)
+    e_out = rel_frob(to_f64(host(layer.out[toks_t])), to_f64(out_ref))
+    # tokens with no local entry are exactly zero
+    none_local = np.nonzero(~(ep >= 0).any(1))[0][:64]
+    if len(none_local):
+        assert torch.count_nonzero(layer.out[torch.from_numpy(none_local).to(layer.out.device)]) == 0
+    print(f"rows={len(rows)} tokens={len(toks)} act={e_act:.2e} yp={e_yp:.2e} out={e_out:.2e}")
+    assert e_act <= c.tol and e_yp <= c.tol and e_out <= c.tol
+    del layer
+    torch.cuda.empty_cache()
