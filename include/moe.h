@@ -73,6 +73,10 @@ int32_t moe_max_moves(int E_loc, int P);
 /* int32 elements of scratch that moe_permute needs: ceil(T/16) * E_loc. */
 int64_t moe_permute_workspace_elems(int T, int E_loc);
 
+/* int32 elements of scratch that moe_expert_ffn needs (its GEMM tile schedule):
+ * 1 + 4 * max_blocks. */
+int64_t moe_ffn_workspace_elems(int max_blocks);
+
 /* ------------------------------------------------------------------------ route --- */
 
 /* Router top-k and routing weights ([MF §1]; [MF §4.1]: k distinct experts per token;
@@ -149,23 +153,31 @@ moe_status_t moe_plan(const int32_t* expert_counts, int E, int expert_begin,
  * rounded to dt on store (bf16: nearest-even; float32 accumulation throughout).
  *   xp  [max_rows, H]; w1 [E_loc, 2I, H] (rows 0..I-1 gate, I..2I-1 up); w2 [E_loc, H, I];
  *   blocks/n_blocks from moe_plan (n_blocks read on the device; max_blocks bounds it);
- *   act [max_rows, I] out; yp [max_rows, H] out; rows no block covers are untouched.
- * bf16 needs H and I to be multiples of 64; float32 needs multiples of 4. */
+ *   act [max_rows, I] out; yp [max_rows, H] out; rows no block covers are untouched;
+ *   workspace  int32 scratch, workspace_elems >= moe_ffn_workspace_elems(max_blocks); the
+ *       bf16 path writes its tile schedule there (128-row pieces of one expert's blocks paired
+ *       into 256-row GEMM tiles).
+ * bf16 needs H and I to be multiples of 64; float32 needs multiples of 4.  E_loc <= 256. */
 moe_status_t moe_expert_ffn(const void* xp, const void* w1, const void* w2, moe_dtype_t dt,
                             int H, int I, int E_loc,
                             const int32_t* blocks, const int32_t* n_blocks, int max_blocks,
-                            void* act, void* yp, int64_t max_rows, hipStream_t stream);
+                            void* act, void* yp, int64_t max_rows,
+                            int32_t* workspace, int64_t workspace_elems, hipStream_t stream);
 
 /* The two halves of moe_expert_ffn, same arguments and semantics, for callers that
  * schedule or time FC1 and FC2 apart ([MF §2.1, §3.2]: FC1 needs only W1 and the input
- * block; FC2 needs W2 and FC1's activation block).  moe_expert_ffn = fc1 then fc2. */
+ * block; FC2 needs W2 and FC1's activation block).  moe_expert_ffn = fc1 then fc2.  fc1
+ * writes the tile schedule into `workspace`; fc2 reads it, so fc2 must follow an fc1 call
+ * with the same blocks and workspace on the same stream. */
 moe_status_t moe_expert_ffn_fc1(const void* xp, const void* w1, moe_dtype_t dt, int H, int I,
                                 int E_loc, const int32_t* blocks, const int32_t* n_blocks,
                                 int max_blocks, void* act, int64_t max_rows,
+                                int32_t* workspace, int64_t workspace_elems,
                                 hipStream_t stream);
 moe_status_t moe_expert_ffn_fc2(const void* act, const void* w2, moe_dtype_t dt, int H, int I,
                                 int E_loc, const int32_t* blocks, const int32_t* n_blocks,
                                 int max_blocks, void* yp, int64_t max_rows,
+                                const int32_t* workspace, int64_t workspace_elems,
                                 hipStream_t stream);
 
 /* ---------------------------------------------------------------------- combine --- */

@@ -32,17 +32,18 @@ _SIGNATURES = {
     "moe_max_blocks": (ctypes.c_int32, [_i32, _i32, _i32, _i32, _i32]),
     "moe_max_moves": (ctypes.c_int32, [_i32, _i32]),
     "moe_permute_workspace_elems": (_i64, [_i32, _i32]),
+    "moe_ffn_workspace_elems": (_i64, [_i32]),
     "moe_route": (_i32, [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
     "moe_permute": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
                            _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp]),
     "moe_plan": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _vp, _vp,
                         _i32, _vp, _vp]),
     "moe_expert_ffn": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _vp,
-                              _i64, _vp]),
+                              _i64, _vp, _i64, _vp]),
     "moe_expert_ffn_fc1": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _i64,
-                                  _vp]),
+                                  _vp, _i64, _vp]),
     "moe_expert_ffn_fc2": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _i64,
-                                  _vp]),
+                                  _vp, _i64, _vp]),
     "moe_combine": (_i32, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
 }
 
@@ -120,6 +121,10 @@ def moe_permute_workspace_elems(T: int, E_loc: int) -> int:
     return int(lib().moe_permute_workspace_elems(T, E_loc))
 
 
+def moe_ffn_workspace_elems(max_blocks: int) -> int:
+    return int(lib().moe_ffn_workspace_elems(max_blocks))
+
+
 # ------------------------------------------------------------------------ calls ---
 
 def moe_route(logits, K, topk_ids, topk_w, expert_counts, renormalize=True, stream=None):
@@ -159,7 +164,7 @@ def moe_plan(expert_counts, E, expert_begin, expert_stride, E_loc, P, block_m, q
            "moe_plan")
 
 
-def moe_expert_ffn(xp, w1, w2, blocks, n_blocks, act, yp, stream=None):
+def moe_expert_ffn(xp, w1, w2, blocks, n_blocks, act, yp, workspace, stream=None):
     E_loc, two_I, H = w1.shape
     I = two_I // 2
     if xp.shape[1] != H or w2.shape != (E_loc, H, I) or act.shape[1] != I or yp.shape[1] != H:
@@ -172,11 +177,12 @@ def moe_expert_ffn(xp, w1, w2, blocks, n_blocks, act, yp, stream=None):
                                 _ptr(blocks, torch.int32, "blocks"),
                                 _ptr(n_blocks, torch.int32, "n_blocks"), blocks.shape[0],
                                 _ptr(act, xp.dtype, "act"), _ptr(yp, xp.dtype, "yp"),
-                                xp.shape[0], _stream(stream)),
+                                xp.shape[0], _ptr(workspace, torch.int32, "workspace"),
+                                workspace.numel(), _stream(stream)),
            "moe_expert_ffn")
 
 
-def moe_expert_ffn_fc1(xp, w1, blocks, n_blocks, act, stream=None):
+def moe_expert_ffn_fc1(xp, w1, blocks, n_blocks, act, workspace, stream=None):
     E_loc, two_I, H = w1.shape
     I = two_I // 2
     if xp.shape[1] != H or act.shape[1] != I or act.shape[0] < xp.shape[0]:
@@ -184,18 +190,22 @@ def moe_expert_ffn_fc1(xp, w1, blocks, n_blocks, act, stream=None):
     _check(lib().moe_expert_ffn_fc1(_ptr(xp, xp.dtype, "xp"), _ptr(w1, xp.dtype, "w1"), _dt(xp),
                                     H, I, E_loc, _ptr(blocks, torch.int32, "blocks"),
                                     _ptr(n_blocks, torch.int32, "n_blocks"), blocks.shape[0],
-                                    _ptr(act, xp.dtype, "act"), xp.shape[0], _stream(stream)),
+                                    _ptr(act, xp.dtype, "act"), xp.shape[0],
+                                    _ptr(workspace, torch.int32, "workspace"), workspace.numel(),
+                                    _stream(stream)),
            "moe_expert_ffn_fc1")
 
 
-def moe_expert_ffn_fc2(act, w2, blocks, n_blocks, yp, stream=None):
+def moe_expert_ffn_fc2(act, w2, blocks, n_blocks, yp, workspace, stream=None):
     E_loc, H, I = w2.shape
     if act.shape[1] != I or yp.shape[1] != H or yp.shape[0] < act.shape[0]:
         raise MoeError("moe_expert_ffn_fc2: inconsistent shapes")
     _check(lib().moe_expert_ffn_fc2(_ptr(act, act.dtype, "act"), _ptr(w2, act.dtype, "w2"),
                                     _dt(act), H, I, E_loc, _ptr(blocks, torch.int32, "blocks"),
                                     _ptr(n_blocks, torch.int32, "n_blocks"), blocks.shape[0],
-                                    _ptr(yp, act.dtype, "yp"), act.shape[0], _stream(stream)),
+                                    _ptr(yp, act.dtype, "yp"), act.shape[0],
+                                    _ptr(workspace, torch.int32, "workspace"), workspace.numel(),
+                                    _stream(stream)),
            "moe_expert_ffn_fc2")
 
 
@@ -247,6 +257,7 @@ class RoutedExperts:
         self.blocks = torch.empty((self.max_blocks, 4), **i32)
         self.n_blocks = torch.empty((1,), **i32)
         self.err_word = torch.empty((1,), **i32)
+        self.ffn_workspace = torch.empty((moe_ffn_workspace_elems(self.max_blocks),), **i32)
         self.act = torch.empty((self.max_rows, I), dtype=dtype, device=device)
         self.yp = torch.empty((self.max_rows, H), dtype=dtype, device=device)
         self.out = torch.empty((T, H), dtype=dtype, device=device)
@@ -265,13 +276,16 @@ class RoutedExperts:
                  stream)
 
     def expert_ffn(self, w1, w2, stream=None):
-        moe_expert_ffn(self.xp, w1, w2, self.blocks, self.n_blocks, self.act, self.yp, stream)
+        moe_expert_ffn(self.xp, w1, w2, self.blocks, self.n_blocks, self.act, self.yp,
+                       self.ffn_workspace, stream)
 
     def expert_ffn_fc1(self, w1, stream=None):
-        moe_expert_ffn_fc1(self.xp, w1, self.blocks, self.n_blocks, self.act, stream)
+        moe_expert_ffn_fc1(self.xp, w1, self.blocks, self.n_blocks, self.act, self.ffn_workspace,
+                           stream)
 
     def expert_ffn_fc2(self, w2, stream=None):
-        moe_expert_ffn_fc2(self.act, w2, self.blocks, self.n_blocks, self.yp, stream)
+        moe_expert_ffn_fc2(self.act, w2, self.blocks, self.n_blocks, self.yp, self.ffn_workspace,
+                           stream)
 
     def combine(self, stream=None):
         moe_combine(self.yp, self.topk_w, self.entry_pos, self.out, stream)

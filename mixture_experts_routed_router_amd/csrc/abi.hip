@@ -117,44 +117,57 @@ moe_status_t check_ffn_shape(moe_dtype_t dt, int H, int I, int E_loc, int max_bl
 
 }  // namespace
 
+int64_t moe_ffn_workspace_elems(int max_blocks) {
+    if (max_blocks < 1) return -1;
+    return moe_ffn_workspace_elems_impl(max_blocks);
+}
+
 moe_status_t moe_expert_ffn_fc1(const void* xp, const void* w1, moe_dtype_t dt, int H, int I,
                                 int E_loc, const int32_t* blocks, const int32_t* n_blocks,
                                 int max_blocks, void* act, int64_t max_rows,
+                                int32_t* workspace, int64_t workspace_elems,
                                 hipStream_t stream) {
-    if (!xp || !w1 || !blocks || !n_blocks || !act) return MOE_ERR_INVALID;
+    if (!xp || !w1 || !blocks || !n_blocks || !act || !workspace) return MOE_ERR_INVALID;
     if (!aligned16(xp) || !aligned16(w1) || !aligned16(act)) return MOE_ERR_INVALID;
     moe_status_t st = check_ffn_shape(dt, H, I, E_loc, max_blocks, max_rows);
     if (st != MOE_OK) return st;
-    return launched(moe_launch_ffn_fc1(xp, w1, dt, H, I, blocks, n_blocks, max_blocks, act,
-                                       max_rows, stream));
+    if (workspace_elems < moe_ffn_workspace_elems(max_blocks)) return MOE_ERR_INVALID;
+    if (E_loc > 256) return MOE_ERR_UNSUPPORTED;
+    if (dt == MOE_BF16) {
+        st = launched(moe_launch_ffn_schedule(blocks, n_blocks, max_blocks, E_loc, workspace,
+                                              stream));
+        if (st != MOE_OK) return st;
+    }
+    return launched(moe_launch_ffn_fc1(xp, w1, dt, H, I, blocks, n_blocks, max_blocks,
+                                       workspace, act, max_rows, stream));
 }
 
 moe_status_t moe_expert_ffn_fc2(const void* act, const void* w2, moe_dtype_t dt, int H, int I,
                                 int E_loc, const int32_t* blocks, const int32_t* n_blocks,
                                 int max_blocks, void* yp, int64_t max_rows,
+                                const int32_t* workspace, int64_t workspace_elems,
                                 hipStream_t stream) {
-    if (!act || !w2 || !blocks || !n_blocks || !yp) return MOE_ERR_INVALID;
+    if (!act || !w2 || !blocks || !n_blocks || !yp || !workspace) return MOE_ERR_INVALID;
     if (!aligned16(act) || !aligned16(w2) || !aligned16(yp)) return MOE_ERR_INVALID;
     moe_status_t st = check_ffn_shape(dt, H, I, E_loc, max_blocks, max_rows);
     if (st != MOE_OK) return st;
-    return launched(moe_launch_ffn_fc2(act, w2, dt, H, I, blocks, n_blocks, max_blocks, yp,
-                                       max_rows, stream));
+    if (workspace_elems < moe_ffn_workspace_elems(max_blocks)) return MOE_ERR_INVALID;
+    if (E_loc > 256) return MOE_ERR_UNSUPPORTED;
+    return launched(moe_launch_ffn_fc2(act, w2, dt, H, I, blocks, n_blocks, max_blocks,
+                                       workspace, yp, max_rows, stream));
 }
 
 moe_status_t moe_expert_ffn(const void* xp, const void* w1, const void* w2, moe_dtype_t dt,
                             int H, int I, int E_loc, const int32_t* blocks,
                             const int32_t* n_blocks, int max_blocks, void* act, void* yp,
-                            int64_t max_rows, hipStream_t stream) {
-    if (!xp || !w1 || !w2 || !blocks || !n_blocks || !act || !yp) return MOE_ERR_INVALID;
-    if (!aligned16(xp) || !aligned16(w1) || !aligned16(w2) || !aligned16(act) || !aligned16(yp))
-        return MOE_ERR_INVALID;
-    moe_status_t st = check_ffn_shape(dt, H, I, E_loc, max_blocks, max_rows);
+                            int64_t max_rows, int32_t* workspace, int64_t workspace_elems,
+                            hipStream_t stream) {
+    if (!w2 || !yp || !aligned16(w2) || !aligned16(yp)) return MOE_ERR_INVALID;
+    moe_status_t st = moe_expert_ffn_fc1(xp, w1, dt, H, I, E_loc, blocks, n_blocks, max_blocks,
+                                         act, max_rows, workspace, workspace_elems, stream);
     if (st != MOE_OK) return st;
-    st = launched(moe_launch_ffn_fc1(xp, w1, dt, H, I, blocks, n_blocks, max_blocks, act,
-                                     max_rows, stream));
-    if (st != MOE_OK) return st;
-    return launched(moe_launch_ffn_fc2(act, w2, dt, H, I, blocks, n_blocks, max_blocks, yp,
-                                       max_rows, stream));
+    return moe_expert_ffn_fc2(act, w2, dt, H, I, E_loc, blocks, n_blocks, max_blocks, yp,
+                              max_rows, workspace, workspace_elems, stream);
 }
 
 moe_status_t moe_combine(const void* yp, moe_dtype_t dt, const float* topk_w,

@@ -1,71 +1,190 @@
 // ffn.hip -- SwiGLU expert FFN over the plan's block table (moe_expert_ffn).
 //
 // MegaFlux §2.1: FC1 (gate and up projections) then FC2; §4.1: SwiGLU experts, FP32
-// accumulation, BF16 outputs; §3.1: the token dimension of the expert GEMM tiles is the
-// plan's block of at most beta rows.  The fused gate+up idea (both projections from the same
-// input tile, activation applied in registers) is the one the TritonMoE abstract (Daily Papers
+// accumulation, BF16 outputs; §3.1: the token dimension of the expert GEMM work is the plan's
+// block of at most beta rows.  The fused gate+up idea (both projections from the same input
+// tile, activation applied in registers) is the one the TritonMoE abstract (Daily Papers
 // listing) describes.
 //
-// bf16 path: two grouped GEMMs on v_mfma_f32_32x32x16_bf16.
-//   gate/up: per (block, 64 act columns): a 128-row A tile of xp times 128 rows of W1 (64 gate
-//            rows n0.. and the 64 up rows I+n0..), then act = SiLU(g) * u in registers.
-//   down:    per (block, 128 columns of H): act tile times 128 rows of W2.
-// Both operands are K-contiguous (C = A * B^T), so each lane's MFMA fragment is one 16-byte
-// LDS read.  Tiles are staged through LDS in 64-wide K slices, double buffered, rows XOR-
-// swizzled in 16-byte chunks so the fragment reads of 8 consecutive rows hit distinct banks.
-// Four waves per workgroup in a 2 x 2 grid, each owning 64 rows x 64 B-rows (2 x 2 MFMA
-// tiles).  The grid is persistent: workgroup w runs on XCD w % 8 and walks a contiguous slice
-// of the (block, column tile) items, so items that share A rows run on the same XCD's L2.
-// The block count is read on the device; there is no host round trip.
+// bf16 path: a schedule pass, then two grouped GEMMs on v_mfma_f32_32x32x16_bf16.
+//   schedule: pairs each expert's blocks (in table order) into 256-row tiles of two <=128-row
+//             halves with independent row bases; an expert with an odd block count ends with
+//             a half tile.  Tiles are listed expert by expert.
+//   FC1:      per (tile, 128 act columns): A = the tile's xp rows, B = 128 gate rows of W1[l]
+//             and the matching 128 up rows; act = SiLU(g) * u in registers, bf16 store.
+//   FC2:      per (tile, 256 columns of H): A = act rows, B = 256 rows of W2[l].
+// Why 256 x 256: a CU fills LDS from L2 at roughly 14-20 B/clk (bounded by outstanding L1
+// misses times L2 latency), while its four SIMDs consume 4096 flop/clk; a tile must therefore
+// do >= ~200 flop per staged byte to approach the MFMA roof.  256 x 256 gives 128 flop/B at
+// one workgroup (256 accumulators per lane, in AGPRs) per CU; 128 x 256 gave 85.
+// Both operands are K-contiguous (C = A * B^T), so an MFMA fragment is one 16-byte LDS read.
+// K is staged in 32-wide slices through a 4-deep LDS ring filled by gfx950 direct-to-LDS
+// loads (three slices in flight while one is consumed), with one wait + barrier per slice
+// placed behind that slice's last MFMAs.  Each wave owns all 256 rows x 64 B rows.  The grid
+// is persistent: workgroup w runs on XCD w % 8 and walks a contiguous eighth of the
+// (tile, column tile) items, so concurrent items share A rows and B rows in that XCD's L2.
+// Block and tile counts are read on the device; there is no host round trip.
 #include "moe_launch.h"
 
 namespace {
 
-constexpr int BM = 128;      // rows per tile (= the plan's block of <= 128 rows)
+constexpr int HALF = 128;    // rows per tile half (= the plan's largest block at beta 128)
+constexpr int BM = 2 * HALF; // rows per tile
 constexpr int BN = 256;      // B rows per tile (FC1: 128 gate + 128 up; FC2: 256 columns of H)
-constexpr int BK = 64;       // K slice per LDS stage
-constexpr int STAGES = 3;    // LDS ring depth: two slices in flight while one is consumed
-constexpr int kThreads = 256;
+constexpr int BK = 64;       // K slice per LDS stage: 128-byte rows = whole cache lines
+constexpr int STAGES = 2;    // LDS ring depth (one slice consumed while the next lands)
+constexpr int kWaves = 8;    // two waves per SIMD
+constexpr int kThreads = kWaves * MOE_WAVE;
 constexpr int kXcds = 8;
-constexpr int A_STAGE_BYTES = BM * BK * 2;                  // 16 KB
-constexpr int B_STAGE_BYTES = BN * BK * 2;                  // 32 KB
-constexpr int STAGE_BYTES = A_STAGE_BYTES + B_STAGE_BYTES;  // 48 KB
-constexpr int LOADS_PER_STAGE = STAGE_BYTES / (kThreads * 16);  // 12 x 16 B per thread
+constexpr int ROW_BYTES = BK * 2;                           // 128
+constexpr int A_STAGE_BYTES = BM * ROW_BYTES;               // 32 KB
+constexpr int B_STAGE_BYTES = BN * ROW_BYTES;               // 32 KB
+constexpr int STAGE_BYTES = A_STAGE_BYTES + B_STAGE_BYTES;  // 64 KB
+constexpr int SEG_ROWS = 1024 / ROW_BYTES;                  // 8 rows per 1 KB copy
+constexpr int DMA_PER_WAVE = STAGE_BYTES / 1024 / kWaves;   // 8 (6 for a half tile)
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
 
-__device__ __forceinline__ bf16x8_t lds_frag(const uint8_t* base, int row, int ch) {
-    // 16-byte chunk `ch` of row `row` in a [rows][64] bf16 tile whose chunks are XOR-swizzled
-    // by (row & 7): 8 consecutive rows reading one logical chunk hit 8 different bank groups.
-    const uint4 v = *reinterpret_cast<const uint4*>(base + row * (BK * 2) + ((ch ^ (row & 7)) << 4));
+// Stage layout.  A stage holds the tile's 256 A rows and 256 B rows, 128 bytes (64 bf16, one
+// cache line) each, in 1 KB segments of 8 rows: A segment g = rows 8g..8g+7, B likewise.
+// Wave w fills A segments w, w+8, w+16, w+24 and B segments w, w+8, w+16, w+24, placed
+// contiguously at [w * 8 KB, w * 8 KB + 8 KB) in that order, so the wave needs one M0 value
+// per four copies and selects segments with the copy instruction's immediate offset (which
+// moves the LDS destination and the global source alike).  Within the tile, row r's logical
+// 16-byte chunk c sits at physical chunk c ^ ((r >> 1) & 7): a ds_read_b128 serves 16 lanes
+// at a time over 64 four-byte banks, and 16 consecutive rows reading one logical chunk then
+// land in 16 distinct bank groups (r & 1 picks the 128-byte half, the XOR the group in it).
+__device__ __forceinline__ int swz_chunk(int row, int c) { return c ^ ((row >> 1) & 7); }
+
+__device__ __forceinline__ uint32_t stage_row_offset(int row, bool b_side) {
+    const int g = row >> 3;  // segment of the row among its side's 32
+    return (uint32_t)((g & 7) * 8192 + ((b_side ? 4 : 0) + (g >> 3)) * 1024 + (row & 7) * ROW_BYTES);
+}
+
+__device__ __forceinline__ bf16x8_t lds_frag(const uint8_t* stage, int row, bool b_side, int ch) {
+    const uint4 v = *reinterpret_cast<const uint4*>(stage + stage_row_offset(row, b_side) +
+                                                    (swz_chunk(row, ch) << 4));
     return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// 16 bytes per lane from global memory straight into LDS (gfx950 global_load_lds_dwordx4):
-// lane i's bytes land at LDS address lds_addr + 16 * i.  Issued from inline asm so that the
-// compiler does not drain every outstanding copy before each LDS access; the caller waits
-// with vmcnt and a barrier instead.  M0 (the LDS base) is saved and restored around it.
-__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_addr) {
+// Four copies of one stage for this wave straight from global memory into LDS (gfx950
+// global_load_lds_dwordx4, scalar base + 32-bit lane offset): copy i moves 16 B per lane to
+// LDS address M0 + 1024 i + 16 lane from base_i + lane offset + 1024 i (the scalar bases are
+// passed pre-biased by -1024 i).  Issued from inline asm so that the compiler does not drain
+// every outstanding copy before each LDS access; the kernel waits with explicit vmcnt counts
+// and a barrier instead.  M0 is saved and restored.  With `two` false only copies 0 and 1 go.
+__device__ __forceinline__ void four_copies(uint32_t m0, const void* b0, const void* b1,
+                                            const void* b2, const void* b3, uint32_t o0,
+                                            uint32_t o1, uint32_t o2, uint32_t o3, bool two) {
     uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %2\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, off\n\t"
-        "s_nop 0\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(gptr), "s"(lds_addr)
-        : "memory");
+    if (two)
+        asm volatile(
+            "s_mov_b32 %0, m0\n\t"
+            "s_mov_b32 m0, %5\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %1, %6\n\t"
+            "global_load_lds_dwordx4 %2, %7 offset:1024\n\t"
+            "global_load_lds_dwordx4 %3, %8 offset:2048\n\t"
+            "global_load_lds_dwordx4 %4, %9 offset:3072\n\t"
+            "s_nop 0\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(saved)
+            : "v"(o0), "v"(o1), "v"(o2), "v"(o3), "s"(m0), "s"(b0), "s"(b1), "s"(b2), "s"(b3)
+            : "memory");
+    else
+        asm volatile(
+            "s_mov_b32 %0, m0\n\t"
+            "s_mov_b32 m0, %3\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %1, %4\n\t"
+            "global_load_lds_dwordx4 %2, %5 offset:1024\n\t"
+            "s_nop 0\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(saved)
+            : "v"(o0), "v"(o1), "s"(m0), "s"(b0), "s"(b1)
+            : "memory");
 }
 
-// All but the newest stage's copies of this wave have landed; then the whole workgroup meets.
-#define MOE_WAIT_STAGE_AND_BARRIER() \
-    asm volatile("s_waitcnt vmcnt(12)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
-#define MOE_WAIT_ALL_AND_BARRIER() \
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
+// Wait until at most n of this wave's copies are outstanding, then meet the workgroup.
+// n = pending stages (0 or 1) x copies per stage (8, or 6 for a half tile).
+#define MOE_WAIT_CASE(n)                                                                      \
+    case n:                                                                                   \
+        asm volatile("s_waitcnt vmcnt(" #n ")\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); \
+        break;
+__device__ __forceinline__ void wait_copies_and_barrier(int n) {
+    switch (n) {
+        MOE_WAIT_CASE(8)
+        MOE_WAIT_CASE(6)
+        default:
+            asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            break;
+    }
+}
+#undef MOE_WAIT_CASE
 
-// One grouped GEMM over the block table: C[p][n] for rows p of each block (expert l),
+// ------------------------------------------------------------------ tile schedule ---
+
+// One workgroup.  The unit of pairing is a 128-row piece of a block: unit 2b + s covers rows
+// [first_b + 128 s, first_b + min(rows_b, 128 (s + 1))) of block b (s = 1 exists only for a
+// block of more than 128 rows).  tiles[0] = tile count; tile t = (tiles[1 + 2t],
+// tiles[2 + 2t]) = its two units (second = -1 for a half tile).  An expert's units are paired
+// in table order; experts follow one another in ascending local id.
+__global__ void __launch_bounds__(256)
+ffn_schedule_kernel(const int32_t* __restrict__ blocks, const int32_t* __restrict__ n_blocks_ptr,
+                    int max_blocks, int E_loc, int32_t* __restrict__ tiles) {
+    __shared__ int cnt[256];
+    __shared__ int tstart[257];
+    __shared__ int running[256];
+    __shared__ unsigned long long mask[4][256];
+    const int tid = threadIdx.x, lane = moe_lane_id(), wave = tid / MOE_WAVE;
+    int nb = *n_blocks_ptr;
+    nb = nb < max_blocks ? nb : max_blocks;
+    for (int l = tid; l < E_loc; l += 256) {
+        cnt[l] = 0;
+        running[l] = 0;
+    }
+    __syncthreads();
+    for (int b = tid; b < nb; b += 256)
+        atomicAdd(&cnt[blocks[4 * b + 1]], blocks[4 * b + 3] > HALF ? 2 : 1);
+    __syncthreads();
+    if (tid == 0) {  // tile starts per expert (<= 256 experts: a short serial scan)
+        int s = 0;
+        for (int l = 0; l < E_loc; ++l) {
+            tstart[l] = s;
+            s += (cnt[l] + 1) / 2;
+        }
+        tstart[E_loc] = s;
+        tiles[0] = s;
+    }
+    __syncthreads();
+    // stable rank of each unit among its expert's units, 256 units per round
+    for (int u0 = 0; u0 < 2 * nb; u0 += 256) {
+        for (int i = tid; i < 4 * 256; i += 256) mask[i / 256][i % 256] = 0ull;
+        __syncthreads();
+        const int u = u0 + tid;
+        const int b = u >> 1;
+        int l = -1;
+        if (b < nb && ((u & 1) == 0 || blocks[4 * b + 3] > HALF)) l = blocks[4 * b + 1];
+        if (l >= 0) atomicOr(&mask[wave][l], 1ull << lane);
+        __syncthreads();
+        if (l >= 0) {
+            int pos = running[l] + __popcll(mask[wave][l] & ((1ull << lane) - 1ull));
+            for (int w = 0; w < wave; ++w) pos += __popcll(mask[w][l]);
+            tiles[1 + 2 * (tstart[l] + pos / 2) + (pos & 1)] = u;
+        }
+        __syncthreads();
+        for (int e = tid; e < E_loc; e += 256)
+            running[e] += __popcll(mask[0][e]) + __popcll(mask[1][e]) + __popcll(mask[2][e]) +
+                          __popcll(mask[3][e]);
+        __syncthreads();
+    }
+    for (int e = tid; e < E_loc; e += 256)
+        if (cnt[e] & 1) tiles[1 + 2 * (tstart[e] + cnt[e] / 2) + 1] = -1;
+}
+
+// ------------------------------------------------------------------ grouped GEMMs ---
+
+// C[p][c] for the rows p of each tile (expert l):
 //   FC1 (kSwiGLU): act[p][c] = SiLU(A[p].W1[l][c]) * (A[p].W1[l][I + c]), c < I
 //   FC2:           yp[p][c]  = A[p].W2[l][c],                              c < H
 // A is [a_rows, Kdim], B per expert [b_rows, Kdim]; both K-contiguous.
@@ -74,19 +193,17 @@ __global__ void __launch_bounds__(kThreads, 1)
 ffn_bf16_kernel(const uint16_t* __restrict__ A, int64_t a_rows, int Kdim,
                 const uint16_t* __restrict__ B, int64_t b_expert_stride, int b_rows,
                 uint16_t* __restrict__ C, int ldc, int n_cols, int I, int NT,
-                const int32_t* __restrict__ blocks, const int32_t* __restrict__ n_blocks_ptr,
-                int max_blocks) {
+                const int32_t* __restrict__ blocks, const int32_t* __restrict__ tiles) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
 
-    static_assert(LOADS_PER_STAGE == 12, "the stage wait below counts 12 copies per thread");
     const int tid = threadIdx.x;
     const int lane = moe_lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(tid / MOE_WAVE);
+    const int wm = wave >> 2;  // tile half (128 rows) this wave computes
+    const int wn = wave & 3;   // 64 B rows (FC1: 32 gate + the matching 32 up) of the tile
     const uint32_t smem_base = (uint32_t)(uintptr_t)(lds_u8_t*)smem;
 
-    int nb = *n_blocks_ptr;
-    nb = nb < max_blocks ? nb : max_blocks;
-    const int total = nb * NT;
+    const int total = tiles[0] * NT;
     // persistent grid: XCD x (= blockIdx % 8) walks the x-th eighth of the items in order
     const int xcd = blockIdx.x % kXcds;
     const int slot = blockIdx.x / kXcds;
@@ -95,86 +212,112 @@ ffn_bf16_kernel(const uint16_t* __restrict__ A, int64_t a_rows, int Kdim,
     const int it_begin = xcd * per_xcd_items;
     const int it_end = min(total, it_begin + per_xcd_items);
 
-    // Direct-to-LDS loads: each instruction moves 64 lanes x 16 B = 8 rows of a stage.
-    // Load i of this wave fills 8-row segment (i * 4 + wave): A segments 0..15, B 16..47.
-    // Lane j writes LDS chunk j of its segment: row j/8, physical chunk j%8, which holds
-    // logical chunk (j%8) ^ (j/8) (the read-side swizzle).
+    // A copy fills one 8-row segment: lane j writes physical chunk j%8 of segment row j/8 and
+    // so fetches the logical chunk stored there.  This wave's segments all have the parity of
+    // w, which is the only part of the segment index that enters the swizzle.
     const int seg_row = lane >> 3;
-    const int seg_lchunk = (lane & 7) ^ (lane >> 3);
+    const int seg_lchunk = swz_chunk((wave & 1) * 8 + seg_row, lane & 7);
     const int nk = Kdim / BK;
 
     for (int it = it_begin + slot; it < it_end; it += per_xcd_wgs) {
-        const int b = it / NT;
-        const int nt = it - b * NT;
-        const int l = blocks[4 * b + 1];
-        const int blk_row0 = blocks[4 * b + 2];
-        const int blk_rows = blocks[4 * b + 3];
-        const uint16_t* Bexp = B + (int64_t)l * b_expert_stride;
-
-        for (int sub = 0; sub < blk_rows; sub += BM) {  // blocks of 256 rows take two tiles
-            const int row0 = blk_row0 + sub;
-            const int m = blk_rows - sub < BM ? blk_rows - sub : BM;
-
-            const uint16_t* src[LOADS_PER_STAGE];
+        const int t = it / NT;
+        const int nt = it - t * NT;
+        const int u0 = tiles[1 + 2 * t];
+        const int u1 = tiles[2 + 2 * t];
+        const bool pair = u1 >= 0;
+        const int l = blocks[4 * (u0 >> 1) + 1];
+        int h_row0[2], h_rows[2];
 #pragma unroll
-            for (int i = 0; i < LOADS_PER_STAGE; ++i) {
-                const int segm = i * 4 + wave;
-                if (segm < BM / 8) {
-                    int64_t ar = row0 + segm * 8 + seg_row;
-                    if (ar > a_rows - 1) ar = a_rows - 1;  // rows past the block: read, unused
-                    src[i] = A + ar * Kdim + seg_lchunk * 8;
-                } else {
-                    const int rr = (segm - BM / 8) * 8 + seg_row;
-                    int br;
-                    if (kSwiGLU)
-                        br = rr < BN / 2 ? nt * (BN / 2) + rr : I + nt * (BN / 2) + (rr - BN / 2);
-                    else
-                        br = nt * BN + rr;
-                    if (br > b_rows - 1) br = b_rows - 1;  // columns past H: read, not stored
-                    src[i] = Bexp + (int64_t)br * Kdim + seg_lchunk * 8;
-                }
+        for (int h = 0; h < 2; ++h) {
+            const int u = h == 0 ? u0 : u1;
+            if (u >= 0) {
+                const int sub = (u & 1) * HALF;
+                h_row0[h] = blocks[4 * (u >> 1) + 2] + sub;
+                const int r = blocks[4 * (u >> 1) + 3] - sub;
+                h_rows[h] = r < HALF ? r : HALF;
+            } else {
+                h_row0[h] = 0;
+                h_rows[h] = 0;
             }
-            auto issue = [&](int kt) {
-                const uint32_t stage = smem_base + (kt % STAGES) * STAGE_BYTES;
-#pragma unroll
-                for (int i = 0; i < LOADS_PER_STAGE; ++i)
-                    lds_dma16(src[i] + kt * BK, stage + (i * 4 + wave) * 1024);
-            };
+        }
+        const uint16_t* Bexp = B + (int64_t)l * b_expert_stride;
+        const int copies = pair ? DMA_PER_WAVE : DMA_PER_WAVE - 2;  // a half tile skips A half 1
+        const bool active = pair || wm == 0;                         // waves of an empty half idle
 
-            f32x16_t acc[4][2];
+        // per copy: a wave-uniform base (A half 0, A half 1, or the expert's B) and this
+        // lane's byte offset from it (row * Kdim * 2 + chunk * 16; < 4 GiB)
+        const uint8_t* a0 = reinterpret_cast<const uint8_t*>(A + (int64_t)h_row0[0] * Kdim);
+        const uint8_t* a1 = reinterpret_cast<const uint8_t*>(A + (int64_t)h_row0[1] * Kdim);
+        const uint8_t* bx = reinterpret_cast<const uint8_t*>(Bexp);
+        // copy q = 0..3: A segment wave + 8q (q = 0, 1: half 0; q = 2, 3: half 1);
+        // copy q = 4..7: B segment wave + 8(q-4).  off = lane's byte offset from its base.
+        uint32_t off[DMA_PER_WAVE];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int h = q >> 1;
+            int rr = ((q & 1) * 8 + wave) * SEG_ROWS + seg_row;  // row within half h
+            if (h_row0[h] + rr > a_rows - 1) rr = (int)(a_rows - 1 - h_row0[h]);  // read, unused
+            off[q] = (uint32_t)rr * (uint32_t)Kdim * 2u + seg_lchunk * 16u;
+        }
+#pragma unroll
+        for (int q = 4; q < 8; ++q) {
+            const int rr = ((q - 4) * 8 + wave) * SEG_ROWS + seg_row;  // B row in the tile
+            int br;
+            if (kSwiGLU)
+                br = rr < BN / 2 ? nt * (BN / 2) + rr : I + nt * (BN / 2) + (rr - BN / 2);
+            else
+                br = nt * BN + rr;
+            if (br > b_rows - 1) br = b_rows - 1;  // columns past the end: read, not stored
+            off[q] = (uint32_t)br * (uint32_t)Kdim * 2u + seg_lchunk * 16u;
+        }
+        auto issue = [&](int kt) {
+            const uint32_t m0 = smem_base + (kt % STAGES) * STAGE_BYTES + wave * 8192;
+            const uint32_t koff = (uint32_t)kt * (BK * 2);
+            // A: half 0 segments (copies 0, 1), half 1 segments (2, 3) only for a pair
+            four_copies(m0, a0, a0 - 1024, a1 - 2048, a1 - 3072, off[0] + koff, off[1] + koff,
+                        off[2] + koff, off[3] + koff, pair);
+            four_copies(m0 + 4096, bx, bx - 1024, bx - 2048, bx - 3072, off[4] + koff,
+                        off[5] + koff, off[6] + koff, off[7] + koff, true);
+        };
+
+        f32x16_t acc[4][2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+        // fragments double-buffered one 16-wide K step ahead of the MFMAs
+        bf16x8_t fa[2][4], fb[2][2];
+        auto load_frags = [&](int kt, int kk, int buf) {
+            const uint8_t* st = smem + (kt % STAGES) * STAGE_BYTES;
+            const int ch = kk * 2 + (lane >> 5);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int br = kSwiGLU ? j * (BN / 2) + wn * 32 + (lane & 31)
+                                       : wn * 64 + j * 32 + (lane & 31);
+                fb[buf][j] = lds_frag(st, br, true, ch);
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+                fa[buf][i] = lds_frag(st, wm * HALF + i * 32 + (lane & 31), false, ch);
+        };
+        // copies of this wave still allowed in flight when `pending` later stages are issued
+        auto pend = [&](int pending) { return pending * copies; };
 
-            __syncthreads();  // the previous tile's last LDS reads are done
-            issue(0);
-            if (nk > 1) issue(1);
+        __syncthreads();  // the previous tile's last LDS reads are done
+        const int pre = nk < STAGES ? nk : STAGES;  // every slot filled before the loop
+        for (int s = 0; s < pre; ++s) issue(s);
+        wait_copies_and_barrier(pend(pre - 1));
+        if (active) load_frags(0, 0, 0);
 
-            for (int kt = 0; kt < nk; ++kt) {
-                // slice kt has landed in every wave's share of its stage (kt+1 may be in flight)
-                if (kt + 1 < nk)
-                    MOE_WAIT_STAGE_AND_BARRIER();
-                else
-                    MOE_WAIT_ALL_AND_BARRIER();
-                if (kt + 2 < nk) issue(kt + 2);   // refills the stage read in iteration kt-1
-
-                const uint8_t* As = smem + (kt % STAGES) * STAGE_BYTES;
-                const uint8_t* Bs = As + A_STAGE_BYTES;
+        for (int kt = 0; kt < nk; ++kt) {
 #pragma unroll
-                for (int kk = 0; kk < BK / 16; ++kk) {
-                    const int ch = kk * 2 + (lane >> 5);
-                    bf16x8_t bfr[2], af[4];
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const int br = kSwiGLU ? j * (BN / 2) + wave * 32 + (lane & 31)
-                                               : wave * 64 + j * 32 + (lane & 31);
-                        bfr[j] = lds_frag(Bs, br, ch);
-                    }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) af[i] = lds_frag(As, i * 32 + (lane & 31), ch);
+            for (int kk = 0; kk < BK / 16; ++kk) {
+                const int cur = kk & 1;
+                if (active) {
+                    if (kk + 1 < BK / 16) load_frags(kt, kk + 1, cur ^ 1);
                     // D = B-rows x A-rows: lane keeps one A row and 4 consecutive columns per
                     // register group, so the epilogue stores 8 bytes at a time
 #pragma unroll
@@ -182,29 +325,40 @@ ffn_bf16_kernel(const uint16_t* __restrict__ A, int64_t a_rows, int Kdim,
 #pragma unroll
                         for (int j = 0; j < 2; ++j)
                             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                bfr[j], af[i], acc[i][j], 0, 0, 0);
+                                fb[cur][j], fa[cur][i], acc[i][j], 0, 0, 0);
+                }
+                if (kk + 1 == BK / 16 && kt + 1 < nk) {
+                    // behind slice kt's last MFMAs: wait for slice kt+1 everywhere (slices up
+                    // to kt+STAGES-1 are issued); then slice kt's stage is free for slice
+                    // kt+STAGES; first fragments of slice kt+1
+                    const int issued = kt + STAGES - 1 < nk ? kt + STAGES - 1 : nk - 1;
+                    wait_copies_and_barrier(pend(issued - (kt + 1)));
+                    if (kt + STAGES < nk) issue(kt + STAGES);
+                    if (active) load_frags(kt + 1, 0, cur ^ 1);
                 }
             }
+        }
 
-            // epilogue: acc[i][j][4g + e] = C[row i*32 + lane%32][col base + 8g + 4(lane/32) + e]
+        // epilogue: acc[i][j][4g + e] = C[row wm*128 + i*32 + lane%32][col + 8g + 4(lane/32) + e]
+        if (active) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int rl = i * 32 + (lane & 31);
-                if (rl >= m) continue;
-                uint16_t* crow = C + (int64_t)(row0 + rl) * ldc;
+                if (rl >= h_rows[wm]) continue;
+                uint16_t* crow = C + (int64_t)(h_row0[wm] + rl) * ldc;
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int c4 = 8 * g + 4 * (lane >> 5);
                     if (kSwiGLU) {
-                        float v[4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float gt = acc[i][0][4 * g + e];
-                            const float up = acc[i][1][4 * g + e];
-                            v[e] = gt / (1.f + expf(-gt)) * up;
-                        }
-                        const int col = nt * (BN / 2) + wave * 32 + c4;
+                        const int col = nt * (BN / 2) + wn * 32 + c4;
                         if (col < n_cols) {  // n_cols is a multiple of 64: all 4 or none
+                            float v[4];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const float gt = acc[i][0][4 * g + e];
+                                const float up = acc[i][1][4 * g + e];
+                                v[e] = gt / (1.f + expf(-gt)) * up;
+                            }
                             uint2 o;
                             o.x = moe_pack_bf16x2(v[0], v[1]);
                             o.y = moe_pack_bf16x2(v[2], v[3]);
@@ -213,8 +367,8 @@ ffn_bf16_kernel(const uint16_t* __restrict__ A, int64_t a_rows, int Kdim,
                     } else {
 #pragma unroll
                         for (int j = 0; j < 2; ++j) {
-                            const int col = nt * BN + wave * 64 + j * 32 + c4;
-                            if (col < n_cols) {  // n_cols is a multiple of 64: all 4 or none
+                            const int col = nt * BN + wn * 64 + j * 32 + c4;
+                            if (col < n_cols) {
                                 uint2 o;
                                 o.x = moe_pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]);
                                 o.y = moe_pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
@@ -273,22 +427,30 @@ ffn_f32_down_kernel(const float* __restrict__ act, const float* __restrict__ w2,
     }
 }
 
-int persistent_grid(int wgs_per_cu) {
+int persistent_grid() {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
         cus = 256;
-    int g = cus * wgs_per_cu;
-    g = g / kXcds * kXcds;
+    int g = cus / kXcds * kXcds;  // one workgroup per CU (128 KB of LDS each)
     return g < kXcds ? kXcds : g;
 }
 
 }  // namespace
 
+int64_t moe_ffn_workspace_elems_impl(int max_blocks) { return 1 + 4 * (int64_t)max_blocks; }
+
+hipError_t moe_launch_ffn_schedule(const int32_t* blocks, const int32_t* n_blocks, int max_blocks,
+                                   int E_loc, int32_t* ws, hipStream_t stream) {
+    ffn_schedule_kernel<<<1, 256, 0, stream>>>(blocks, n_blocks, max_blocks, E_loc, ws);
+    return hipGetLastError();
+}
+
 hipError_t moe_launch_ffn_fc1(const void* xp, const void* w1, moe_dtype_t dt, int H, int I,
                               const int32_t* blocks, const int32_t* n_blocks, int max_blocks,
-                              void* act, int64_t max_rows, hipStream_t stream) {
+                              const int32_t* ws, void* act, int64_t max_rows,
+                              hipStream_t stream) {
     if (dt == MOE_F32) {
         int grid = max_blocks < 1024 ? max_blocks : 1024;
         ffn_f32_gateup_kernel<<<grid, 256, 0, stream>>>(
@@ -296,17 +458,17 @@ hipError_t moe_launch_ffn_fc1(const void* xp, const void* w1, moe_dtype_t dt, in
             max_blocks, static_cast<float*>(act));
         return hipGetLastError();
     }
-    ffn_bf16_kernel<true><<<persistent_grid(1), kThreads, 0, stream>>>(
+    ffn_bf16_kernel<true><<<persistent_grid(), kThreads, 0, stream>>>(
         static_cast<const uint16_t*>(xp), max_rows, H, static_cast<const uint16_t*>(w1),
         (int64_t)2 * I * H, 2 * I, static_cast<uint16_t*>(act), I, I, I,
-        (I + BN / 2 - 1) / (BN / 2), blocks,
-        n_blocks, max_blocks);
+        (I + BN / 2 - 1) / (BN / 2), blocks, ws);
     return hipGetLastError();
 }
 
 hipError_t moe_launch_ffn_fc2(const void* act, const void* w2, moe_dtype_t dt, int H, int I,
                               const int32_t* blocks, const int32_t* n_blocks, int max_blocks,
-                              void* yp, int64_t max_rows, hipStream_t stream) {
+                              const int32_t* ws, void* yp, int64_t max_rows,
+                              hipStream_t stream) {
     if (dt == MOE_F32) {
         int grid = max_blocks < 1024 ? max_blocks : 1024;
         ffn_f32_down_kernel<<<grid, 256, 0, stream>>>(
@@ -314,9 +476,8 @@ hipError_t moe_launch_ffn_fc2(const void* act, const void* w2, moe_dtype_t dt, i
             n_blocks, max_blocks, static_cast<float*>(yp));
         return hipGetLastError();
     }
-    ffn_bf16_kernel<false><<<persistent_grid(1), kThreads, 0, stream>>>(
+    ffn_bf16_kernel<false><<<persistent_grid(), kThreads, 0, stream>>>(
         static_cast<const uint16_t*>(act), max_rows, I, static_cast<const uint16_t*>(w2),
-        (int64_t)H * I, H, static_cast<uint16_t*>(yp), H, H, I, (H + BN - 1) / BN, blocks,
-        n_blocks, max_blocks);
+        (int64_t)H * I, H, static_cast<uint16_t*>(yp), H, H, I, (H + BN - 1) / BN, blocks, ws);
     return hipGetLastError();
 }

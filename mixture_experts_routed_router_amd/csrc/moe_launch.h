@@ -21,13 +21,20 @@ hipError_t moe_launch_plan(const int32_t* counts, int begin, int stride, int E_l
                            int max_moves, int32_t* blocks, int32_t* n_blocks, int max_blocks,
                            int32_t* err_word, hipStream_t stream);
 
+int64_t moe_ffn_workspace_elems_impl(int max_blocks);
+
+hipError_t moe_launch_ffn_schedule(const int32_t* blocks, const int32_t* n_blocks, int max_blocks,
+                                   int E_loc, int32_t* ws, hipStream_t stream);
+
 hipError_t moe_launch_ffn_fc1(const void* xp, const void* w1, moe_dtype_t dt, int H, int I,
                               const int32_t* blocks, const int32_t* n_blocks, int max_blocks,
-                              void* act, int64_t max_rows, hipStream_t stream);
+                              const int32_t* ws, void* act, int64_t max_rows,
+                              hipStream_t stream);
 
 hipError_t moe_launch_ffn_fc2(const void* act, const void* w2, moe_dtype_t dt, int H, int I,
                               const int32_t* blocks, const int32_t* n_blocks, int max_blocks,
-                              void* yp, int64_t max_rows, hipStream_t stream);
+                              const int32_t* ws, void* yp, int64_t max_rows,
+                              hipStream_t stream);
 
 hipError_t moe_launch_combine(const void* yp, moe_dtype_t dt, const float* w,
                               const int32_t* entry_pos, int T, int H, int K, void* out,
