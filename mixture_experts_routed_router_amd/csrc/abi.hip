@@ -145,7 +145,7 @@ moe_status_t moe_expert_ffn_fc1(const void* xp, const void* w1, moe_dtype_t dt, 
 moe_status_t moe_expert_ffn_fc2(const void* act, const void* w2, moe_dtype_t dt, int H, int I,
                                 int E_loc, const int32_t* blocks, const int32_t* n_blocks,
                                 int max_blocks, void* yp, int64_t max_rows,
-                                const int32_t* workspace, int64_t workspace_elems,
+                                int32_t* workspace, int64_t workspace_elems,
                                 hipStream_t stream) {
     if (!act || !w2 || !blocks || !n_blocks || !yp || !workspace) return MOE_ERR_INVALID;
     if (!aligned16(act) || !aligned16(w2) || !aligned16(yp)) return MOE_ERR_INVALID;

@@ -36,6 +36,10 @@ constexpr int STAGES = 2;    // LDS ring depth (one slice consumed while the nex
 constexpr int kWaves = 8;    // two waves per SIMD
 constexpr int kThreads = kWaves * MOE_WAVE;
 constexpr int kXcds = 8;
+// FFN workspace (int32): [0] tile count; [8 + x] FC1 item counter of XCD x, [16 + x] FC2's;
+// [24] FC1 / [25] FC2 finished-workgroup counters; tiles from [32] on (two units each).
+constexpr int WS_NTILES = 0, WS_CTR_FC1 = 8, WS_CTR_FC2 = 16, WS_DONE_FC1 = 24, WS_DONE_FC2 = 25;
+constexpr int WS_TILES = 32;
 constexpr int ROW_BYTES = BK * 2;                           // 128
 constexpr int A_STAGE_BYTES = BM * ROW_BYTES;               // 32 KB
 constexpr int B_STAGE_BYTES = BN * ROW_BYTES;               // 32 KB
@@ -126,12 +130,13 @@ __device__ __forceinline__ void wait_copies_and_barrier(int n) {
 
 // One workgroup.  The unit of pairing is a 128-row piece of a block: unit 2b + s covers rows
 // [first_b + 128 s, first_b + min(rows_b, 128 (s + 1))) of block b (s = 1 exists only for a
-// block of more than 128 rows).  tiles[0] = tile count; tile t = (tiles[1 + 2t],
-// tiles[2 + 2t]) = its two units (second = -1 for a half tile).  An expert's units are paired
-// in table order; experts follow one another in ascending local id.
+// block of more than 128 rows).  Output in the workspace: ws[WS_NTILES] = tile count; tile t
+// = (ws[WS_TILES + 2t], ws[WS_TILES + 2t + 1]) = its two units (second = -1 for a half tile).
+// An expert's units are paired in table order; experts follow one another in ascending local
+// id.  The GEMMs' item and finished counters are cleared too.
 __global__ void __launch_bounds__(256)
 ffn_schedule_kernel(const int32_t* __restrict__ blocks, const int32_t* __restrict__ n_blocks_ptr,
-                    int max_blocks, int E_loc, int32_t* __restrict__ tiles) {
+                    int max_blocks, int E_loc, int32_t* __restrict__ ws) {
     __shared__ int cnt[256];
     __shared__ int tstart[257];
     __shared__ int running[256];
@@ -139,6 +144,7 @@ ffn_schedule_kernel(const int32_t* __restrict__ blocks, const int32_t* __restric
     const int tid = threadIdx.x, lane = moe_lane_id(), wave = tid / MOE_WAVE;
     int nb = *n_blocks_ptr;
     nb = nb < max_blocks ? nb : max_blocks;
+    if (tid >= WS_CTR_FC1 && tid < WS_TILES) ws[tid] = 0;  // item and finished counters
     for (int l = tid; l < E_loc; l += 256) {
         cnt[l] = 0;
         running[l] = 0;
@@ -154,7 +160,7 @@ ffn_schedule_kernel(const int32_t* __restrict__ blocks, const int32_t* __restric
             s += (cnt[l] + 1) / 2;
         }
         tstart[E_loc] = s;
-        tiles[0] = s;
+        ws[WS_NTILES] = s;
     }
     __syncthreads();
     // stable rank of each unit among its expert's units, 256 units per round
@@ -170,7 +176,7 @@ ffn_schedule_kernel(const int32_t* __restrict__ blocks, const int32_t* __restric
         if (l >= 0) {
             int pos = running[l] + __popcll(mask[wave][l] & ((1ull << lane) - 1ull));
             for (int w = 0; w < wave; ++w) pos += __popcll(mask[w][l]);
-            tiles[1 + 2 * (tstart[l] + pos / 2) + (pos & 1)] = u;
+            ws[WS_TILES + 2 * (tstart[l] + pos / 2) + (pos & 1)] = u;
         }
         __syncthreads();
         for (int e = tid; e < E_loc; e += 256)
@@ -179,7 +185,7 @@ ffn_schedule_kernel(const int32_t* __restrict__ blocks, const int32_t* __restric
         __syncthreads();
     }
     for (int e = tid; e < E_loc; e += 256)
-        if (cnt[e] & 1) tiles[1 + 2 * (tstart[e] + cnt[e] / 2) + 1] = -1;
+        if (cnt[e] & 1) ws[WS_TILES + 2 * (tstart[e] + cnt[e] / 2) + 1] = -1;
 }
 
 // ------------------------------------------------------------------ grouped GEMMs ---
@@ -193,8 +199,11 @@ __global__ void __launch_bounds__(kThreads, 1)
 ffn_bf16_kernel(const uint16_t* __restrict__ A, int64_t a_rows, int Kdim,
                 const uint16_t* __restrict__ B, int64_t b_expert_stride, int b_rows,
                 uint16_t* __restrict__ C, int ldc, int n_cols, int I, int NT,
-                const int32_t* __restrict__ blocks, const int32_t* __restrict__ tiles) {
+                const int32_t* __restrict__ blocks, int32_t* __restrict__ ws) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
+    __shared__ int item_s;
+    const int32_t* tiles = ws + WS_TILES;
+    int32_t* ctr = ws + (kSwiGLU ? WS_CTR_FC1 : WS_CTR_FC2);
 
     const int tid = threadIdx.x;
     const int lane = moe_lane_id();
@@ -203,14 +212,13 @@ ffn_bf16_kernel(const uint16_t* __restrict__ A, int64_t a_rows, int Kdim,
     const int wn = wave & 3;   // 64 B rows (FC1: 32 gate + the matching 32 up) of the tile
     const uint32_t smem_base = (uint32_t)(uintptr_t)(lds_u8_t*)smem;
 
-    const int total = tiles[0] * NT;
-    // persistent grid: XCD x (= blockIdx % 8) walks the x-th eighth of the items in order
+    const int total = ws[WS_NTILES] * NT;
+    // Items (tile, column tile) in tile-major order are cut into 8 contiguous ranges, one per
+    // XCD (workgroup w runs on XCD w % 8), so the items in flight on an XCD share A rows and
+    // B rows in its L2.  Workgroups take items from their XCD's range through an atomic
+    // counter (in order, self-balancing); a workgroup whose range is drained helps the others.
     const int xcd = blockIdx.x % kXcds;
-    const int slot = blockIdx.x / kXcds;
-    const int per_xcd_wgs = gridDim.x / kXcds;
     const int per_xcd_items = (total + kXcds - 1) / kXcds;
-    const int it_begin = xcd * per_xcd_items;
-    const int it_end = min(total, it_begin + per_xcd_items);
 
     // A copy fills one 8-row segment: lane j writes physical chunk j%8 of segment row j/8 and
     // so fetches the logical chunk stored there.  This wave's segments all have the parity of
@@ -219,11 +227,28 @@ ffn_bf16_kernel(const uint16_t* __restrict__ A, int64_t a_rows, int Kdim,
     const int seg_lchunk = swz_chunk((wave & 1) * 8 + seg_row, lane & 7);
     const int nk = Kdim / BK;
 
-    for (int it = it_begin + slot; it < it_end; it += per_xcd_wgs) {
+    int q = 0;  // queues tried: own XCD first, then the others in turn
+    for (;;) {
+        if (tid == 0) {
+            int got = -1;
+            for (; q < kXcds; ++q) {
+                const int x = (xcd + q) % kXcds;
+                const int k = atomicAdd(&ctr[x], 1);
+                const int it = x * per_xcd_items + k;
+                if (k < per_xcd_items && it < total) {
+                    got = it;
+                    break;
+                }
+            }
+            item_s = got;
+        }
+        __syncthreads();
+        const int it = item_s;
+        if (it < 0) break;
         const int t = it / NT;
         const int nt = it - t * NT;
-        const int u0 = tiles[1 + 2 * t];
-        const int u1 = tiles[2 + 2 * t];
+        const int u0 = tiles[2 * t];
+        const int u1 = tiles[2 * t + 1];
         const bool pair = u1 >= 0;
         const int l = blocks[4 * (u0 >> 1) + 1];
         int h_row0[2], h_rows[2];
@@ -379,6 +404,15 @@ ffn_bf16_kernel(const uint16_t* __restrict__ A, int64_t a_rows, int Kdim,
                 }
             }
         }
+        __syncthreads();  // everyone has read item_s before thread 0 takes the next item
+    }
+    // the last workgroup out clears this GEMM's counters so the kernel can run again
+    if (tid == 0) {
+        int32_t* done = ws + (kSwiGLU ? WS_DONE_FC1 : WS_DONE_FC2);
+        if (atomicAdd(done, 1) == (int)gridDim.x - 1) {
+            for (int x = 0; x < kXcds; ++x) atomicExch(&ctr[x], 0);
+            atomicExch(done, 0);
+        }
     }
 }
 
@@ -439,7 +473,7 @@ int persistent_grid() {
 
 }  // namespace
 
-int64_t moe_ffn_workspace_elems_impl(int max_blocks) { return 1 + 4 * (int64_t)max_blocks; }
+int64_t moe_ffn_workspace_elems_impl(int max_blocks) { return WS_TILES + 4 * (int64_t)max_blocks; }
 
 hipError_t moe_launch_ffn_schedule(const int32_t* blocks, const int32_t* n_blocks, int max_blocks,
                                    int E_loc, int32_t* ws, hipStream_t stream) {
@@ -449,7 +483,7 @@ hipError_t moe_launch_ffn_schedule(const int32_t* blocks, const int32_t* n_block
 
 hipError_t moe_launch_ffn_fc1(const void* xp, const void* w1, moe_dtype_t dt, int H, int I,
                               const int32_t* blocks, const int32_t* n_blocks, int max_blocks,
-                              const int32_t* ws, void* act, int64_t max_rows,
+                              int32_t* ws, void* act, int64_t max_rows,
                               hipStream_t stream) {
     if (dt == MOE_F32) {
         int grid = max_blocks < 1024 ? max_blocks : 1024;
@@ -467,7 +501,7 @@ hipError_t moe_launch_ffn_fc1(const void* xp, const void* w1, moe_dtype_t dt, in
 
 hipError_t moe_launch_ffn_fc2(const void* act, const void* w2, moe_dtype_t dt, int H, int I,
                               const int32_t* blocks, const int32_t* n_blocks, int max_blocks,
-                              const int32_t* ws, void* yp, int64_t max_rows,
+                              int32_t* ws, void* yp, int64_t max_rows,
                               hipStream_t stream) {
     if (dt == MOE_F32) {
         int grid = max_blocks < 1024 ? max_blocks : 1024;

@@ -28,12 +28,12 @@ hipError_t moe_launch_ffn_schedule(const int32_t* blocks, const int32_t* n_block
 
 hipError_t moe_launch_ffn_fc1(const void* xp, const void* w1, moe_dtype_t dt, int H, int I,
                               const int32_t* blocks, const int32_t* n_blocks, int max_blocks,
-                              const int32_t* ws, void* act, int64_t max_rows,
+                              int32_t* ws, void* act, int64_t max_rows,
                               hipStream_t stream);
 
 hipError_t moe_launch_ffn_fc2(const void* act, const void* w2, moe_dtype_t dt, int H, int I,
                               const int32_t* blocks, const int32_t* n_blocks, int max_blocks,
-                              const int32_t* ws, void* yp, int64_t max_rows,
+                              int32_t* ws, void* yp, int64_t max_rows,
                               hipStream_t stream);
 
 hipError_t moe_launch_combine(const void* yp, moe_dtype_t dt, const float* w,
