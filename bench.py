@@ -17,6 +17,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -33,8 +35,14 @@ def parse():
     ap.add_argument("--workload", default="olmoe_shaped")
     ap.add_argument("--skew", default=None, help="Zipf exponent or 'hot4' (default: middle skew)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (tokens)")
-    ap.add_argument("--all-skews", action="store_true", help="also time every skew of the workload")
+    ap.add_argument("--cpu-tokens", type=int, default=0,
+                    help="tokens of the oracle's sizing pass (the measured sample is scaled to "
+                         "about 12 s of CPU work)")
+    ap.add_argument("--no-all-skews", action="store_true",
+                    help="skip timing every skew of the workload (the by_skew field)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (a reference for "
+                         "hardware byte counters)")
     return ap.parse_args()
 
 
@@ -107,30 +115,40 @@ def ffn_traffic(workload: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, skew, T_s):
-    """The CPU oracle, as it stands, over the first T_s tokens of the same batch (whole path)."""
-    import numpy as np
+def cpu_baseline(w, skew, T_s, target_s=12.0):
+    """The CPU oracle, as it stands, over the first tokens of the same batch (whole path).
+    A first pass over T_s tokens sizes the measured sample to about target_s seconds of CPU
+    work (at most the whole batch, a multiple of P tokens)."""
     sys.path.insert(0, os.path.join(ROOT, "oracle"))
     import oracle
     from mixture_experts_routed_router_amd import inputs
 
-    logits = inputs.make_logits(w, skew)[:T_s].copy()
-    x = inputs.as_oracle_array(inputs.make_x(w)[:T_s].contiguous())
+    logits_all = inputs.make_logits(w, skew)
+    x_all = inputs.as_oracle_array(inputs.make_x(w))
     W1, W2 = (inputs.as_oracle_array(t) for t in inputs.make_weights(w, threads=16))
     oracle.build()
-    t0 = time.perf_counter()
-    ids, wt, counts = oracle.route(logits, w.K)
-    _, ep, _, xp = oracle.permute(ids, counts, w.E, w.expert_begin, w.expert_stride, w.n_local,
-                                  w.beta, x)
-    _, _, blocks = oracle.plan(counts, w.E, w.expert_begin, w.expert_stride, w.n_local, w.P,
-                               w.beta)
-    _, yp = oracle.ffn_blocks(xp, W1, W2, blocks)
-    oracle.combine(yp, wt, ep, T_s, w.K)
-    dt = time.perf_counter() - t0
-    return {"value": round(T_s / dt, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
+
+    def run(n):
+        logits = np.ascontiguousarray(logits_all[:n])
+        x = np.ascontiguousarray(x_all[:n])
+        t0 = time.perf_counter()
+        ids, wt, counts = oracle.route(logits, w.K)
+        _, ep, _, xp = oracle.permute(ids, counts, w.E, w.expert_begin, w.expert_stride,
+                                      w.n_local, w.beta, x)
+        _, _, blocks = oracle.plan(counts, w.E, w.expert_begin, w.expert_stride, w.n_local, w.P,
+                                   w.beta)
+        _, yp = oracle.ffn_blocks(xp, W1, W2, blocks)
+        oracle.combine(yp, wt, ep, n, w.K)
+        return time.perf_counter() - t0
+
+    t_probe = run(T_s)
+    n = int(T_s * target_s / max(t_probe, 1e-6))
+    n = max(w.P, min(w.T, n) // w.P * w.P)
+    dt = run(n) if n != T_s else t_probe
+    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"first {T_s} tokens of the same batch, whole path (route, permute, plan, "
-                      f"FFN, combine), float64 plain C, {dt:.1f} s"}
+            "sample": f"first {n} of {w.T} tokens of the same batch, whole path (route, permute, "
+                      f"plan, FFN, combine), float64 plain C with OpenMP, {dt:.1f} s"}
 
 
 def main():
@@ -157,6 +175,14 @@ def main():
     layer = binding.RoutedExperts(w.T, w.H, w.E, w.K, w.I, w.P, dtype=dt, E_loc=w.n_local,
                                   expert_begin=w.expert_begin, expert_stride=w.expert_stride,
                                   block_m=w.beta)
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def measure(sk, steps, warmup):
         logits = torch.from_numpy(inputs.make_logits(w, sk)).to(dev)
@@ -210,7 +236,7 @@ def main():
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
     }
-    if args.all_skews:
+    if not args.no_all_skews:
         by = []
         for sk in w.skews:
             wl, pr, n_, nb_, _ = measure(sk, max(5, args.steps // 2), 2)
@@ -220,9 +246,9 @@ def main():
                        "gemm_tflops": round(f / ((pr["fc1"] + pr["fc2"]) * 1e-6) / 1e12, 1)})
         line["by_skew"] = by
     if not args.no_cpu_baseline:
-        T_s = args.cpu_tokens or {"tiny_f32": 64, "olmoe_shaped": 1024,
-                                  "qwen3_30b_a3b_shaped": 1024, "gpt_oss_120b_shaped": 256,
-                                  "gpt_oss_120b_decode": 64, "deepseek_v3_share": 1024}[w.name]
+        T_s = args.cpu_tokens or {"tiny_f32": 64, "olmoe_shaped": 256,
+                                  "qwen3_30b_a3b_shaped": 256, "gpt_oss_120b_shaped": 64,
+                                  "gpt_oss_120b_decode": 64, "deepseek_v3_share": 256}[w.name]
         T_s = max(w.P, T_s // w.P * w.P)
         del layer
         torch.cuda.empty_cache()
