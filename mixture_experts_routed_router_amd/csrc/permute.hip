@@ -4,7 +4,7 @@
 // source and (token, top-k slot), i.e. the flat entry index t*K + k, and the rows are cut into
 // blocks of at most beta rows; each expert's segment therefore starts on a multiple of beta.
 //
-// Three launches, all without order-dependent atomics:
+// Four launches, all without order-dependent atomics:
 //   hist    per chunk of 16 tokens, the number of entries of each local expert (LDS counts);
 //   scan    one workgroup per local expert: the padded segment start, an exclusive scan of
 //           the expert's chunk counts (so each chunk knows where its rows begin), and -1 in
@@ -12,8 +12,9 @@
 //   scatter one workgroup per chunk: an entry's rank inside the chunk is the number of
 //           earlier tokens of the chunk that picked the same expert, read off a 16-bit token
 //           mask per expert (a token's K experts are distinct, so each (token, expert) pair
-//           is one entry); then every token row of x is read once and written to each of its
-//           local rows of xp with 16-byte accesses (HBM-bound part).
+//           is one entry); writes entry_pos and row_token;
+//   copy    each token row of x that has a local entry is read once and written to each of
+//           its local rows of xp, 16 bytes per thread (the HBM-bound part).
 #include "moe_launch.h"
 
 namespace {
@@ -99,16 +100,14 @@ permute_scan_kernel(const int32_t* __restrict__ counts, int begin, int stride, i
     for (int p = off + n_l + tid; p < off + seg; p += kThreads) row_token[p] = -1;
 }
 
-// Block c: rows of the entries of tokens [16c, 16c + 16), then the row copy.
+// Block c: rows of the entries of tokens [16c, 16c + 16).
 __global__ void __launch_bounds__(kThreads)
-permute_scatter_kernel(const uint8_t* __restrict__ x, int64_t row_bytes,
-                       const int32_t* __restrict__ ids, int T, int K, int begin, int stride,
+permute_scatter_kernel(const int32_t* __restrict__ ids, int T, int K, int begin, int stride,
                        int E_loc, const int32_t* __restrict__ ws,
                        const int32_t* __restrict__ offsets, int32_t* __restrict__ entry_pos,
-                       int32_t* __restrict__ row_token, uint8_t* __restrict__ xp) {
+                       int32_t* __restrict__ row_token) {
     __shared__ uint32_t mask[256];
     __shared__ int base[256];
-    __shared__ int pos_s[kChunk * MOE_MAX_K];
     const int c = blockIdx.x;
     const int tid = threadIdx.x;
     const int t0 = c * kChunk;
@@ -136,25 +135,32 @@ permute_scatter_kernel(const uint8_t* __restrict__ x, int64_t row_bytes,
             row_token[p] = t;
         }
         entry_pos[(size_t)t * K + k] = p;
-        pos_s[j * K + k] = p;
     }
-    __syncthreads();
+}
 
-    // row copy: each wave moves whole token rows, 16 bytes per lane per step
-    const int lane = moe_lane_id();
-    const int wave = tid / MOE_WAVE;
-    const int nt = min(kChunk, T - t0);
-    for (int jj = wave; jj < nt; jj += kThreads / MOE_WAVE) {
-        const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)(t0 + jj) * row_bytes);
-        const int n16 = (int)(row_bytes / 16);
-#pragma unroll 4
-        for (int i = lane; i < n16; i += MOE_WAVE) {
-            uint4 v = src[i];
-            for (int kk = 0; kk < K; ++kk) {
-                int p = pos_s[jj * K + kk];
-                if (p >= 0) reinterpret_cast<uint4*>(xp + (size_t)p * row_bytes)[i] = v;
-            }
+// Row copy: block b moves 16-byte chunks [256 s, 256 s + 256) of token t's row (b = t * segs + s)
+// to each of the token's local rows.  entry_pos of a token is block-uniform (scalar loads);
+// a token with no local entry is not read.
+__global__ void __launch_bounds__(kThreads)
+permute_copy_kernel(const uint8_t* __restrict__ x, int64_t row_bytes, int T, int K, int segs,
+                    const int32_t* __restrict__ entry_pos, uint8_t* __restrict__ xp) {
+    const int n16 = (int)(row_bytes / 16);
+    const int64_t total = (int64_t)T * segs;
+    for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
+        const int t = (int)(b / segs);
+        const int c = (int)(b - (int64_t)t * segs) * kThreads + threadIdx.x;
+        int pos[MOE_MAX_K];
+        bool any = false;
+#pragma unroll
+        for (int k = 0; k < MOE_MAX_K; ++k) {
+            pos[k] = k < K ? entry_pos[(int64_t)t * K + k] : -1;
+            any |= pos[k] >= 0;
         }
+        if (!any || c >= n16) continue;
+        const uint4 v = reinterpret_cast<const uint4*>(x + (int64_t)t * row_bytes)[c];
+#pragma unroll
+        for (int k = 0; k < MOE_MAX_K; ++k)
+            if (pos[k] >= 0) reinterpret_cast<uint4*>(xp + (int64_t)pos[k] * row_bytes)[c] = v;
     }
 }
 
@@ -169,8 +175,13 @@ hipError_t moe_launch_permute(const void* x, int64_t row_bytes, int T, int K,
         ids, T, K, begin, stride, E_loc, n_chunks, ws);
     permute_scan_kernel<<<E_loc, kThreads, 0, stream>>>(counts, begin, stride, E_loc, beta,
                                                          n_chunks, ws, offsets, row_token);
-    permute_scatter_kernel<<<n_chunks, kThreads, 0, stream>>>(
-        static_cast<const uint8_t*>(x), row_bytes, ids, T, K, begin, stride, E_loc, ws, offsets,
-        entry_pos, row_token, static_cast<uint8_t*>(xp));
+    permute_scatter_kernel<<<n_chunks, kThreads, 0, stream>>>(ids, T, K, begin, stride, E_loc, ws,
+                                                               offsets, entry_pos, row_token);
+    const int segs = (int)((row_bytes / 16 + kThreads - 1) / kThreads);
+    int64_t grid = (int64_t)T * segs;
+    if (grid > 65536) grid = 65536;
+    permute_copy_kernel<<<(int)grid, kThreads, 0, stream>>>(static_cast<const uint8_t*>(x),
+                                                          row_bytes, T, K, segs, entry_pos,
+                                                          static_cast<uint8_t*>(xp));
     return hipGetLastError();
 }
