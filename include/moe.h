@@ -74,7 +74,7 @@ int32_t moe_max_moves(int E_loc, int P);
 int64_t moe_permute_workspace_elems(int T, int E_loc);
 
 /* int32 elements of scratch that moe_expert_ffn needs (its GEMM tile schedule):
- * 32 + 4 * max_blocks. */
+ * 32 + 11 * max_blocks. */
 int64_t moe_ffn_workspace_elems(int max_blocks);
 
 /* ------------------------------------------------------------------------ route --- */
@@ -155,8 +155,8 @@ moe_status_t moe_plan(const int32_t* expert_counts, int E, int expert_begin,
  *   blocks/n_blocks from moe_plan (n_blocks read on the device; max_blocks bounds it);
  *   act [max_rows, I] out; yp [max_rows, H] out; rows no block covers are untouched;
  *   workspace  int32 scratch, workspace_elems >= moe_ffn_workspace_elems(max_blocks); the
- *       bf16 path keeps its tile schedule there (128-row pieces of one expert's blocks paired
- *       into 256-row GEMM tiles) and the GEMMs' work counters; calls that share one
+ *       bf16 path keeps its tile schedule there (each expert's row-contiguous blocks cut into
+ *       128-row pieces, paired into 256-row GEMM tiles) and the GEMMs' work counters; calls that share one
  *       workspace must not overlap (use one workspace per stream).
  * bf16 needs H and I to be multiples of 64; float32 needs multiples of 4.  E_loc <= 256. */
 moe_status_t moe_expert_ffn(const void* xp, const void* w1, const void* w2, moe_dtype_t dt,

@@ -7,22 +7,24 @@
 // listing) describes.
 //
 // bf16 path: a schedule pass, then two grouped GEMMs on v_mfma_f32_32x32x16_bf16.
-//   schedule: pairs each expert's blocks (in table order) into 256-row tiles of two <=128-row
-//             halves with independent row bases; an expert with an odd block count ends with
-//             a half tile.  Tiles are listed expert by expert.
+//   schedule: each expert's row-contiguous blocks are cut into 128-row pieces and paired into
+//             256-row tiles of two halves with independent row bases; an expert with an odd
+//             piece count ends with a half tile.  Tiles are listed expert by expert.
 //   FC1:      per (tile, 128 act columns): A = the tile's xp rows, B = 128 gate rows of W1[l]
 //             and the matching 128 up rows; act = SiLU(g) * u in registers, bf16 store.
 //   FC2:      per (tile, 256 columns of H): A = act rows, B = 256 rows of W2[l].
 // Why 256 x 256: a CU fills LDS from L2 at roughly 14-20 B/clk (bounded by outstanding L1
 // misses times L2 latency), while its four SIMDs consume 4096 flop/clk; a tile must therefore
 // do >= ~200 flop per staged byte to approach the MFMA roof.  256 x 256 gives 128 flop/B at
-// one workgroup (256 accumulators per lane, in AGPRs) per CU; 128 x 256 gave 85.
+// one workgroup (256 accumulators per lane) per CU; 128 x 256 gave 85.
 // Both operands are K-contiguous (C = A * B^T), so an MFMA fragment is one 16-byte LDS read.
-// K is staged in 32-wide slices through a 4-deep LDS ring filled by gfx950 direct-to-LDS
-// loads (three slices in flight while one is consumed), with one wait + barrier per slice
-// placed behind that slice's last MFMAs.  Each wave owns all 256 rows x 64 B rows.  The grid
-// is persistent: workgroup w runs on XCD w % 8 and walks a contiguous eighth of the
-// (tile, column tile) items, so concurrent items share A rows and B rows in that XCD's L2.
+// K is staged in 64-wide slices (128-byte rows: whole cache lines) through a 2-deep LDS ring
+// filled by gfx950 direct-to-LDS loads, one slice in flight while the other is consumed, with
+// one wait + barrier per slice placed behind that slice's last MFMAs.  The grid is
+// persistent, one workgroup per CU: workgroup w runs on XCD w % 8 and takes (tile, column
+// tile) items from its XCD's contiguous eighth of the item list through an atomic counter,
+// so the items in flight on an XCD share A rows and B rows in its L2; a workgroup whose
+// eighth is drained takes items from the other XCDs' eighths.
 // Block and tile counts are read on the device; there is no host round trip.
 #include "moe_launch.h"
 
@@ -37,9 +39,12 @@ constexpr int kWaves = 8;    // two waves per SIMD
 constexpr int kThreads = kWaves * MOE_WAVE;
 constexpr int kXcds = 8;
 // FFN workspace (int32): [0] tile count; [8 + x] FC1 item counter of XCD x, [16 + x] FC2's;
-// [24] FC1 / [25] FC2 finished-workgroup counters; tiles from [32] on (two units each).
+// [24] FC1 / [25] FC2 finished-workgroup counters; from [32]: max_blocks block indices
+// sorted by expert, then the tiles, 5 ints each (expert, first row and row count of half 0,
+// first row and row count of half 1; count 0 = no half 1).
 constexpr int WS_NTILES = 0, WS_CTR_FC1 = 8, WS_CTR_FC2 = 16, WS_DONE_FC1 = 24, WS_DONE_FC2 = 25;
-constexpr int WS_TILES = 32;
+constexpr int WS_HEAD = 32;
+constexpr int TILE_INTS = 5;
 constexpr int ROW_BYTES = BK * 2;                           // 128
 constexpr int A_STAGE_BYTES = BM * ROW_BYTES;               // 32 KB
 constexpr int B_STAGE_BYTES = BN * ROW_BYTES;               // 32 KB
@@ -128,55 +133,55 @@ __device__ __forceinline__ void wait_copies_and_barrier(int n) {
 
 // ------------------------------------------------------------------ tile schedule ---
 
-// One workgroup.  The unit of pairing is a 128-row piece of a block: unit 2b + s covers rows
-// [first_b + 128 s, first_b + min(rows_b, 128 (s + 1))) of block b (s = 1 exists only for a
-// block of more than 128 rows).  Output in the workspace: ws[WS_NTILES] = tile count; tile t
-// = (ws[WS_TILES + 2t], ws[WS_TILES + 2t + 1]) = its two units (second = -1 for a half tile).
-// An expert's units are paired in table order; experts follow one another in ascending local
-// id.  The GEMMs' item and finished counters are cleared too.
+// One workgroup.  The blocks of each expert are taken in table order (a stable counting sort
+// by expert); consecutive blocks whose rows are contiguous form one run (the plan's shares of
+// an expert are consecutive ranges of its segment, so a whole table gives one run per
+// expert).  Each run is cut into 128-row pieces from its start, and an expert's pieces are
+// paired in order into 256-row tiles (an odd last piece is a half tile).  Experts follow one
+// another in ascending local id.  The GEMMs' item and finished counters are cleared too.
 __global__ void __launch_bounds__(256)
 ffn_schedule_kernel(const int32_t* __restrict__ blocks, const int32_t* __restrict__ n_blocks_ptr,
                     int max_blocks, int E_loc, int32_t* __restrict__ ws) {
     __shared__ int cnt[256];
+    __shared__ int bstart[257];
+    __shared__ int npieces[256];
     __shared__ int tstart[257];
     __shared__ int running[256];
     __shared__ unsigned long long mask[4][256];
     const int tid = threadIdx.x, lane = moe_lane_id(), wave = tid / MOE_WAVE;
+    int32_t* sorted = ws + WS_HEAD;
+    int32_t* tiles = ws + WS_HEAD + max_blocks;
     int nb = *n_blocks_ptr;
     nb = nb < max_blocks ? nb : max_blocks;
-    if (tid >= WS_CTR_FC1 && tid < WS_TILES) ws[tid] = 0;  // item and finished counters
+    if (tid >= WS_CTR_FC1 && tid < WS_HEAD) ws[tid] = 0;  // item and finished counters
     for (int l = tid; l < E_loc; l += 256) {
         cnt[l] = 0;
         running[l] = 0;
     }
     __syncthreads();
-    for (int b = tid; b < nb; b += 256)
-        atomicAdd(&cnt[blocks[4 * b + 1]], blocks[4 * b + 3] > HALF ? 2 : 1);
+    for (int b = tid; b < nb; b += 256) atomicAdd(&cnt[blocks[4 * b + 1]], 1);
     __syncthreads();
-    if (tid == 0) {  // tile starts per expert (<= 256 experts: a short serial scan)
+    if (tid == 0) {
         int s = 0;
         for (int l = 0; l < E_loc; ++l) {
-            tstart[l] = s;
-            s += (cnt[l] + 1) / 2;
+            bstart[l] = s;
+            s += cnt[l];
         }
-        tstart[E_loc] = s;
-        ws[WS_NTILES] = s;
+        bstart[E_loc] = s;
     }
     __syncthreads();
-    // stable rank of each unit among its expert's units, 256 units per round
-    for (int u0 = 0; u0 < 2 * nb; u0 += 256) {
+    // stable counting sort of the blocks by expert, 256 blocks per round
+    for (int b0 = 0; b0 < nb; b0 += 256) {
         for (int i = tid; i < 4 * 256; i += 256) mask[i / 256][i % 256] = 0ull;
         __syncthreads();
-        const int u = u0 + tid;
-        const int b = u >> 1;
-        int l = -1;
-        if (b < nb && ((u & 1) == 0 || blocks[4 * b + 3] > HALF)) l = blocks[4 * b + 1];
+        const int b = b0 + tid;
+        const int l = b < nb ? blocks[4 * b + 1] : -1;
         if (l >= 0) atomicOr(&mask[wave][l], 1ull << lane);
         __syncthreads();
         if (l >= 0) {
             int pos = running[l] + __popcll(mask[wave][l] & ((1ull << lane) - 1ull));
             for (int w = 0; w < wave; ++w) pos += __popcll(mask[w][l]);
-            ws[WS_TILES + 2 * (tstart[l] + pos / 2) + (pos & 1)] = u;
+            sorted[bstart[l] + pos] = b;
         }
         __syncthreads();
         for (int e = tid; e < E_loc; e += 256)
@@ -184,8 +189,66 @@ ffn_schedule_kernel(const int32_t* __restrict__ blocks, const int32_t* __restric
                           __popcll(mask[3][e]);
         __syncthreads();
     }
-    for (int e = tid; e < E_loc; e += 256)
-        if (cnt[e] & 1) ws[WS_TILES + 2 * (tstart[e] + cnt[e] / 2) + 1] = -1;
+    // pieces per expert: walk its blocks, joining row-contiguous ones into runs
+    for (int l = tid; l < E_loc; l += 256) {
+        int pieces = 0, run_first = 0, run_rows = 0;
+        for (int i = bstart[l]; i < bstart[l + 1]; ++i) {
+            const int b = sorted[i];
+            const int first = blocks[4 * b + 2], rows = blocks[4 * b + 3];
+            if (run_rows > 0 && first == run_first + run_rows) {
+                run_rows += rows;
+            } else {
+                pieces += (run_rows + HALF - 1) / HALF;
+                run_first = first;
+                run_rows = rows;
+            }
+        }
+        pieces += (run_rows + HALF - 1) / HALF;
+        npieces[l] = pieces;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int s = 0;
+        for (int l = 0; l < E_loc; ++l) {
+            tstart[l] = s;
+            s += (npieces[l] + 1) / 2;
+        }
+        tstart[E_loc] = s;
+        ws[WS_NTILES] = s;
+    }
+    __syncthreads();
+    // emit the tiles: pieces of an expert in order, two per tile
+    for (int l = tid; l < E_loc; l += 256) {
+        int piece = 0, run_first = 0, run_rows = 0;
+        auto emit_run = [&]() {
+            for (int off = 0; off < run_rows; off += HALF, ++piece) {
+                int32_t* t = tiles + TILE_INTS * (tstart[l] + piece / 2);
+                const int rows = run_rows - off < HALF ? run_rows - off : HALF;
+                if ((piece & 1) == 0) {
+                    t[0] = l;
+                    t[1] = run_first + off;
+                    t[2] = rows;
+                    t[3] = 0;
+                    t[4] = 0;
+                } else {
+                    t[3] = run_first + off;
+                    t[4] = rows;
+                }
+            }
+        };
+        for (int i = bstart[l]; i < bstart[l + 1]; ++i) {
+            const int b = sorted[i];
+            const int first = blocks[4 * b + 2], rows = blocks[4 * b + 3];
+            if (run_rows > 0 && first == run_first + run_rows) {
+                run_rows += rows;
+            } else {
+                emit_run();
+                run_first = first;
+                run_rows = rows;
+            }
+        }
+        emit_run();
+    }
 }
 
 // ------------------------------------------------------------------ grouped GEMMs ---
@@ -199,10 +262,10 @@ __global__ void __launch_bounds__(kThreads, 1)
 ffn_bf16_kernel(const uint16_t* __restrict__ A, int64_t a_rows, int Kdim,
                 const uint16_t* __restrict__ B, int64_t b_expert_stride, int b_rows,
                 uint16_t* __restrict__ C, int ldc, int n_cols, int I, int NT,
-                const int32_t* __restrict__ blocks, int32_t* __restrict__ ws) {
+                int max_blocks, int32_t* __restrict__ ws) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
     __shared__ int item_s;
-    const int32_t* tiles = ws + WS_TILES;
+    const int32_t* tiles = ws + WS_HEAD + max_blocks;
     int32_t* ctr = ws + (kSwiGLU ? WS_CTR_FC1 : WS_CTR_FC2);
 
     const int tid = threadIdx.x;
@@ -247,24 +310,11 @@ ffn_bf16_kernel(const uint16_t* __restrict__ A, int64_t a_rows, int Kdim,
         if (it < 0) break;
         const int t = it / NT;
         const int nt = it - t * NT;
-        const int u0 = tiles[2 * t];
-        const int u1 = tiles[2 * t + 1];
-        const bool pair = u1 >= 0;
-        const int l = blocks[4 * (u0 >> 1) + 1];
-        int h_row0[2], h_rows[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int u = h == 0 ? u0 : u1;
-            if (u >= 0) {
-                const int sub = (u & 1) * HALF;
-                h_row0[h] = blocks[4 * (u >> 1) + 2] + sub;
-                const int r = blocks[4 * (u >> 1) + 3] - sub;
-                h_rows[h] = r < HALF ? r : HALF;
-            } else {
-                h_row0[h] = 0;
-                h_rows[h] = 0;
-            }
-        }
+        const int32_t* tl = tiles + TILE_INTS * t;
+        const int l = tl[0];
+        const int h_row0[2] = {tl[1], tl[3]};
+        const int h_rows[2] = {tl[2], tl[4]};
+        const bool pair = h_rows[1] > 0;
         const uint16_t* Bexp = B + (int64_t)l * b_expert_stride;
         const int copies = pair ? DMA_PER_WAVE : DMA_PER_WAVE - 2;  // a half tile skips A half 1
         const bool active = pair || wm == 0;                         // waves of an empty half idle
@@ -473,7 +523,9 @@ int persistent_grid() {
 
 }  // namespace
 
-int64_t moe_ffn_workspace_elems_impl(int max_blocks) { return WS_TILES + 4 * (int64_t)max_blocks; }
+int64_t moe_ffn_workspace_elems_impl(int max_blocks) {
+    return WS_HEAD + (int64_t)max_blocks + (int64_t)TILE_INTS * 2 * max_blocks;
+}
 
 hipError_t moe_launch_ffn_schedule(const int32_t* blocks, const int32_t* n_blocks, int max_blocks,
                                    int E_loc, int32_t* ws, hipStream_t stream) {
@@ -495,7 +547,7 @@ hipError_t moe_launch_ffn_fc1(const void* xp, const void* w1, moe_dtype_t dt, in
     ffn_bf16_kernel<true><<<persistent_grid(), kThreads, 0, stream>>>(
         static_cast<const uint16_t*>(xp), max_rows, H, static_cast<const uint16_t*>(w1),
         (int64_t)2 * I * H, 2 * I, static_cast<uint16_t*>(act), I, I, I,
-        (I + BN / 2 - 1) / (BN / 2), blocks, ws);
+        (I + BN / 2 - 1) / (BN / 2), max_blocks, ws);
     return hipGetLastError();
 }
 
@@ -512,6 +564,7 @@ hipError_t moe_launch_ffn_fc2(const void* act, const void* w2, moe_dtype_t dt, i
     }
     ffn_bf16_kernel<false><<<persistent_grid(), kThreads, 0, stream>>>(
         static_cast<const uint16_t*>(act), max_rows, I, static_cast<const uint16_t*>(w2),
-        (int64_t)H * I, H, static_cast<uint16_t*>(yp), H, H, I, (H + BN - 1) / BN, blocks, ws);
+        (int64_t)H * I, H, static_cast<uint16_t*>(yp), H, H, I, (H + BN - 1) / BN, max_blocks,
+        ws);
     return hipGetLastError();
 }
