@@ -3,7 +3,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--skew S]
 
 One step = route -> permute -> plan -> expert FFN (FC1, FC2) -> combine over one batch of
-seeded synthetic input already resident in HBM.  Prints ONE JSON line: whole-path tokens/s,
+seeded synthetic input already resident in HBM, timed as eager calls on one stream (--graph:
+as HIP-graph replays of the whole path; the eager figure is then reported beside it).  Prints ONE JSON line: whole-path tokens/s,
 the grouped GEMM's TFLOP/s, the dominant kernel (FC1, the gate/up GEMM with fused SwiGLU)
 against the bf16 MFMA peak, per-call times, and the CPU oracle timed on a bounded sample of
 the same workload on the host cores.
@@ -35,6 +36,8 @@ def parse():
     ap.add_argument("--workload", default="olmoe_shaped")
     ap.add_argument("--skew", default=None, help="Zipf exponent or 'hot4' (default: middle skew)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time HIP-graph replays of the whole path instead of eager calls")
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="tokens of the oracle's sizing pass (the measured sample is scaled to "
                          "about 12 s of CPU work)")
@@ -83,13 +86,16 @@ class Step:
         rec(6)
 
 
-def time_steps(step, steps, warmup, torch):
+def time_steps(step, steps, warmup, torch, graph=None):
+    """Wall time per step (HIP-graph replays of the whole path if `graph`, else eager calls)
+    and per-call durations from event-bracketed eager steps."""
+    run = graph.replay if graph is not None else step.run
     for _ in range(warmup):
-        step.run()
+        run()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        step.run()
+        run()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
     # per-call durations: HIP events on the stream the kernels are launched on
@@ -187,13 +193,16 @@ def main():
     def measure(sk, steps, warmup):
         logits = torch.from_numpy(inputs.make_logits(w, sk)).to(dev)
         step = Step(layer, logits, x, W1, W2)
-        wall, per = time_steps(step, steps, warmup, torch)
+        graph = layer.capture(logits, x, W1, W2) if args.graph else None
+        wall, per = time_steps(step, steps, warmup, torch, graph)
+        eager_wall = time_steps(step, steps, 1, torch)[0] if graph is not None else wall
         counts = layer.counts.cpu()
         N = int(counts[w.expert_begin::w.expert_stride][: w.n_local].sum())
         nb = int(layer.n_blocks.item())
-        return wall, per, N, nb, counts
+        del graph
+        return wall, per, N, nb, counts, eager_wall
 
-    wall, per, N, nb, counts = measure(skew, args.steps, args.warmup)
+    wall, per, N, nb, counts, eager_wall = measure(skew, args.steps, args.warmup)
     flops_fc1 = 4.0 * w.H * w.I * N
     flops_ffn = 6.0 * w.H * w.I * N
     fc1_s = per["fc1"] * 1e-6
@@ -215,6 +224,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(wall * 1e3, 4),
+        "eager_ms_per_step": round(eager_wall * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -224,7 +234,8 @@ def main():
         "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "E_loc": w.n_local,
                    "K": w.K, "I": w.I, "P": w.P, "block_m": w.beta,
                    "skew": w.skew_label(skew), "local_entries": N, "blocks": nb,
-                   "maxvio": round(maxvio, 3), "parallelism": "single GPU"},
+                   "maxvio": round(maxvio, 3), "parallelism": "single GPU",
+                   "launch": "hip graph replay" if args.graph else "eager"},
         "gemm_tflops": round(flops_ffn / ffn_s / 1e12, 1),
         "gemm_frac_of_peak": round(flops_ffn / ffn_s / 1e12 / PEAK_BF16_TFLOPS, 4),
         "per_call_us": {k: round(v, 2) for k, v in per.items()},
@@ -239,7 +250,7 @@ def main():
     if not args.no_all_skews:
         by = []
         for sk in w.skews:
-            wl, pr, n_, nb_, _ = measure(sk, max(5, args.steps // 2), 2)
+            wl, pr, n_, nb_, _, _ = measure(sk, max(5, args.steps // 2), 2)
             f = 6.0 * w.H * w.I * n_
             by.append({"skew": w.skew_label(sk), "tokens_per_s": round(w.T / wl, 1),
                        "ms_per_step": round(wl * 1e3, 4),

@@ -74,7 +74,7 @@ int32_t moe_max_moves(int E_loc, int P);
 int64_t moe_permute_workspace_elems(int T, int E_loc);
 
 /* int32 elements of scratch that moe_expert_ffn needs (its GEMM tile schedule):
- * 32 + 11 * max_blocks. */
+ * 32 + 15 * max_blocks. */
 int64_t moe_ffn_workspace_elems(int max_blocks);
 
 /* ------------------------------------------------------------------------ route --- */

@@ -298,3 +298,18 @@ class RoutedExperts:
         self.expert_ffn(w1, w2, stream)
         self.combine(stream)
         return self.out
+
+    def capture(self, logits, x, w1, w2):
+        """Record forward() on these tensors into a HIP graph (torch.cuda.CUDAGraph).
+
+        Each replay reruns the whole path on whatever logits / x / w1 / w2 hold at that time
+        and leaves the results in the static buffers.  The path launches kernels only (its
+        counters are cleared by kernels, not memsets), and every kernel reads its data-dependent
+        sizes on the device, so one graph serves every batch of this shape.  One eager forward
+        runs first, outside the capture."""
+        self.forward(logits, x, w1, w2)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.forward(logits, x, w1, w2)
+        return graph

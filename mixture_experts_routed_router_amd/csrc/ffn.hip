@@ -40,11 +40,19 @@ constexpr int kThreads = kWaves * MOE_WAVE;
 constexpr int kXcds = 8;
 // FFN workspace (int32): [0] tile count; [8 + x] FC1 item counter of XCD x, [16 + x] FC2's;
 // [24] FC1 / [25] FC2 finished-workgroup counters; from [32]: max_blocks block indices
-// sorted by expert, then the tiles, 5 ints each (expert, first row and row count of half 0,
-// first row and row count of half 1; count 0 = no half 1).
+// sorted by expert, then the tiles, 7 ints each (expert, first row and row count of half 0,
+// first row and row count of half 1 (count 0 = no half 1), the expert's first tile and its
+// tile count).
 constexpr int WS_NTILES = 0, WS_CTR_FC1 = 8, WS_CTR_FC2 = 16, WS_DONE_FC1 = 24, WS_DONE_FC2 = 25;
 constexpr int WS_HEAD = 32;
-constexpr int TILE_INTS = 5;
+constexpr int TILE_INTS = 7;
+// Items of one expert are taken in groups of up to GROUP_TILES tiles, column tile by column
+// tile within a group: the items in flight on an XCD then share a few A tiles and a few B
+// column tiles, which stay in its L2 instead of being fetched again from HBM.
+#ifndef GROUP_TILES
+#define GROUP_TILES 4
+#endif
+constexpr int kGroupTiles = GROUP_TILES;
 constexpr int ROW_BYTES = BK * 2;                           // 128
 constexpr int A_STAGE_BYTES = BM * ROW_BYTES;               // 32 KB
 constexpr int B_STAGE_BYTES = BN * ROW_BYTES;               // 32 KB
@@ -230,6 +238,8 @@ ffn_schedule_kernel(const int32_t* __restrict__ blocks, const int32_t* __restric
                     t[2] = rows;
                     t[3] = 0;
                     t[4] = 0;
+                    t[5] = tstart[l];
+                    t[6] = tstart[l + 1] - tstart[l];
                 } else {
                     t[3] = run_first + off;
                     t[4] = rows;
@@ -308,8 +318,16 @@ ffn_bf16_kernel(const uint16_t* __restrict__ A, int64_t a_rows, int Kdim,
         __syncthreads();
         const int it = item_s;
         if (it < 0) break;
-        const int t = it / NT;
-        const int nt = it - t * NT;
+        // item -> (tile, column tile): the expert's items [ts * NT, (ts + cnt) * NT) in groups
+        // of kGroupTiles tiles, column-tile-major inside a group
+        const int32_t* tg = tiles + TILE_INTS * (it / NT);
+        const int ts = tg[5], cnt = tg[6];
+        const int local = it - ts * NT;
+        const int grp = local / (kGroupTiles * NT);
+        const int r = local - grp * (kGroupTiles * NT);
+        const int ct = cnt - grp * kGroupTiles < kGroupTiles ? cnt - grp * kGroupTiles : kGroupTiles;
+        const int nt = r / ct;
+        const int t = ts + grp * kGroupTiles + (r - nt * ct);
         const int32_t* tl = tiles + TILE_INTS * t;
         const int l = tl[0];
         const int h_row0[2] = {tl[1], tl[3]};

@@ -46,7 +46,7 @@ def test_static_bounds(lib):
     assert b.moe_max_blocks(4096, 8, 64, 8, 128) == 4096 * 8 // 128 + 64 * 8
     assert b.moe_max_blocks(100, 3, 5, 5, 16) == -(-300 // 16) + 25
     assert b.moe_max_moves(64, 8) == 72
-    assert b.moe_ffn_workspace_elems(290) == 32 + 11 * 290
+    assert b.moe_ffn_workspace_elems(290) == 32 + 15 * 290
     assert b.moe_permute_workspace_elems(4096, 64) == 256 * 64
     assert b.moe_permute_workspace_elems(37, 3) == 3 * 3
     assert b.moe_max_rows(0, 8, 64, 128) == -1
@@ -104,13 +104,13 @@ def test_plan_rejects(lib):
 
 
 def test_ffn_and_combine_reject(lib):
-    ffn = lambda dt, H, I, blocks=P[3], ws_elems=208: lib.moe_expert_ffn(
+    ffn = lambda dt, H, I, blocks=P[3], ws_elems=272: lib.moe_expert_ffn(
         P[0], P[1], P[2], dt, H, I, 8, blocks, P[4], 16, P[5], P[6], 1024, P[7], ws_elems, NULL)
     assert ffn(1, 128, 256, blocks=NULL) == INVALID
     assert ffn(5, 128, 256) == INVALID
     assert ffn(1, 2880, 100) == UNSUPPORTED   # bf16 needs multiples of 64
     assert ffn(0, 126, 256) == UNSUPPORTED    # float32 needs multiples of 4
-    assert ffn(1, 128, 256, ws_elems=207) == INVALID  # schedule scratch below 32 + 11*max_blocks
+    assert ffn(1, 128, 256, ws_elems=271) == INVALID  # schedule scratch below 32 + 15*max_blocks
     assert lib.moe_combine(P[0], 1, P[1], P[2], 4, 100, 2, P[3], NULL) == INVALID  # 200-B rows
     assert lib.moe_combine(P[0], 1, P[1], NULL, 4, 128, 2, P[3], NULL) == INVALID
     assert lib.moe_combine(P[0], 1, P[1], P[2], 0, 128, 2, P[3], NULL) == INVALID

@@ -112,6 +112,39 @@ def test_repeat_runs_are_bit_identical():
         assert torch.equal(getattr(a, name)[valid], getattr(b, name)[valid]), name
 
 
+def test_graph_replay_matches_eager():
+    """The whole path captured as one HIP graph: replays on new logits written in place, with
+    eager calls and synchronisations between them, reproduce the eager results bit for bit."""
+    c = workload_case("olmoe_shaped", 1.2, T=1024)
+    _announce("graph replay vs eager, olmoe_shaped first 1024 tokens")
+    layer = run_gpu(c)
+    logits, x, W1, W2 = layer._inputs
+    graph = layer.capture(logits, x, W1, W2)
+    names = ("topk_ids", "topk_w", "counts", "offsets", "entry_pos", "q", "n_moves", "n_blocks",
+             "out")
+    w = inputs.WORKLOADS["olmoe_shaped"]
+    for skew in (0.0, 1.2, 0.5):
+        logits.copy_(torch.from_numpy(inputs.make_logits(w, skew)[: c.T].copy()))
+        layer.forward(logits, x, W1, W2)  # eager reference
+        torch.cuda.synchronize()
+        ref = {n: getattr(layer, n).clone() for n in names}
+        nb = int(ref["n_blocks"].item())
+        ref_blocks = layer.blocks[:nb].clone()
+        rows = int(ref["offsets"][-1].item())
+        valid = torch.nonzero(layer.row_token[:rows] >= 0).squeeze(1)
+        ref_yp = layer.yp[valid].clone()
+        for n in ("out", "yp", "act", "topk_ids", "topk_w", "entry_pos"):
+            getattr(layer, n).zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for n in names:
+            assert torch.equal(getattr(layer, n), ref[n]), (skew, n)
+        assert torch.equal(layer.blocks[:nb], ref_blocks), (skew, "blocks")
+        assert torch.equal(layer.yp[valid], ref_yp), (skew, "yp")
+    del graph
+
+
 # ------------------------------------------------------ full-size layers: sampled ---
 
 FULL = [(n, s) for n in ("olmoe_shaped", "qwen3_30b_a3b_shaped", "gpt_oss_120b_shaped",
