@@ -147,6 +147,10 @@ __device__ __forceinline__ void wait_copies_and_barrier(int n) {
 // expert).  Each run is cut into 128-row pieces from its start, and an expert's pieces are
 // paired in order into 256-row tiles (an odd last piece is a half tile).  Experts follow one
 // another in ascending local id.  The GEMMs' item and finished counters are cleared too.
+// Tables of up to kSchedLds blocks are staged in LDS first, so the per-expert walks (one
+// thread per expert) touch LDS only; larger tables are walked in global memory.
+constexpr int kSchedLds = 3072;
+
 __global__ void __launch_bounds__(256)
 ffn_schedule_kernel(const int32_t* __restrict__ blocks, const int32_t* __restrict__ n_blocks_ptr,
                     int max_blocks, int E_loc, int32_t* __restrict__ ws) {
@@ -156,26 +160,41 @@ ffn_schedule_kernel(const int32_t* __restrict__ blocks, const int32_t* __restric
     __shared__ int tstart[257];
     __shared__ int running[256];
     __shared__ unsigned long long mask[4][256];
+    __shared__ int s_l[kSchedLds], s_first[kSchedLds], s_rows[kSchedLds], s_sorted[kSchedLds];
     const int tid = threadIdx.x, lane = moe_lane_id(), wave = tid / MOE_WAVE;
-    int32_t* sorted = ws + WS_HEAD;
+    int32_t* sorted_g = ws + WS_HEAD;
     int32_t* tiles = ws + WS_HEAD + max_blocks;
     int nb = *n_blocks_ptr;
     nb = nb < max_blocks ? nb : max_blocks;
+    const bool in_lds = nb <= kSchedLds;
     if (tid >= WS_CTR_FC1 && tid < WS_HEAD) ws[tid] = 0;  // item and finished counters
     for (int l = tid; l < E_loc; l += 256) {
         cnt[l] = 0;
         running[l] = 0;
     }
+    if (in_lds) {
+        for (int b = tid; b < nb; b += 256) {
+            const int4 v = reinterpret_cast<const int4*>(blocks)[b];
+            s_l[b] = v.y;
+            s_first[b] = v.z;
+            s_rows[b] = v.w;
+        }
+    }
     __syncthreads();
-    for (int b = tid; b < nb; b += 256) atomicAdd(&cnt[blocks[4 * b + 1]], 1);
+    auto blk_l = [&](int b) { return in_lds ? s_l[b] : blocks[4 * b + 1]; };
+    auto blk_first = [&](int b) { return in_lds ? s_first[b] : blocks[4 * b + 2]; };
+    auto blk_rows = [&](int b) { return in_lds ? s_rows[b] : blocks[4 * b + 3]; };
+    auto sorted_at = [&](int i) { return in_lds ? s_sorted[i] : sorted_g[i]; };
+
+    for (int b = tid; b < nb; b += 256) atomicAdd(&cnt[blk_l(b)], 1);
     __syncthreads();
     if (tid == 0) {
-        int s = 0;
+        int acc = 0;
         for (int l = 0; l < E_loc; ++l) {
-            bstart[l] = s;
-            s += cnt[l];
+            bstart[l] = acc;
+            acc += cnt[l];
         }
-        bstart[E_loc] = s;
+        bstart[E_loc] = acc;
     }
     __syncthreads();
     // stable counting sort of the blocks by expert, 256 blocks per round
@@ -183,13 +202,16 @@ ffn_schedule_kernel(const int32_t* __restrict__ blocks, const int32_t* __restric
         for (int i = tid; i < 4 * 256; i += 256) mask[i / 256][i % 256] = 0ull;
         __syncthreads();
         const int b = b0 + tid;
-        const int l = b < nb ? blocks[4 * b + 1] : -1;
+        const int l = b < nb ? blk_l(b) : -1;
         if (l >= 0) atomicOr(&mask[wave][l], 1ull << lane);
         __syncthreads();
         if (l >= 0) {
             int pos = running[l] + __popcll(mask[wave][l] & ((1ull << lane) - 1ull));
             for (int w = 0; w < wave; ++w) pos += __popcll(mask[w][l]);
-            sorted[bstart[l] + pos] = b;
+            if (in_lds)
+                s_sorted[bstart[l] + pos] = b;
+            else
+                sorted_g[bstart[l] + pos] = b;
         }
         __syncthreads();
         for (int e = tid; e < E_loc; e += 256)
@@ -201,8 +223,8 @@ ffn_schedule_kernel(const int32_t* __restrict__ blocks, const int32_t* __restric
     for (int l = tid; l < E_loc; l += 256) {
         int pieces = 0, run_first = 0, run_rows = 0;
         for (int i = bstart[l]; i < bstart[l + 1]; ++i) {
-            const int b = sorted[i];
-            const int first = blocks[4 * b + 2], rows = blocks[4 * b + 3];
+            const int b = sorted_at(i);
+            const int first = blk_first(b), rows = blk_rows(b);
             if (run_rows > 0 && first == run_first + run_rows) {
                 run_rows += rows;
             } else {
@@ -216,13 +238,13 @@ ffn_schedule_kernel(const int32_t* __restrict__ blocks, const int32_t* __restric
     }
     __syncthreads();
     if (tid == 0) {
-        int s = 0;
+        int acc = 0;
         for (int l = 0; l < E_loc; ++l) {
-            tstart[l] = s;
-            s += (npieces[l] + 1) / 2;
+            tstart[l] = acc;
+            acc += (npieces[l] + 1) / 2;
         }
-        tstart[E_loc] = s;
-        ws[WS_NTILES] = s;
+        tstart[E_loc] = acc;
+        ws[WS_NTILES] = acc;
     }
     __syncthreads();
     // emit the tiles: pieces of an expert in order, two per tile
@@ -247,8 +269,8 @@ ffn_schedule_kernel(const int32_t* __restrict__ blocks, const int32_t* __restric
             }
         };
         for (int i = bstart[l]; i < bstart[l + 1]; ++i) {
-            const int b = sorted[i];
-            const int first = blocks[4 * b + 2], rows = blocks[4 * b + 3];
+            const int b = sorted_at(i);
+            const int first = blk_first(b), rows = blk_rows(b);
             if (run_rows > 0 && first == run_first + run_rows) {
                 run_rows += rows;
             } else {

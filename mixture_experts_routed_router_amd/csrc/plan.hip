@@ -8,11 +8,12 @@
 // expert's rows are cut into blocks of at most beta rows in the expert's stable order.
 //
 // One workgroup.  The greedy is sequential by nature (at most P-1 rank moves, each a few
-// slices) and runs in wave 0 with every per-rank surplus and per-expert remaining count
-// held in registers (lane r holds rank r; lane j holds experts j, j+64, j+128, j+192);
-// arg-min / arg-max are butterfly shuffles under total orders (value, then lowest id), so
-// ties resolve exactly as stated in moe.h.  The block table is then emitted by all threads
-// from a scan of per-(rank, expert) block counts.
+// slices) and runs in wave 0: lane r holds rank r's surplus in a register, the experts'
+// remaining counts sit in LDS.  Arg-min / arg-max run only over the lanes that compete (the
+// P ranks, or the donor's G = E_loc / P experts, one per lane) under total orders (value,
+// then lowest id), so ties resolve exactly as stated in moe.h; groups of up to 16 lanes
+// reduce with DPP lane swaps inside a row, larger ones add cross-row shuffles.  The block
+// table is then emitted by all threads from a scan of per-(rank, expert) block counts.
 #include "moe_launch.h"
 
 namespace {
@@ -20,28 +21,38 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxSlices = 4096;  // E_loc * P
 
-__device__ __forceinline__ void argmin_lowest(int& v, int& i) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        int ov = __shfl_xor(v, off, MOE_WAVE);
-        int oi = __shfl_xor(i, off, MOE_WAVE);
-        if (ov < v || (ov == v && oi < i)) {
-            v = ov;
-            i = oi;
-        }
-    }
+// value of lane (lane ^ 1), (lane ^ 2), (7 - lane within 8), (15 - lane within 16): after
+// reductions over the smaller groups, each step pairs a lane with the other half of its group
+template <int kStep>
+__device__ __forceinline__ int dpp_partner(int v) {
+    constexpr int ctrl = kStep == 0 ? 0xB1 : kStep == 1 ? 0x4E : kStep == 2 ? 0x141 : 0x140;
+    return __builtin_amdgcn_update_dpp(v, v, ctrl, 0xF, 0xF, false);
 }
 
-__device__ __forceinline__ void argmax_lowest(int& v, int& i) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        int ov = __shfl_xor(v, off, MOE_WAVE);
-        int oi = __shfl_xor(i, off, MOE_WAVE);
-        if (ov > v || (ov == v && oi < i)) {
+// Best (v, i) over the aligned group of 2^levels lanes containing this lane (levels <= 6);
+// every lane of the group ends with the result.  kMax: larger v wins, else smaller v; equal
+// v: smaller i.
+template <bool kMax>
+__device__ __forceinline__ void group_best(int& v, int& i, int levels) {
+    auto take = [&](int ov, int oi) {
+        const bool better = kMax ? (ov > v || (ov == v && oi < i)) : (ov < v || (ov == v && oi < i));
+        if (better) {
             v = ov;
             i = oi;
         }
-    }
+    };
+    if (levels > 0) take(dpp_partner<0>(v), dpp_partner<0>(i));
+    if (levels > 1) take(dpp_partner<1>(v), dpp_partner<1>(i));
+    if (levels > 2) take(dpp_partner<2>(v), dpp_partner<2>(i));
+    if (levels > 3) take(dpp_partner<3>(v), dpp_partner<3>(i));
+    if (levels > 4) take(__shfl_xor(v, 16, MOE_WAVE), __shfl_xor(i, 16, MOE_WAVE));
+    if (levels > 5) take(__shfl_xor(v, 32, MOE_WAVE), __shfl_xor(i, 32, MOE_WAVE));
+}
+
+__device__ __forceinline__ int ceil_log2(int n) {
+    int l = 0;
+    while ((1 << l) < n) ++l;
+    return l;
 }
 
 __global__ void __launch_bounds__(kThreads)
@@ -50,6 +61,7 @@ plan_kernel(const int32_t* __restrict__ counts, int begin, int stride, int E_loc
             int32_t* __restrict__ n_moves, int max_moves, int32_t* __restrict__ blocks,
             int32_t* __restrict__ n_blocks, int max_blocks, int32_t* __restrict__ err_word) {
     __shared__ int n_s[256];
+    __shared__ int rem_s[256];
     __shared__ int off_s[257];
     __shared__ int q_s[kMaxSlices];      // [l * P + r]
     __shared__ int start_s[kMaxSlices];  // first row of slice (l, r), then its first block
@@ -60,7 +72,11 @@ plan_kernel(const int32_t* __restrict__ counts, int begin, int stride, int E_loc
     const int lane = moe_lane_id();
     const int G = E_loc / P;
 
-    for (int l = tid; l < E_loc; l += kThreads) n_s[l] = counts[begin + l * stride];
+    for (int l = tid; l < E_loc; l += kThreads) {
+        const int n = counts[begin + l * stride];
+        n_s[l] = n;
+        rem_s[l] = n;
+    }
     for (int i = tid; i < E_loc * P; i += kThreads) q_s[i] = 0;
     if (tid == 0) err_s = 0;
     __syncthreads();
@@ -92,13 +108,6 @@ plan_kernel(const int32_t* __restrict__ counts, int begin, int stride, int E_loc
         if (lane == MOE_WAVE - 1) off_s[E_loc] = incl;
         const int N = moe_wave_sum_i32(raw);
 
-        // remaining entries of experts lane + 64*j (registers)
-        int rem[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            int l = lane + MOE_WAVE * j;
-            rem[j] = l < E_loc ? n_s[l] : 0;
-        }
         // surplus of rank `lane`
         int d = 0;
         if (lane < P) {
@@ -106,12 +115,18 @@ plan_kernel(const int32_t* __restrict__ counts, int begin, int stride, int E_loc
             for (int l = lane * G; l < (lane + 1) * G; ++l) load += n_s[l];
             d = load - (N / P + (lane < N % P ? 1 : 0));
         }
+        const int rank_levels = ceil_log2(P);
+        const int gsize = G < MOE_WAVE ? G : MOE_WAVE;
+        const int expert_levels = ceil_log2(gsize);
         int nm = 0, err = 0;
         for (int iter = 0; iter <= P; ++iter) {
             int mn = lane < P ? d : 0x7FFFFFFF, mn_i = lane;
             int mx = lane < P ? d : (int)0x80000000, mx_i = lane;
-            argmin_lowest(mn, mn_i);
-            argmax_lowest(mx, mx_i);
+            group_best<false>(mn, mn_i, rank_levels);
+            group_best<true>(mx, mx_i, rank_levels);
+            mn = __builtin_amdgcn_readfirstlane(mn);
+            mn_i = __builtin_amdgcn_readfirstlane(mn_i);
+            mx_i = __builtin_amdgcn_readfirstlane(mx_i);
             if (mn >= 0) break;
             if (iter == P) {  // cannot happen: each move settles one rank for good
                 err |= 4;
@@ -122,34 +137,33 @@ plan_kernel(const int32_t* __restrict__ counts, int begin, int stride, int E_loc
             if (lane == donor) d -= need;
             if (lane == recv) d = 0;
             for (int s = 0; need > 0; ++s) {
-                // donor's own expert with the most remaining entries (lowest id on ties)
+                // donor's own expert with the most remaining entries (lowest id on ties):
+                // lane i looks at experts donor*G + i, + 64, ...
                 int bv = 0, bl = 0x7FFFFFFF;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    int l = lane + MOE_WAVE * j;
-                    if (l >= donor * G && l < (donor + 1) * G && rem[j] > 0 &&
-                        (rem[j] > bv || (rem[j] == bv && l < bl))) {
-                        bv = rem[j];
+                for (int l = donor * G + lane; l < (donor + 1) * G; l += MOE_WAVE) {
+                    const int r = rem_s[l];
+                    if (r > 0 && (r > bv || (r == bv && l < bl))) {
+                        bv = r;
                         bl = l;
                     }
                 }
-                argmax_lowest(bv, bl);
+                group_best<true>(bv, bl, expert_levels);
+                bv = __builtin_amdgcn_readfirstlane(bv);
+                bl = __builtin_amdgcn_readfirstlane(bl);
                 if (bv <= 0 || s > G) {  // cannot happen: a donor always covers its move
                     err |= 4;
                     break;
                 }
                 const int take = bv < need ? bv : need;
-                if ((bl & (MOE_WAVE - 1)) == lane) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        if (bl == lane + MOE_WAVE * j) rem[j] -= take;
+                if (lane == 0) {
+                    rem_s[bl] = bv - take;
                     q_s[bl * P + recv] += take;
-                }
-                if (lane == 0 && nm < max_moves) {
-                    moves[4 * nm + 0] = donor;
-                    moves[4 * nm + 1] = recv;
-                    moves[4 * nm + 2] = bl;
-                    moves[4 * nm + 3] = take;
+                    if (nm < max_moves) {
+                        moves[4 * nm + 0] = donor;
+                        moves[4 * nm + 1] = recv;
+                        moves[4 * nm + 2] = bl;
+                        moves[4 * nm + 3] = take;
+                    }
                 }
                 ++nm;
                 need -= take;
@@ -158,11 +172,7 @@ plan_kernel(const int32_t* __restrict__ counts, int begin, int stride, int E_loc
         }
         if (nm > max_moves) err |= 2;
         // leftovers stay with the owner
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            int l = lane + MOE_WAVE * j;
-            if (l < E_loc) q_s[l * P + l / G] += rem[j];
-        }
+        for (int l = lane; l < E_loc; l += MOE_WAVE) q_s[l * P + l / G] += rem_s[l];
         if (lane == 0) {
             *n_moves = nm < max_moves ? nm : max_moves;
             err_s = err;

@@ -70,6 +70,17 @@ def test_tiny_f32_full():
     ("wide_k", dict(seed=8, T=80, H=64, E=256, K=16, I=64, P=16, block_m=16)),
     ("f32_ragged", dict(seed=9, T=50, H=32, E=6, K=2, I=48, P=3, dtype=torch.float32,
                         block_m=16)),
+    # plan reductions: 64 ranks (cross-row rank groups), 32 and 128 experts per rank (cross-row
+    # and several experts per lane), a single rank (no moves)
+    ("many_ranks", dict(seed=11, T=300, H=64, E=64, K=4, I=64, P=64, block_m=16,
+                        logit_bias=[1.5] * 8 + [0.0] * 56)),
+    ("g32", dict(seed=13, T=500, H=64, E=128, K=4, I=64, P=4, block_m=64,
+                 logit_bias=[1.0] * 32 + [0.0] * 96)),
+    ("wide_groups", dict(seed=12, T=400, H=64, E=256, K=8, I=64, P=2, block_m=32,
+                         logit_bias=[0.8] * 128 + [0.0] * 128)),
+    ("one_rank", dict(seed=14, T=100, H=64, E=16, K=2, I=64, P=1)),
+    # more than 3072 blocks: the FFN tile schedule walks the block table in global memory
+    ("many_blocks", dict(seed=15, T=8192, H=64, E=64, K=8, I=64, P=8, block_m=16)),
 ])
 def test_small_layers_full(name, kw):
     c = random_case(**kw)
