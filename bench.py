@@ -108,6 +108,21 @@ def time_steps(step, steps, warmup, torch, graph=None):
     return wall, per
 
 
+def ffn_roofline(w, n_loc, eb):
+    """Per-expert roofline of the two expert GEMMs: each touched expert costs the larger of
+    its valid-row flops at the MFMA peak and one read of its weights (3 H I values) at the
+    HBM peak.  Returns (t_roof seconds, touched experts, weight bytes of touched experts,
+    bound of the sum: 'mfma' or 'hbm')."""
+    per_flop = 6.0 * w.H * w.I / (PEAK_BF16_TFLOPS * 1e12)
+    wbytes = 3.0 * w.H * w.I * eb
+    per_byte = wbytes / (PEAK_HBM_GBS * 1e9)
+    touched = [int(n) for n in n_loc if n > 0]
+    t_mfma = sum(n * per_flop for n in touched)
+    t_roof = sum(max(n * per_flop, per_byte) for n in touched)
+    bound = "hbm" if len(touched) * per_byte > t_mfma else "mfma"
+    return t_roof, len(touched), len(touched) * wbytes, bound
+
+
 def ffn_traffic(workload: str):
     """HBM bytes per FC1 launch from committed rocprofv3 counter runs, if they were taken on
     the current FC1 kernel source; else None."""
@@ -215,6 +230,19 @@ def main():
     permute_bytes = (w.T + N) * w.H * eb + 4 * (w.T * w.K + rows_pad)
     combine_bytes = (N + w.T) * w.H * eb + 8 * w.T * w.K
     traffic = ffn_traffic(w.name)
+    t_roof, touched, wbytes, bound = ffn_roofline(w, loc.tolist(), eb)
+    if bound == "hbm":
+        # weight-read bound (decode): FC1 streams the gate/up weights of every touched expert
+        fc1_bytes = wbytes * 2.0 / 3.0
+        roofline = {"kernel": "moe_expert_ffn_fc1 (gate/up grouped GEMM + SwiGLU)",
+                    "bound": "hbm", "achieved": round(fc1_bytes / fc1_s / 1e9, 1),
+                    "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(fc1_bytes / fc1_s / 1e9 / PEAK_HBM_GBS, 4), "traffic": traffic}
+    else:
+        roofline = {"kernel": "moe_expert_ffn_fc1 (gate/up grouped GEMM + SwiGLU)",
+                    "bound": "mfma", "achieved": round(achieved, 1),
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
 
     line = {
         "metric": METRIC,
@@ -241,20 +269,27 @@ def main():
         "per_call_us": {k: round(v, 2) for k, v in per.items()},
         "permute_gbs": round(permute_bytes / (per["permute"] * 1e-6) / 1e9, 1),
         "combine_gbs": round(combine_bytes / (per["combine"] * 1e-6) / 1e9, 1),
-        "roofline": {"kernel": "moe_expert_ffn_fc1 (gate/up grouped GEMM + SwiGLU)",
-                     "bound": "mfma", "achieved": round(achieved, 1),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic},
+        "ffn_t_roof_us": round(t_roof * 1e6, 2),
+        "ffn_frac_of_t_roof": round(t_roof / ffn_s, 4),
+        "touched_experts": touched,
+        "ffn_weight_gbs": round(wbytes / ffn_s / 1e9, 1),
+        "ffn_weight_frac_of_hbm": round(wbytes / ffn_s / 1e9 / PEAK_HBM_GBS, 4),
+        "roofline": roofline,
     }
     if not args.no_all_skews:
         by = []
         for sk in w.skews:
-            wl, pr, n_, nb_, _, _ = measure(sk, max(5, args.steps // 2), 2)
+            wl, pr, n_, nb_, cnt_, _ = measure(sk, max(5, args.steps // 2), 2)
             f = 6.0 * w.H * w.I * n_
+            ffn_t = (pr["fc1"] + pr["fc2"]) * 1e-6
+            loc_ = cnt_[w.expert_begin::w.expert_stride][: w.n_local].tolist()
+            tr, tch, wb, _ = ffn_roofline(w, loc_, eb)
             by.append({"skew": w.skew_label(sk), "tokens_per_s": round(w.T / wl, 1),
                        "ms_per_step": round(wl * 1e3, 4),
-                       "gemm_tflops": round(f / ((pr["fc1"] + pr["fc2"]) * 1e-6) / 1e12, 1)})
+                       "gemm_tflops": round(f / ffn_t / 1e12, 1),
+                       "ffn_frac_of_t_roof": round(tr / ffn_t, 4),
+                       "touched_experts": tch,
+                       "ffn_weight_gbs": round(wb / ffn_t / 1e9, 1)})
         line["by_skew"] = by
     if not args.no_cpu_baseline:
         T_s = args.cpu_tokens or {"tiny_f32": 64, "olmoe_shaped": 256,

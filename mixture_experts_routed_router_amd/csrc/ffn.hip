@@ -31,10 +31,8 @@
 namespace {
 
 constexpr int HALF = 128;    // rows per tile half (= the plan's largest block at beta 128)
-constexpr int BM = 2 * HALF; // rows per tile
 constexpr int BN = 256;      // B rows per tile (FC1: 128 gate + 128 up; FC2: 256 columns of H)
 constexpr int BK = 64;       // K slice per LDS stage: 128-byte rows = whole cache lines
-constexpr int STAGES = 2;    // LDS ring depth (one slice consumed while the next lands)
 constexpr int kWaves = 8;    // two waves per SIMD
 constexpr int kThreads = kWaves * MOE_WAVE;
 constexpr int kXcds = 8;
@@ -53,33 +51,52 @@ constexpr int TILE_INTS = 7;
 #define GROUP_TILES 4
 #endif
 constexpr int kGroupTiles = GROUP_TILES;
-constexpr int ROW_BYTES = BK * 2;                           // 128
-constexpr int A_STAGE_BYTES = BM * ROW_BYTES;               // 32 KB
-constexpr int B_STAGE_BYTES = BN * ROW_BYTES;               // 32 KB
-constexpr int STAGE_BYTES = A_STAGE_BYTES + B_STAGE_BYTES;  // 64 KB
-constexpr int SEG_ROWS = 1024 / ROW_BYTES;                  // 8 rows per 1 KB copy
-constexpr int DMA_PER_WAVE = STAGE_BYTES / 1024 / kWaves;   // 8 (6 for a half tile)
+constexpr int ROW_BYTES = BK * 2;           // 128
+constexpr int SEG_ROWS = 1024 / ROW_BYTES;  // 8 rows per 1 KB copy
+constexpr int B_REGION = BN * ROW_BYTES;    // 32 KB of B rows per stage
+
+// An item stages kRowsA rows of A per K slice: 256 (two 128-row halves, a 2-deep ring of
+// 64 KB stages), 128 or 64 (one half of at most that many rows, a 3-deep ring of 48 or 40 KB
+// stages).  The smaller items keep two slices in flight instead of one, where the kernel is
+// mostly streaming weights, and stage only the A rows they use.
+template <int kRowsA>
+struct Mode {
+    static constexpr int kStages = kRowsA == 256 ? 2 : 3;
+    static constexpr int kARegion = kRowsA * ROW_BYTES;
+    static constexpr int kStageBytes = kARegion + B_REGION;
+    static constexpr int kACopies = kRowsA / 64;  // 1 KB A copies per wave per stage
+    static constexpr int kCopies = kACopies + 4;  // + 4 B copies
+    static constexpr int kRowBlocks = kRowsA / 64;  // 32-row MFMA blocks per wave
+};
+constexpr int SMEM_BYTES = Mode<128>::kStages * Mode<128>::kStageBytes;  // 144 KB
+static_assert(Mode<256>::kStages * Mode<256>::kStageBytes <= SMEM_BYTES, "ring size");
+static_assert(Mode<64>::kStages * Mode<64>::kStageBytes <= SMEM_BYTES, "ring size");
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
 
-// Stage layout.  A stage holds the tile's 256 A rows and 256 B rows, 128 bytes (64 bf16, one
-// cache line) each, in 1 KB segments of 8 rows: A segment g = rows 8g..8g+7, B likewise.
-// Wave w fills A segments w, w+8, w+16, w+24 and B segments w, w+8, w+16, w+24, placed
-// contiguously at [w * 8 KB, w * 8 KB + 8 KB) in that order, so the wave needs one M0 value
-// per four copies and selects segments with the copy instruction's immediate offset (which
+// Stage layout.  A stage holds the item's kRowsA A rows and 256 B rows, 128 bytes (64 bf16,
+// one cache line) each, in 1 KB segments of 8 rows: A segment g = rows 8g..8g+7, B likewise.
+// Wave w fills A segments w, w+8, ... and B segments w, w+8, w+16, w+24, each run placed
+// contiguously (A at w * kACopies KB, B at kARegion + w * 4 KB), so the wave needs one M0
+// value per run and selects segments with the copy instruction's immediate offset (which
 // moves the LDS destination and the global source alike).  Within the tile, row r's logical
 // 16-byte chunk c sits at physical chunk c ^ ((r >> 1) & 7): a ds_read_b128 serves 16 lanes
 // at a time over 64 four-byte banks, and 16 consecutive rows reading one logical chunk then
-// land in 16 distinct bank groups (r & 1 picks the 128-byte half, the XOR the group in it).
+// land in 16 distinct bank groups (r & 1 picks the 128-byte half, the XOR the group in it;
+// segment bases are multiples of 256 bytes).
 __device__ __forceinline__ int swz_chunk(int row, int c) { return c ^ ((row >> 1) & 7); }
 
+template <int kRowsA>
 __device__ __forceinline__ uint32_t stage_row_offset(int row, bool b_side) {
-    const int g = row >> 3;  // segment of the row among its side's 32
-    return (uint32_t)((g & 7) * 8192 + ((b_side ? 4 : 0) + (g >> 3)) * 1024 + (row & 7) * ROW_BYTES);
+    const int g = row >> 3;  // segment of the row on its side
+    const uint32_t in_seg = (uint32_t)(row & 7) * ROW_BYTES;
+    if (b_side) return (uint32_t)(Mode<kRowsA>::kARegion + (g & 7) * 4096 + (g >> 3) * 1024) + in_seg;
+    return (uint32_t)((g & 7) * (Mode<kRowsA>::kACopies * 1024) + (g >> 3) * 1024) + in_seg;
 }
 
+template <int kRowsA>
 __device__ __forceinline__ bf16x8_t lds_frag(const uint8_t* stage, int row, bool b_side, int ch) {
-    const uint4 v = *reinterpret_cast<const uint4*>(stage + stage_row_offset(row, b_side) +
+    const uint4 v = *reinterpret_cast<const uint4*>(stage + stage_row_offset<kRowsA>(row, b_side) +
                                                     (swz_chunk(row, ch) << 4));
     return __builtin_bit_cast(bf16x8_t, v);
 }
@@ -122,16 +139,34 @@ __device__ __forceinline__ void four_copies(uint32_t m0, const void* b0, const v
             : "memory");
 }
 
+// One copy: 16 B per lane from base + lane offset to LDS address M0 + 16 lane.
+__device__ __forceinline__ void one_copy(uint32_t m0, const void* base, uint32_t off) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %3\n\t"
+        "s_nop 0\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(off), "s"(m0), "s"(base)
+        : "memory");
+}
+
 // Wait until at most n of this wave's copies are outstanding, then meet the workgroup.
-// n = pending stages (0 or 1) x copies per stage (8, or 6 for a half tile).
+// n = pending stages (0, 1 or 2) x copies per stage (8, 6 or 5).
 #define MOE_WAIT_CASE(n)                                                                      \
     case n:                                                                                   \
         asm volatile("s_waitcnt vmcnt(" #n ")\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); \
         break;
 __device__ __forceinline__ void wait_copies_and_barrier(int n) {
     switch (n) {
+        MOE_WAIT_CASE(12)
+        MOE_WAIT_CASE(10)
         MOE_WAIT_CASE(8)
         MOE_WAIT_CASE(6)
+        MOE_WAIT_CASE(5)
         default:
             asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
             break;
@@ -285,6 +320,164 @@ ffn_schedule_kernel(const int32_t* __restrict__ blocks, const int32_t* __restric
 
 // ------------------------------------------------------------------ grouped GEMMs ---
 
+// One item: C rows of tile (h_row0, h_rows) x column tile nt of expert B (see ffn_bf16_kernel).
+// Wave (wm, wn) = (wave >> 2, wave & 3) computes kRowBlocks 32-row blocks starting at tile row
+// wm * kRowsA / 2, against 64 B rows (FC1: 32 gate rows and the 32 matching up rows).
+template <bool kSwiGLU, int kRowsA>
+__device__ __forceinline__ void gemm_item(const uint16_t* __restrict__ A, int64_t a_rows, int Kdim,
+                                          const uint16_t* __restrict__ Bexp, int b_rows,
+                                          uint16_t* __restrict__ C, int ldc, int n_cols, int I,
+                                          int nt, const int (&h_row0)[2], const int (&h_rows)[2],
+                                          uint8_t* smem, uint32_t smem_base, int wave, int lane,
+                                          int seg_row, int seg_lchunk) {
+    using M = Mode<kRowsA>;
+    constexpr int RB = M::kRowBlocks;
+    const int wm = wave >> 2;
+    const int wn = wave & 3;
+    const int wrow = wm * (kRowsA / 2);  // first tile row of this wave
+    const bool active = kRowsA != 64 || wrow < h_rows[0];  // 64-row items: idle past the rows
+    const int nk = Kdim / BK;
+
+    // per copy: a wave-uniform base (A half 0, A half 1, or the expert's B) and this lane's
+    // byte offset from it (row * Kdim * 2 + chunk * 16; < 4 GiB).  A copy q fills segment
+    // wave + 8q: tile rows 64q + 8 wave + (0..7), i.e. half q / 2.
+    const uint8_t* a0 = reinterpret_cast<const uint8_t*>(A + (int64_t)h_row0[0] * Kdim);
+    const uint8_t* a1 = reinterpret_cast<const uint8_t*>(A + (int64_t)h_row0[1] * Kdim);
+    const uint8_t* bx = reinterpret_cast<const uint8_t*>(Bexp);
+    uint32_t offa[M::kACopies], offb[4];
+#pragma unroll
+    for (int q = 0; q < M::kACopies; ++q) {
+        const int h = q >> 1;
+        int rr = ((q & 1) * 8 + wave) * SEG_ROWS + seg_row;  // row within half h
+        if (h_row0[h] + rr > a_rows - 1) rr = (int)(a_rows - 1 - h_row0[h]);  // read, unused
+        offa[q] = (uint32_t)rr * (uint32_t)Kdim * 2u + seg_lchunk * 16u;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int rr = (q * 8 + wave) * SEG_ROWS + seg_row;  // B row in the tile
+        int br;
+        if (kSwiGLU)
+            br = rr < BN / 2 ? nt * (BN / 2) + rr : I + nt * (BN / 2) + (rr - BN / 2);
+        else
+            br = nt * BN + rr;
+        if (br > b_rows - 1) br = b_rows - 1;  // columns past the end: read, not stored
+        offb[q] = (uint32_t)br * (uint32_t)Kdim * 2u + seg_lchunk * 16u;
+    }
+    auto issue = [&](int kt) {
+        const uint32_t st = smem_base + (kt % M::kStages) * M::kStageBytes;
+        const uint32_t koff = (uint32_t)kt * (BK * 2);
+        const uint32_t ma = st + wave * (M::kACopies * 1024);
+        if constexpr (kRowsA == 256)
+            four_copies(ma, a0, a0 - 1024, a1 - 2048, a1 - 3072, offa[0] + koff, offa[1] + koff,
+                        offa[2] + koff, offa[3] + koff, true);
+        else if constexpr (kRowsA == 128)
+            four_copies(ma, a0, a0 - 1024, a0, a0, offa[0] + koff, offa[1] + koff, 0, 0, false);
+        else
+            one_copy(ma, a0, offa[0] + koff);
+        four_copies(st + M::kARegion + wave * 4096, bx, bx - 1024, bx - 2048, bx - 3072,
+                    offb[0] + koff, offb[1] + koff, offb[2] + koff, offb[3] + koff, true);
+    };
+
+    f32x16_t acc[RB][2];
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    // fragments double-buffered one 16-wide K step ahead of the MFMAs
+    bf16x8_t fa[2][RB], fb[2][2];
+    auto load_frags = [&](int kt, int kk, int buf) {
+        const uint8_t* st = smem + (kt % M::kStages) * M::kStageBytes;
+        const int ch = kk * 2 + (lane >> 5);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int br = kSwiGLU ? j * (BN / 2) + wn * 32 + (lane & 31)
+                                   : wn * 64 + j * 32 + (lane & 31);
+            fb[buf][j] = lds_frag<kRowsA>(st, br, true, ch);
+        }
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+            fa[buf][i] = lds_frag<kRowsA>(st, wrow + i * 32 + (lane & 31), false, ch);
+    };
+
+    __syncthreads();  // the previous item's last LDS reads are done
+    const int pre = nk < M::kStages ? nk : M::kStages;  // every slot filled before the loop
+    for (int s = 0; s < pre; ++s) issue(s);
+    wait_copies_and_barrier((pre - 1) * M::kCopies);
+    if (active) load_frags(0, 0, 0);
+
+    for (int kt = 0; kt < nk; ++kt) {
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            const int cur = kk & 1;
+            if (active) {
+                if (kk + 1 < BK / 16) load_frags(kt, kk + 1, cur ^ 1);
+                // D = B-rows x A-rows: lane keeps one A row and 4 consecutive columns per
+                // register group, so the epilogue stores 8 bytes at a time
+#pragma unroll
+                for (int i = 0; i < RB; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cur][j], fa[cur][i],
+                                                                            acc[i][j], 0, 0, 0);
+            }
+            if (kk + 1 == BK / 16 && kt + 1 < nk) {
+                // behind slice kt's last MFMAs: wait for slice kt+1 everywhere (slices up to
+                // kt+kStages-1 are issued); then slice kt's slot is free for slice
+                // kt+kStages; first fragments of slice kt+1
+                const int issued = kt + M::kStages - 1 < nk ? kt + M::kStages - 1 : nk - 1;
+                wait_copies_and_barrier((issued - (kt + 1)) * M::kCopies);
+                if (kt + M::kStages < nk) issue(kt + M::kStages);
+                if (active) load_frags(kt + 1, 0, cur ^ 1);
+            }
+        }
+    }
+
+    // epilogue: acc[i][j][4g + e] = C[tile row wrow + i*32 + lane%32][col + 8g + 4(lane/32) + e]
+    if (active) {
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+            const int tr = wrow + i * 32 + (lane & 31);
+            const int h = tr >> 7, rl = tr & (HALF - 1);
+            if (rl >= h_rows[h]) continue;
+            uint16_t* crow = C + (int64_t)(h_row0[h] + rl) * ldc;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int c4 = 8 * g + 4 * (lane >> 5);
+                if (kSwiGLU) {
+                    const int col = nt * (BN / 2) + wn * 32 + c4;
+                    if (col < n_cols) {  // n_cols is a multiple of 64: all 4 or none
+                        float v[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float gt = acc[i][0][4 * g + e];
+                            const float up = acc[i][1][4 * g + e];
+                            v[e] = gt / (1.f + expf(-gt)) * up;
+                        }
+                        uint2 o;
+                        o.x = moe_pack_bf16x2(v[0], v[1]);
+                        o.y = moe_pack_bf16x2(v[2], v[3]);
+                        *reinterpret_cast<uint2*>(crow + col) = o;
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const int col = nt * BN + wn * 64 + j * 32 + c4;
+                        if (col < n_cols) {
+                            uint2 o;
+                            o.x = moe_pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]);
+                            o.y = moe_pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+                            *reinterpret_cast<uint2*>(crow + col) = o;
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
 // C[p][c] for the rows p of each tile (expert l):
 //   FC1 (kSwiGLU): act[p][c] = SiLU(A[p].W1[l][c]) * (A[p].W1[l][I + c]), c < I
 //   FC2:           yp[p][c]  = A[p].W2[l][c],                              c < H
@@ -295,7 +488,7 @@ ffn_bf16_kernel(const uint16_t* __restrict__ A, int64_t a_rows, int Kdim,
                 const uint16_t* __restrict__ B, int64_t b_expert_stride, int b_rows,
                 uint16_t* __restrict__ C, int ldc, int n_cols, int I, int NT,
                 int max_blocks, int32_t* __restrict__ ws) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM_BYTES];
     __shared__ int item_s;
     const int32_t* tiles = ws + WS_HEAD + max_blocks;
     int32_t* ctr = ws + (kSwiGLU ? WS_CTR_FC1 : WS_CTR_FC2);
@@ -303,15 +496,13 @@ ffn_bf16_kernel(const uint16_t* __restrict__ A, int64_t a_rows, int Kdim,
     const int tid = threadIdx.x;
     const int lane = moe_lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(tid / MOE_WAVE);
-    const int wm = wave >> 2;  // tile half (128 rows) this wave computes
-    const int wn = wave & 3;   // 64 B rows (FC1: 32 gate + the matching 32 up) of the tile
     const uint32_t smem_base = (uint32_t)(uintptr_t)(lds_u8_t*)smem;
 
     const int total = ws[WS_NTILES] * NT;
-    // Items (tile, column tile) in tile-major order are cut into 8 contiguous ranges, one per
-    // XCD (workgroup w runs on XCD w % 8), so the items in flight on an XCD share A rows and
-    // B rows in its L2.  Workgroups take items from their XCD's range through an atomic
-    // counter (in order, self-balancing); a workgroup whose range is drained helps the others.
+    // Items (tile, column tile) are cut into 8 contiguous ranges, one per XCD (workgroup w
+    // runs on XCD w % 8), so the items in flight on an XCD share A rows and B rows in its
+    // L2.  Workgroups take items from their XCD's range through an atomic counter (in order,
+    // self-balancing); a workgroup whose range is drained helps the others.
     const int xcd = blockIdx.x % kXcds;
     const int per_xcd_items = (total + kXcds - 1) / kXcds;
 
@@ -320,7 +511,6 @@ ffn_bf16_kernel(const uint16_t* __restrict__ A, int64_t a_rows, int Kdim,
     // w, which is the only part of the segment index that enters the swizzle.
     const int seg_row = lane >> 3;
     const int seg_lchunk = swz_chunk((wave & 1) * 8 + seg_row, lane & 7);
-    const int nk = Kdim / BK;
 
     int q = 0;  // queues tried: own XCD first, then the others in turn
     for (;;) {
@@ -354,146 +544,16 @@ ffn_bf16_kernel(const uint16_t* __restrict__ A, int64_t a_rows, int Kdim,
         const int l = tl[0];
         const int h_row0[2] = {tl[1], tl[3]};
         const int h_rows[2] = {tl[2], tl[4]};
-        const bool pair = h_rows[1] > 0;
         const uint16_t* Bexp = B + (int64_t)l * b_expert_stride;
-        const int copies = pair ? DMA_PER_WAVE : DMA_PER_WAVE - 2;  // a half tile skips A half 1
-        const bool active = pair || wm == 0;                         // waves of an empty half idle
-
-        // per copy: a wave-uniform base (A half 0, A half 1, or the expert's B) and this
-        // lane's byte offset from it (row * Kdim * 2 + chunk * 16; < 4 GiB)
-        const uint8_t* a0 = reinterpret_cast<const uint8_t*>(A + (int64_t)h_row0[0] * Kdim);
-        const uint8_t* a1 = reinterpret_cast<const uint8_t*>(A + (int64_t)h_row0[1] * Kdim);
-        const uint8_t* bx = reinterpret_cast<const uint8_t*>(Bexp);
-        // copy q = 0..3: A segment wave + 8q (q = 0, 1: half 0; q = 2, 3: half 1);
-        // copy q = 4..7: B segment wave + 8(q-4).  off = lane's byte offset from its base.
-        uint32_t off[DMA_PER_WAVE];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int h = q >> 1;
-            int rr = ((q & 1) * 8 + wave) * SEG_ROWS + seg_row;  // row within half h
-            if (h_row0[h] + rr > a_rows - 1) rr = (int)(a_rows - 1 - h_row0[h]);  // read, unused
-            off[q] = (uint32_t)rr * (uint32_t)Kdim * 2u + seg_lchunk * 16u;
-        }
-#pragma unroll
-        for (int q = 4; q < 8; ++q) {
-            const int rr = ((q - 4) * 8 + wave) * SEG_ROWS + seg_row;  // B row in the tile
-            int br;
-            if (kSwiGLU)
-                br = rr < BN / 2 ? nt * (BN / 2) + rr : I + nt * (BN / 2) + (rr - BN / 2);
-            else
-                br = nt * BN + rr;
-            if (br > b_rows - 1) br = b_rows - 1;  // columns past the end: read, not stored
-            off[q] = (uint32_t)br * (uint32_t)Kdim * 2u + seg_lchunk * 16u;
-        }
-        auto issue = [&](int kt) {
-            const uint32_t m0 = smem_base + (kt % STAGES) * STAGE_BYTES + wave * 8192;
-            const uint32_t koff = (uint32_t)kt * (BK * 2);
-            // A: half 0 segments (copies 0, 1), half 1 segments (2, 3) only for a pair
-            four_copies(m0, a0, a0 - 1024, a1 - 2048, a1 - 3072, off[0] + koff, off[1] + koff,
-                        off[2] + koff, off[3] + koff, pair);
-            four_copies(m0 + 4096, bx, bx - 1024, bx - 2048, bx - 3072, off[4] + koff,
-                        off[5] + koff, off[6] + koff, off[7] + koff, true);
-        };
-
-        f32x16_t acc[4][2];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-        // fragments double-buffered one 16-wide K step ahead of the MFMAs
-        bf16x8_t fa[2][4], fb[2][2];
-        auto load_frags = [&](int kt, int kk, int buf) {
-            const uint8_t* st = smem + (kt % STAGES) * STAGE_BYTES;
-            const int ch = kk * 2 + (lane >> 5);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int br = kSwiGLU ? j * (BN / 2) + wn * 32 + (lane & 31)
-                                       : wn * 64 + j * 32 + (lane & 31);
-                fb[buf][j] = lds_frag(st, br, true, ch);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                fa[buf][i] = lds_frag(st, wm * HALF + i * 32 + (lane & 31), false, ch);
-        };
-        // copies of this wave still allowed in flight when `pending` later stages are issued
-        auto pend = [&](int pending) { return pending * copies; };
-
-        __syncthreads();  // the previous tile's last LDS reads are done
-        const int pre = nk < STAGES ? nk : STAGES;  // every slot filled before the loop
-        for (int s = 0; s < pre; ++s) issue(s);
-        wait_copies_and_barrier(pend(pre - 1));
-        if (active) load_frags(0, 0, 0);
-
-        for (int kt = 0; kt < nk; ++kt) {
-#pragma unroll
-            for (int kk = 0; kk < BK / 16; ++kk) {
-                const int cur = kk & 1;
-                if (active) {
-                    if (kk + 1 < BK / 16) load_frags(kt, kk + 1, cur ^ 1);
-                    // D = B-rows x A-rows: lane keeps one A row and 4 consecutive columns per
-                    // register group, so the epilogue stores 8 bytes at a time
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int j = 0; j < 2; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                fb[cur][j], fa[cur][i], acc[i][j], 0, 0, 0);
-                }
-                if (kk + 1 == BK / 16 && kt + 1 < nk) {
-                    // behind slice kt's last MFMAs: wait for slice kt+1 everywhere (slices up
-                    // to kt+STAGES-1 are issued); then slice kt's stage is free for slice
-                    // kt+STAGES; first fragments of slice kt+1
-                    const int issued = kt + STAGES - 1 < nk ? kt + STAGES - 1 : nk - 1;
-                    wait_copies_and_barrier(pend(issued - (kt + 1)));
-                    if (kt + STAGES < nk) issue(kt + STAGES);
-                    if (active) load_frags(kt + 1, 0, cur ^ 1);
-                }
-            }
-        }
-
-        // epilogue: acc[i][j][4g + e] = C[row wm*128 + i*32 + lane%32][col + 8g + 4(lane/32) + e]
-        if (active) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int rl = i * 32 + (lane & 31);
-                if (rl >= h_rows[wm]) continue;
-                uint16_t* crow = C + (int64_t)(h_row0[wm] + rl) * ldc;
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int c4 = 8 * g + 4 * (lane >> 5);
-                    if (kSwiGLU) {
-                        const int col = nt * (BN / 2) + wn * 32 + c4;
-                        if (col < n_cols) {  // n_cols is a multiple of 64: all 4 or none
-                            float v[4];
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                const float gt = acc[i][0][4 * g + e];
-                                const float up = acc[i][1][4 * g + e];
-                                v[e] = gt / (1.f + expf(-gt)) * up;
-                            }
-                            uint2 o;
-                            o.x = moe_pack_bf16x2(v[0], v[1]);
-                            o.y = moe_pack_bf16x2(v[2], v[3]);
-                            *reinterpret_cast<uint2*>(crow + col) = o;
-                        }
-                    } else {
-#pragma unroll
-                        for (int j = 0; j < 2; ++j) {
-                            const int col = nt * BN + wn * 64 + j * 32 + c4;
-                            if (col < n_cols) {
-                                uint2 o;
-                                o.x = moe_pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]);
-                                o.y = moe_pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-                                *reinterpret_cast<uint2*>(crow + col) = o;
-                            }
-                        }
-                    }
-                }
-            }
-        }
+        if (h_rows[1] > 0)
+            gemm_item<kSwiGLU, 256>(A, a_rows, Kdim, Bexp, b_rows, C, ldc, n_cols, I, nt, h_row0,
+                                    h_rows, smem, smem_base, wave, lane, seg_row, seg_lchunk);
+        else if (h_rows[0] > 64)
+            gemm_item<kSwiGLU, 128>(A, a_rows, Kdim, Bexp, b_rows, C, ldc, n_cols, I, nt, h_row0,
+                                    h_rows, smem, smem_base, wave, lane, seg_row, seg_lchunk);
+        else
+            gemm_item<kSwiGLU, 64>(A, a_rows, Kdim, Bexp, b_rows, C, ldc, n_cols, I, nt, h_row0,
+                                   h_rows, smem, smem_base, wave, lane, seg_row, seg_lchunk);
         __syncthreads();  // everyone has read item_s before thread 0 takes the next item
     }
     // the last workgroup out clears this GEMM's counters so the kernel can run again
@@ -557,7 +617,7 @@ int persistent_grid() {
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
         cus = 256;
-    int g = cus / kXcds * kXcds;  // one workgroup per CU (128 KB of LDS each)
+    int g = cus / kXcds * kXcds;  // one workgroup per CU (144 KB of LDS each)
     return g < kXcds ? kXcds : g;
 }
 
