@@ -31,11 +31,15 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # a few hundred warm-up steps: the GPU's clocks take on the order of 100 ms to settle
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="olmoe_shaped")
     ap.add_argument("--skew", default=None, help="Zipf exponent or 'hot4' (default: middle skew)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--materialize", action="store_true",
+                    help="write the permuted copy xp of x (moe_permute with xp, moe_expert_ffn) "
+                         "instead of gathering x rows inside the gate/up GEMM")
     ap.add_argument("--graph", action="store_true",
                     help="time HIP-graph replays of the whole path instead of eager calls")
     ap.add_argument("--cpu-tokens", type=int, default=0,
@@ -195,7 +199,7 @@ def main():
     x = inputs.make_x(w).to(dev)
     layer = binding.RoutedExperts(w.T, w.H, w.E, w.K, w.I, w.P, dtype=dt, E_loc=w.n_local,
                                   expert_begin=w.expert_begin, expert_stride=w.expert_stride,
-                                  block_m=w.beta)
+                                  block_m=w.beta, gather=not args.materialize)
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
@@ -263,11 +267,14 @@ def main():
                    "K": w.K, "I": w.I, "P": w.P, "block_m": w.beta,
                    "skew": w.skew_label(skew), "local_entries": N, "blocks": nb,
                    "maxvio": round(maxvio, 3), "parallelism": "single GPU",
-                   "launch": "hip graph replay" if args.graph else "eager"},
+                   "launch": "hip graph replay" if args.graph else "eager",
+                   "dispatch": "materialised xp" if args.materialize else
+                               "gather-on-load (FC1 reads x rows through row_token)"},
         "gemm_tflops": round(flops_ffn / ffn_s / 1e12, 1),
         "gemm_frac_of_peak": round(flops_ffn / ffn_s / 1e12 / PEAK_BF16_TFLOPS, 4),
         "per_call_us": {k: round(v, 2) for k, v in per.items()},
-        "permute_gbs": round(permute_bytes / (per["permute"] * 1e-6) / 1e9, 1),
+        "permute_gbs": (round(permute_bytes / (per["permute"] * 1e-6) / 1e9, 1)
+                        if args.materialize else None),
         "combine_gbs": round(combine_bytes / (per["combine"] * 1e-6) / 1e9, 1),
         "ffn_t_roof_us": round(t_roof * 1e6, 2),
         "ffn_frac_of_t_roof": round(t_roof / ffn_s, 4),
@@ -279,7 +286,7 @@ def main():
     if not args.no_all_skews:
         by = []
         for sk in w.skews:
-            wl, pr, n_, nb_, cnt_, _ = measure(sk, max(5, args.steps // 2), 2)
+            wl, pr, n_, nb_, cnt_, _ = measure(sk, max(10, args.steps // 4), max(10, args.warmup // 4))
             f = 6.0 * w.H * w.I * n_
             ffn_t = (pr["fc1"] + pr["fc2"]) * 1e-6
             loc_ = cnt_[w.expert_begin::w.expert_stride][: w.n_local].tolist()

@@ -6,7 +6,8 @@
  *   moe_route       router top-k over precomputed logits, routing weights, expert counts
  *   moe_permute     dispatch permutation into expert-contiguous, beta-aligned row segments
  *   moe_plan        greedy skew-balancing plan over P logical rank partitions + block table
- *   moe_expert_ffn  SwiGLU expert FFN over the block table (grouped GEMMs on bf16 MFMA)
+ *   moe_expert_ffn  SwiGLU expert FFN over the block table (grouped GEMMs on bf16 MFMA);
+ *                   moe_expert_ffn_gather reads the token rows of x directly
  *   moe_combine     routing-weight combine of each token's expert outputs
  *
  * Sources (the pages these calls restate; cited by title and section):
@@ -106,6 +107,9 @@ moe_status_t moe_route(const float* logits, int T, int E, int K, int renormalize
  *   row_token      [max_rows] out: token of each row in [0, offsets[E_loc]); -1 on padding.
  *                  Rows at or beyond offsets[E_loc] are left untouched.
  *   xp             [max_rows, H] out: xp[entry_pos[i]] = x[i / K]; padding rows untouched.
+ *                  May be NULL: then only the indices are produced, for moe_expert_ffn_gather,
+ *                  which reads the token rows of x itself ([MF §2.1]: the dispatch and the
+ *                  expert GEMMs run as one pipeline, so the permuted copy need not exist).
  *   max_rows       rows allocated for row_token and xp (>= moe_max_rows).
  *   workspace      int32 scratch of workspace_elems >= moe_permute_workspace_elems.
  * Row bytes (H * element size) must be a multiple of 16. */
@@ -180,6 +184,28 @@ moe_status_t moe_expert_ffn_fc2(const void* act, const void* w2, moe_dtype_t dt,
                                 int max_blocks, void* yp, int64_t max_rows,
                                 int32_t* workspace, int64_t workspace_elems,
                                 hipStream_t stream);
+
+/* moe_expert_ffn with the dispatch gather folded into FC1's loads: row p of the GEMM input is
+ * x[row_token[p]] instead of xp[p] ([MF §2.1]: dispatch, FC1, FC2 and combine form one
+ * pipeline; the permuted copy of x is a layout choice, not part of the result).  Results
+ * are bit-identical to moe_permute (with xp) followed by moe_expert_ffn.
+ *   x          [T, H] activations (dtype dt), as given to moe_permute.
+ *   row_token  [max_rows] from moe_permute (which may then be called with xp = NULL).
+ * Other arguments as for moe_expert_ffn.  bf16 additionally needs T * H * 2 < 4 GiB
+ * (MOE_ERR_UNSUPPORTED otherwise). */
+moe_status_t moe_expert_ffn_gather(const void* x, const int32_t* row_token, int T,
+                                   const void* w1, const void* w2, moe_dtype_t dt, int H, int I,
+                                   int E_loc, const int32_t* blocks, const int32_t* n_blocks,
+                                   int max_blocks, void* act, void* yp, int64_t max_rows,
+                                   int32_t* workspace, int64_t workspace_elems,
+                                   hipStream_t stream);
+/* FC1 half of moe_expert_ffn_gather (FC2 is moe_expert_ffn_fc2, unchanged). */
+moe_status_t moe_expert_ffn_fc1_gather(const void* x, const int32_t* row_token, int T,
+                                       const void* w1, moe_dtype_t dt, int H, int I, int E_loc,
+                                       const int32_t* blocks, const int32_t* n_blocks,
+                                       int max_blocks, void* act, int64_t max_rows,
+                                       int32_t* workspace, int64_t workspace_elems,
+                                       hipStream_t stream);
 
 /* ---------------------------------------------------------------------- combine --- */
 

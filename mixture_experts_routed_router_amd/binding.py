@@ -44,6 +44,10 @@ _SIGNATURES = {
                                   _vp, _i64, _vp]),
     "moe_expert_ffn_fc2": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _i64,
                                   _vp, _i64, _vp]),
+    "moe_expert_ffn_gather": (_i32, [_vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp,
+                                     _vp, _i32, _vp, _vp, _i64, _vp, _i64, _vp]),
+    "moe_expert_ffn_fc1_gather": (_i32, [_vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp, _vp,
+                                         _i32, _vp, _i64, _vp, _i64, _vp]),
     "moe_combine": (_i32, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
 }
 
@@ -138,8 +142,11 @@ def moe_route(logits, K, topk_ids, topk_w, expert_counts, renormalize=True, stre
 
 def moe_permute(x, topk_ids, expert_counts, E, expert_begin, expert_stride, E_loc, block_m,
                 expert_offsets, entry_pos, row_token, xp, workspace, stream=None):
+    """xp may be None: indices only (for moe_expert_ffn_gather)."""
     T, H = x.shape
     K = topk_ids.shape[1]
+    if xp is not None and xp.shape[0] != row_token.shape[0]:
+        raise MoeError("moe_permute: xp and row_token must have max_rows rows")
     _check(lib().moe_permute(_ptr(x, None, "x"), _dt(x), T, H, K, E,
                              _ptr(topk_ids, torch.int32, "topk_ids"),
                              _ptr(expert_counts, torch.int32, "expert_counts"),
@@ -147,7 +154,7 @@ def moe_permute(x, topk_ids, expert_counts, E, expert_begin, expert_stride, E_lo
                              _ptr(expert_offsets, torch.int32, "expert_offsets"),
                              _ptr(entry_pos, torch.int32, "entry_pos"),
                              _ptr(row_token, torch.int32, "row_token"),
-                             _ptr(xp, x.dtype, "xp"), xp.shape[0],
+                             _ptr(xp, x.dtype, "xp"), row_token.shape[0],
                              _ptr(workspace, torch.int32, "workspace"), workspace.numel(),
                              _stream(stream)),
            "moe_permute")
@@ -180,6 +187,46 @@ def moe_expert_ffn(xp, w1, w2, blocks, n_blocks, act, yp, workspace, stream=None
                                 xp.shape[0], _ptr(workspace, torch.int32, "workspace"),
                                 workspace.numel(), _stream(stream)),
            "moe_expert_ffn")
+
+
+def moe_expert_ffn_gather(x, row_token, w1, w2, blocks, n_blocks, act, yp, workspace,
+                          stream=None):
+    """moe_expert_ffn on rows gathered from x by row_token (no permuted copy of x)."""
+    T, H = x.shape
+    E_loc, two_I, _ = w1.shape
+    I = two_I // 2
+    rows = row_token.shape[0]
+    if w1.shape[2] != H or w2.shape != (E_loc, H, I) or act.shape[1] != I or yp.shape[1] != H:
+        raise MoeError("moe_expert_ffn_gather: inconsistent shapes")
+    if act.shape[0] < rows or yp.shape[0] < rows:
+        raise MoeError("moe_expert_ffn_gather: act/yp have fewer rows than row_token")
+    _check(lib().moe_expert_ffn_gather(_ptr(x, x.dtype, "x"),
+                                       _ptr(row_token, torch.int32, "row_token"), T,
+                                       _ptr(w1, x.dtype, "w1"), _ptr(w2, x.dtype, "w2"), _dt(x),
+                                       H, I, E_loc, _ptr(blocks, torch.int32, "blocks"),
+                                       _ptr(n_blocks, torch.int32, "n_blocks"), blocks.shape[0],
+                                       _ptr(act, x.dtype, "act"), _ptr(yp, x.dtype, "yp"), rows,
+                                       _ptr(workspace, torch.int32, "workspace"),
+                                       workspace.numel(), _stream(stream)),
+           "moe_expert_ffn_gather")
+
+
+def moe_expert_ffn_fc1_gather(x, row_token, w1, blocks, n_blocks, act, workspace, stream=None):
+    T, H = x.shape
+    E_loc, two_I, _ = w1.shape
+    I = two_I // 2
+    rows = row_token.shape[0]
+    if w1.shape[2] != H or act.shape[1] != I or act.shape[0] < rows:
+        raise MoeError("moe_expert_ffn_fc1_gather: inconsistent shapes")
+    _check(lib().moe_expert_ffn_fc1_gather(_ptr(x, x.dtype, "x"),
+                                           _ptr(row_token, torch.int32, "row_token"), T,
+                                           _ptr(w1, x.dtype, "w1"), _dt(x), H, I, E_loc,
+                                           _ptr(blocks, torch.int32, "blocks"),
+                                           _ptr(n_blocks, torch.int32, "n_blocks"),
+                                           blocks.shape[0], _ptr(act, x.dtype, "act"), rows,
+                                           _ptr(workspace, torch.int32, "workspace"),
+                                           workspace.numel(), _stream(stream)),
+           "moe_expert_ffn_fc1_gather")
 
 
 def moe_expert_ffn_fc1(xp, w1, blocks, n_blocks, act, workspace, stream=None):
@@ -231,8 +278,9 @@ class RoutedExperts:
     """
 
     def __init__(self, T, H, E, K, I, P, dtype=torch.bfloat16, E_loc=None, expert_begin=0,
-                 expert_stride=1, block_m=128, renormalize=True, device="cuda"):
+                 expert_stride=1, block_m=128, renormalize=True, device="cuda", gather=False):
         self.T, self.H, self.E, self.K, self.I, self.P = T, H, E, K, I, P
+        self.gather = gather  # FC1 reads x rows through row_token; xp is never written
         self.E_loc = E_loc or E
         self.begin, self.stride, self.block_m = expert_begin, expert_stride, block_m
         self.renormalize = renormalize
@@ -250,7 +298,7 @@ class RoutedExperts:
         self.entry_pos = torch.empty((T * K,), **i32)
         self.row_token = torch.empty((self.max_rows,), **i32)
         self.workspace = torch.empty((moe_permute_workspace_elems(T, self.E_loc),), **i32)
-        self.xp = torch.empty((self.max_rows, H), dtype=dtype, device=device)
+        self.xp = None if gather else torch.empty((self.max_rows, H), dtype=dtype, device=device)
         self.q = torch.empty((self.E_loc, P), **i32)
         self.moves = torch.empty((self.max_moves, 4), **i32)
         self.n_moves = torch.empty((1,), **i32)
@@ -266,6 +314,7 @@ class RoutedExperts:
         moe_route(logits, self.K, self.topk_ids, self.topk_w, self.counts, self.renormalize, stream)
 
     def permute(self, x, stream=None):
+        self._x = x
         moe_permute(x, self.topk_ids, self.counts, self.E, self.begin, self.stride, self.E_loc,
                     self.block_m, self.offsets, self.entry_pos, self.row_token, self.xp,
                     self.workspace, stream)
@@ -276,12 +325,20 @@ class RoutedExperts:
                  stream)
 
     def expert_ffn(self, w1, w2, stream=None):
-        moe_expert_ffn(self.xp, w1, w2, self.blocks, self.n_blocks, self.act, self.yp,
-                       self.ffn_workspace, stream)
+        if self.gather:
+            moe_expert_ffn_gather(self._x, self.row_token, w1, w2, self.blocks, self.n_blocks,
+                                  self.act, self.yp, self.ffn_workspace, stream)
+        else:
+            moe_expert_ffn(self.xp, w1, w2, self.blocks, self.n_blocks, self.act, self.yp,
+                           self.ffn_workspace, stream)
 
     def expert_ffn_fc1(self, w1, stream=None):
-        moe_expert_ffn_fc1(self.xp, w1, self.blocks, self.n_blocks, self.act, self.ffn_workspace,
-                           stream)
+        if self.gather:
+            moe_expert_ffn_fc1_gather(self._x, self.row_token, w1, self.blocks, self.n_blocks,
+                                      self.act, self.ffn_workspace, stream)
+        else:
+            moe_expert_ffn_fc1(self.xp, w1, self.blocks, self.n_blocks, self.act,
+                               self.ffn_workspace, stream)
 
     def expert_ffn_fc2(self, w2, stream=None):
         moe_expert_ffn_fc2(self.act, w2, self.blocks, self.n_blocks, self.yp, self.ffn_workspace,

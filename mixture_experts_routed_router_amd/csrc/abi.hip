@@ -72,14 +72,14 @@ moe_status_t moe_permute(const void* x, moe_dtype_t dt, int T, int H, int K, int
                          void* xp, int64_t max_rows, int32_t* workspace,
                          int64_t workspace_elems, hipStream_t stream) {
     if (!x || !topk_ids || !expert_counts || !expert_offsets || !entry_pos || !row_token ||
-        !xp || !workspace)
+        !workspace)
         return MOE_ERR_INVALID;
     if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID;
     if (T < 1 || H < 1 || K < 1 || K > E || !valid_block_m(block_m)) return MOE_ERR_INVALID;
     if (!valid_local_set(E, expert_begin, expert_stride, E_loc)) return MOE_ERR_INVALID;
     if ((int64_t)T * K > 0x7FFFFFFFLL) return MOE_ERR_INVALID;
     const int64_t row_bytes = (int64_t)H * (dt == MOE_BF16 ? 2 : 4);
-    if (row_bytes % 16 != 0 || !aligned16(x) || !aligned16(xp)) return MOE_ERR_INVALID;
+    if (row_bytes % 16 != 0 || !aligned16(x) || (xp && !aligned16(xp))) return MOE_ERR_INVALID;
     if (max_rows < moe_max_rows(T, K, E_loc, block_m)) return MOE_ERR_INVALID;
     if (max_rows > 0x7FFFFFFFLL) return MOE_ERR_UNSUPPORTED;
     if (workspace_elems < moe_permute_workspace_elems(T, E_loc)) return MOE_ERR_INVALID;
@@ -139,7 +139,31 @@ moe_status_t moe_expert_ffn_fc1(const void* xp, const void* w1, moe_dtype_t dt, 
         if (st != MOE_OK) return st;
     }
     return launched(moe_launch_ffn_fc1(xp, w1, dt, H, I, blocks, n_blocks, max_blocks,
-                                       workspace, act, max_rows, stream));
+                                       workspace, act, max_rows, nullptr, stream));
+}
+
+moe_status_t moe_expert_ffn_fc1_gather(const void* x, const int32_t* row_token, int T,
+                                       const void* w1, moe_dtype_t dt, int H, int I, int E_loc,
+                                       const int32_t* blocks, const int32_t* n_blocks,
+                                       int max_blocks, void* act, int64_t max_rows,
+                                       int32_t* workspace, int64_t workspace_elems,
+                                       hipStream_t stream) {
+    if (!x || !row_token || !w1 || !blocks || !n_blocks || !act || !workspace)
+        return MOE_ERR_INVALID;
+    if (!aligned16(x) || !aligned16(w1) || !aligned16(act) || T < 1) return MOE_ERR_INVALID;
+    moe_status_t st = check_ffn_shape(dt, H, I, E_loc, max_blocks, max_rows);
+    if (st != MOE_OK) return st;
+    if (workspace_elems < moe_ffn_workspace_elems(max_blocks)) return MOE_ERR_INVALID;
+    if (E_loc > 256) return MOE_ERR_UNSUPPORTED;
+    // the bf16 GEMM addresses x rows with 32-bit byte offsets
+    if (dt == MOE_BF16 && (int64_t)T * H * 2 > 0xFFFFFFFFLL - 16) return MOE_ERR_UNSUPPORTED;
+    if (dt == MOE_BF16) {
+        st = launched(moe_launch_ffn_schedule(blocks, n_blocks, max_blocks, E_loc, workspace,
+                                              stream));
+        if (st != MOE_OK) return st;
+    }
+    return launched(moe_launch_ffn_fc1(x, w1, dt, H, I, blocks, n_blocks, max_blocks, workspace,
+                                       act, T, row_token, stream));
 }
 
 moe_status_t moe_expert_ffn_fc2(const void* act, const void* w2, moe_dtype_t dt, int H, int I,
@@ -165,6 +189,21 @@ moe_status_t moe_expert_ffn(const void* xp, const void* w1, const void* w2, moe_
     if (!w2 || !yp || !aligned16(w2) || !aligned16(yp)) return MOE_ERR_INVALID;
     moe_status_t st = moe_expert_ffn_fc1(xp, w1, dt, H, I, E_loc, blocks, n_blocks, max_blocks,
                                          act, max_rows, workspace, workspace_elems, stream);
+    if (st != MOE_OK) return st;
+    return moe_expert_ffn_fc2(act, w2, dt, H, I, E_loc, blocks, n_blocks, max_blocks, yp,
+                              max_rows, workspace, workspace_elems, stream);
+}
+
+moe_status_t moe_expert_ffn_gather(const void* x, const int32_t* row_token, int T,
+                                   const void* w1, const void* w2, moe_dtype_t dt, int H, int I,
+                                   int E_loc, const int32_t* blocks, const int32_t* n_blocks,
+                                   int max_blocks, void* act, void* yp, int64_t max_rows,
+                                   int32_t* workspace, int64_t workspace_elems,
+                                   hipStream_t stream) {
+    if (!w2 || !yp || !aligned16(w2) || !aligned16(yp)) return MOE_ERR_INVALID;
+    moe_status_t st = moe_expert_ffn_fc1_gather(x, row_token, T, w1, dt, H, I, E_loc, blocks,
+                                                n_blocks, max_blocks, act, max_rows, workspace,
+                                                workspace_elems, stream);
     if (st != MOE_OK) return st;
     return moe_expert_ffn_fc2(act, w2, dt, H, I, E_loc, blocks, n_blocks, max_blocks, yp,
                               max_rows, workspace, workspace_elems, stream);

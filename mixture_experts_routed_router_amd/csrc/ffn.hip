@@ -329,7 +329,8 @@ __device__ __forceinline__ void gemm_item(const uint16_t* __restrict__ A, int64_
                                           uint16_t* __restrict__ C, int ldc, int n_cols, int I,
                                           int nt, const int (&h_row0)[2], const int (&h_rows)[2],
                                           uint8_t* smem, uint32_t smem_base, int wave, int lane,
-                                          int seg_row, int seg_lchunk) {
+                                          int seg_row, int seg_lchunk,
+                                          const int32_t* __restrict__ gather) {
     using M = Mode<kRowsA>;
     constexpr int RB = M::kRowBlocks;
     const int wm = wave >> 2;
@@ -340,17 +341,26 @@ __device__ __forceinline__ void gemm_item(const uint16_t* __restrict__ A, int64_
 
     // per copy: a wave-uniform base (A half 0, A half 1, or the expert's B) and this lane's
     // byte offset from it (row * Kdim * 2 + chunk * 16; < 4 GiB).  A copy q fills segment
-    // wave + 8q: tile rows 64q + 8 wave + (0..7), i.e. half q / 2.
-    const uint8_t* a0 = reinterpret_cast<const uint8_t*>(A + (int64_t)h_row0[0] * Kdim);
-    const uint8_t* a1 = reinterpret_cast<const uint8_t*>(A + (int64_t)h_row0[1] * Kdim);
+    // wave + 8q: tile rows 64q + 8 wave + (0..7), i.e. half q / 2.  With `gather`, tile row p
+    // is row gather[p] of A (the token's row of x) and every A copy uses the base A.
+    const uint8_t* a0 = reinterpret_cast<const uint8_t*>(gather ? A : A + (int64_t)h_row0[0] * Kdim);
+    const uint8_t* a1 = reinterpret_cast<const uint8_t*>(gather ? A : A + (int64_t)h_row0[1] * Kdim);
     const uint8_t* bx = reinterpret_cast<const uint8_t*>(Bexp);
     uint32_t offa[M::kACopies], offb[4];
 #pragma unroll
     for (int q = 0; q < M::kACopies; ++q) {
         const int h = q >> 1;
         int rr = ((q & 1) * 8 + wave) * SEG_ROWS + seg_row;  // row within half h
-        if (h_row0[h] + rr > a_rows - 1) rr = (int)(a_rows - 1 - h_row0[h]);  // read, unused
-        offa[q] = (uint32_t)rr * (uint32_t)Kdim * 2u + seg_lchunk * 16u;
+        int64_t arow;
+        if (gather) {
+            if (rr > h_rows[h] - 1) rr = h_rows[h] - 1;  // rows past the piece: read, unused
+            const int tok = gather[h_row0[h] + rr];
+            arow = tok < 0 ? 0 : tok;
+        } else {
+            if (h_row0[h] + rr > a_rows - 1) rr = (int)(a_rows - 1 - h_row0[h]);  // read, unused
+            arow = rr;
+        }
+        offa[q] = (uint32_t)arow * (uint32_t)Kdim * 2u + seg_lchunk * 16u;
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -481,13 +491,15 @@ __device__ __forceinline__ void gemm_item(const uint16_t* __restrict__ A, int64_
 // C[p][c] for the rows p of each tile (expert l):
 //   FC1 (kSwiGLU): act[p][c] = SiLU(A[p].W1[l][c]) * (A[p].W1[l][I + c]), c < I
 //   FC2:           yp[p][c]  = A[p].W2[l][c],                              c < H
-// A is [a_rows, Kdim], B per expert [b_rows, Kdim]; both K-contiguous.
+// A is [a_rows, Kdim], B per expert [b_rows, Kdim]; both K-contiguous.  With `gather`
+// (row_token of the dispatch permutation), A[p] above means A[gather[p]]: the rows are read
+// straight from the token rows of x and no permuted copy is needed.
 template <bool kSwiGLU>
 __global__ void __launch_bounds__(kThreads, 1)
 ffn_bf16_kernel(const uint16_t* __restrict__ A, int64_t a_rows, int Kdim,
                 const uint16_t* __restrict__ B, int64_t b_expert_stride, int b_rows,
                 uint16_t* __restrict__ C, int ldc, int n_cols, int I, int NT,
-                int max_blocks, int32_t* __restrict__ ws) {
+                int max_blocks, int32_t* __restrict__ ws, const int32_t* __restrict__ gather) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM_BYTES];
     __shared__ int item_s;
     const int32_t* tiles = ws + WS_HEAD + max_blocks;
@@ -547,13 +559,16 @@ ffn_bf16_kernel(const uint16_t* __restrict__ A, int64_t a_rows, int Kdim,
         const uint16_t* Bexp = B + (int64_t)l * b_expert_stride;
         if (h_rows[1] > 0)
             gemm_item<kSwiGLU, 256>(A, a_rows, Kdim, Bexp, b_rows, C, ldc, n_cols, I, nt, h_row0,
-                                    h_rows, smem, smem_base, wave, lane, seg_row, seg_lchunk);
+                                    h_rows, smem, smem_base, wave, lane, seg_row, seg_lchunk,
+                                    gather);
         else if (h_rows[0] > 64)
             gemm_item<kSwiGLU, 128>(A, a_rows, Kdim, Bexp, b_rows, C, ldc, n_cols, I, nt, h_row0,
-                                    h_rows, smem, smem_base, wave, lane, seg_row, seg_lchunk);
+                                    h_rows, smem, smem_base, wave, lane, seg_row, seg_lchunk,
+                                    gather);
         else
             gemm_item<kSwiGLU, 64>(A, a_rows, Kdim, Bexp, b_rows, C, ldc, n_cols, I, nt, h_row0,
-                                   h_rows, smem, smem_base, wave, lane, seg_row, seg_lchunk);
+                                   h_rows, smem, smem_base, wave, lane, seg_row, seg_lchunk,
+                                    gather);
         __syncthreads();  // everyone has read item_s before thread 0 takes the next item
     }
     // the last workgroup out clears this GEMM's counters so the kernel can run again
@@ -570,7 +585,8 @@ ffn_bf16_kernel(const uint16_t* __restrict__ A, int64_t a_rows, int Kdim,
 __global__ void __launch_bounds__(256)
 ffn_f32_gateup_kernel(const float* __restrict__ xp, const float* __restrict__ w1, int H, int I,
                       const int32_t* __restrict__ blocks, const int32_t* __restrict__ n_blocks_ptr,
-                      int max_blocks, float* __restrict__ act) {
+                      int max_blocks, float* __restrict__ act,
+                      const int32_t* __restrict__ gather) {
     int nb = *n_blocks_ptr;
     nb = nb < max_blocks ? nb : max_blocks;
     for (int b = blockIdx.x; b < nb; b += gridDim.x) {
@@ -578,7 +594,8 @@ ffn_f32_gateup_kernel(const float* __restrict__ xp, const float* __restrict__ w1
         const float* wg = w1 + (int64_t)l * 2 * I * H;
         for (int idx = threadIdx.x; idx < m * I; idx += blockDim.x) {
             const int r = idx / I, i = idx - r * I;
-            const float* x = xp + (int64_t)(row0 + r) * H;
+            const int64_t arow = gather ? gather[row0 + r] : row0 + r;
+            const float* x = xp + arow * H;
             const float* g_row = wg + (int64_t)i * H;
             const float* u_row = wg + (int64_t)(I + i) * H;
             float g = 0.f, u = 0.f;
@@ -633,21 +650,21 @@ hipError_t moe_launch_ffn_schedule(const int32_t* blocks, const int32_t* n_block
     return hipGetLastError();
 }
 
-hipError_t moe_launch_ffn_fc1(const void* xp, const void* w1, moe_dtype_t dt, int H, int I,
+hipError_t moe_launch_ffn_fc1(const void* a, const void* w1, moe_dtype_t dt, int H, int I,
                               const int32_t* blocks, const int32_t* n_blocks, int max_blocks,
-                              int32_t* ws, void* act, int64_t max_rows,
+                              int32_t* ws, void* act, int64_t a_rows, const int32_t* gather,
                               hipStream_t stream) {
     if (dt == MOE_F32) {
         int grid = max_blocks < 1024 ? max_blocks : 1024;
         ffn_f32_gateup_kernel<<<grid, 256, 0, stream>>>(
-            static_cast<const float*>(xp), static_cast<const float*>(w1), H, I, blocks, n_blocks,
-            max_blocks, static_cast<float*>(act));
+            static_cast<const float*>(a), static_cast<const float*>(w1), H, I, blocks, n_blocks,
+            max_blocks, static_cast<float*>(act), gather);
         return hipGetLastError();
     }
     ffn_bf16_kernel<true><<<persistent_grid(), kThreads, 0, stream>>>(
-        static_cast<const uint16_t*>(xp), max_rows, H, static_cast<const uint16_t*>(w1),
+        static_cast<const uint16_t*>(a), a_rows, H, static_cast<const uint16_t*>(w1),
         (int64_t)2 * I * H, 2 * I, static_cast<uint16_t*>(act), I, I, I,
-        (I + BN / 2 - 1) / (BN / 2), max_blocks, ws);
+        (I + BN / 2 - 1) / (BN / 2), max_blocks, ws, gather);
     return hipGetLastError();
 }
 
@@ -665,6 +682,6 @@ hipError_t moe_launch_ffn_fc2(const void* act, const void* w2, moe_dtype_t dt, i
     ffn_bf16_kernel<false><<<persistent_grid(), kThreads, 0, stream>>>(
         static_cast<const uint16_t*>(act), max_rows, I, static_cast<const uint16_t*>(w2),
         (int64_t)H * I, H, static_cast<uint16_t*>(yp), H, H, I, (H + BN - 1) / BN, max_blocks,
-        ws);
+        ws, nullptr);
     return hipGetLastError();
 }

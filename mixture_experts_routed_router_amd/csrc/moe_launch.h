@@ -26,9 +26,9 @@ int64_t moe_ffn_workspace_elems_impl(int max_blocks);
 hipError_t moe_launch_ffn_schedule(const int32_t* blocks, const int32_t* n_blocks, int max_blocks,
                                    int E_loc, int32_t* ws, hipStream_t stream);
 
-hipError_t moe_launch_ffn_fc1(const void* xp, const void* w1, moe_dtype_t dt, int H, int I,
+hipError_t moe_launch_ffn_fc1(const void* a, const void* w1, moe_dtype_t dt, int H, int I,
                               const int32_t* blocks, const int32_t* n_blocks, int max_blocks,
-                              int32_t* ws, void* act, int64_t max_rows,
+                              int32_t* ws, void* act, int64_t a_rows, const int32_t* gather,
                               hipStream_t stream);
 
 hipError_t moe_launch_ffn_fc2(const void* act, const void* w2, moe_dtype_t dt, int H, int I,

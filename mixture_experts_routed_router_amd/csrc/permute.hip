@@ -14,7 +14,8 @@
 //           mask per expert (a token's K experts are distinct, so each (token, expert) pair
 //           is one entry); writes entry_pos and row_token;
 //   copy    each token row of x that has a local entry is read once and written to each of
-//           its local rows of xp, 16 bytes per thread (the HBM-bound part).
+//           its local rows of xp, 16 bytes per thread (the HBM-bound part); skipped when xp
+//           is not wanted (the expert GEMM then reads x rows through row_token itself).
 #include "moe_launch.h"
 
 namespace {
@@ -177,6 +178,7 @@ hipError_t moe_launch_permute(const void* x, int64_t row_bytes, int T, int K,
                                                          n_chunks, ws, offsets, row_token);
     permute_scatter_kernel<<<n_chunks, kThreads, 0, stream>>>(ids, T, K, begin, stride, E_loc, ws,
                                                                offsets, entry_pos, row_token);
+    if (xp == nullptr) return hipGetLastError();  // indices only: the GEMM gathers x rows
     const int segs = (int)((row_bytes / 16 + kThreads - 1) / kThreads);
     int64_t grid = (int64_t)T * segs;
     if (grid > 65536) grid = 65536;

@@ -87,11 +87,13 @@ def random_case(seed, T, H, E, K, I, P, dtype=torch.bfloat16, E_loc=0, begin=0, 
                 E_loc=E_loc, begin=begin, stride=stride, block_m=block_m, renormalize=renormalize)
 
 
-def run_gpu(c: Case, dev="cuda"):
-    """The whole path through the C ABI; returns the layer object (all buffers on device)."""
+def run_gpu(c: Case, dev="cuda", gather=False):
+    """The whole path through the C ABI; returns the layer object (all buffers on device).
+    gather: FC1 reads x rows through row_token and xp is not materialised."""
     layer = binding.RoutedExperts(c.T, c.H, c.E, c.K, c.I, c.P, dtype=c.dtype, E_loc=c.n_local,
                                   expert_begin=c.begin, expert_stride=c.stride,
-                                  block_m=c.block_m, renormalize=c.renormalize, device=dev)
+                                  block_m=c.block_m, renormalize=c.renormalize, device=dev,
+                                  gather=gather)
     logits = torch.from_numpy(c.logits).to(dev)
     x = c.x.to(dev)
     W1, W2 = c.W1.to(dev), c.W2.to(dev)

@@ -111,6 +111,13 @@ def test_ffn_and_combine_reject(lib):
     assert ffn(1, 2880, 100) == UNSUPPORTED   # bf16 needs multiples of 64
     assert ffn(0, 126, 256) == UNSUPPORTED    # float32 needs multiples of 4
     assert ffn(1, 128, 256, ws_elems=271) == INVALID  # schedule scratch below 32 + 15*max_blocks
+    gather = lambda row_token=P[8], T=64, H=128, ws_elems=272: lib.moe_expert_ffn_gather(
+        P[0], row_token, T, P[1], P[2], 1, H, 256, 8, P[3], P[4], 16, P[5], P[6], 1024, P[7],
+        ws_elems, NULL)
+    assert gather(row_token=NULL) == INVALID
+    assert gather(T=0) == INVALID
+    assert gather(ws_elems=271) == INVALID
+    assert gather(T=1 << 22, H=1024) == UNSUPPORTED  # 8 GiB of x: past 32-bit row offsets
     assert lib.moe_combine(P[0], 1, P[1], P[2], 4, 100, 2, P[3], NULL) == INVALID  # 200-B rows
     assert lib.moe_combine(P[0], 1, P[1], NULL, 4, 128, 2, P[3], NULL) == INVALID
     assert lib.moe_combine(P[0], 1, P[1], P[2], 0, 128, 2, P[3], NULL) == INVALID

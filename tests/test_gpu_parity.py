@@ -156,6 +156,62 @@ def test_graph_replay_matches_eager():
     del graph
 
 
+# ------------------------------------------------- gather-on-load expert FFN ---
+
+GATHER_CASES = [
+    ("ragged", dict(seed=1, T=37, H=128, E=12, K=3, I=192, P=4, block_m=32)),
+    ("subset_local", dict(seed=4, T=300, H=128, E=16, K=3, I=128, P=2, E_loc=4, begin=1,
+                          stride=3, block_m=64)),
+    ("hot_experts", dict(seed=5, T=700, H=64, E=8, K=2, I=64, P=4,
+                         logit_bias=[30, 29, 0, 0, 0, 0, 0, 0])),
+    ("wide_k", dict(seed=8, T=80, H=64, E=256, K=16, I=64, P=16, block_m=16)),
+    ("f32_ragged", dict(seed=9, T=50, H=32, E=6, K=2, I=48, P=3, dtype=torch.float32,
+                        block_m=16)),
+    ("many_blocks", dict(seed=15, T=8192, H=64, E=64, K=8, I=64, P=8, block_m=16)),
+]
+
+
+def _gather_vs_materialised(c):
+    """The gather path against the materialising path (bit for bit) and the oracle."""
+    mat = run_gpu(c)
+    gat = run_gpu(c, gather=True)
+    ref = oracle_index(c)
+    check_index_parity(gat, ref)
+    assert gat.xp is None
+    rows = int(host(mat.offsets)[-1])
+    valid = torch.nonzero(mat.row_token[:rows] >= 0).squeeze(1)
+    for name in ("act", "yp"):
+        assert torch.equal(getattr(gat, name)[valid], getattr(mat, name)[valid]), name
+    assert torch.equal(gat.out, mat.out), "out"
+    return mat, gat, ref
+
+
+@pytest.mark.parametrize("name,kw", GATHER_CASES)
+def test_gather_small_layers(name, kw):
+    c = random_case(**kw)
+    _announce(f"gather {name} {kw}")
+    _, gat, ref = _gather_vs_materialised(c)
+    # and against the oracle on every row
+    x = inputs.as_oracle_array(c.x)
+    _, _, _, xp = oracle.permute(ref.ids, ref.counts, c.E, c.begin, c.stride, c.n_local,
+                                 c.block_m, x)
+    valid = ref.row_token >= 0
+    act, yp = oracle.ffn_blocks(xp, inputs.as_oracle_array(c.W1), inputs.as_oracle_array(c.W2),
+                                ref.blocks)
+    e_act = rel_frob(to_f64(host(gat.act)[: len(valid)][valid]), to_f64(act[valid]))
+    e_out = rel_frob(to_f64(host(gat.out)), to_f64(oracle.combine(yp, ref.w, ref.entry_pos,
+                                                                   c.T, c.K)))
+    assert e_act <= c.tol and e_out <= c.tol, (e_act, e_out)
+
+
+def test_gather_full_size_olmoe():
+    """Full OLMoE-shaped layer: gather path bit-identical to the materialising path."""
+    _announce("gather full olmoe_shaped s=1.2")
+    c = workload_case("olmoe_shaped", 1.2, weights=_weights("olmoe_shaped"))
+    _gather_vs_materialised(c)
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------ full-size layers: sampled ---
 
 FULL = [(n, s) for n in ("olmoe_shaped", "qwen3_30b_a3b_shaped", "gpt_oss_120b_shaped",
