@@ -185,6 +185,14 @@ moe_status_t moe_expert_ffn_fc2(const void* act, const void* w2, moe_dtype_t dt,
                                 int32_t* workspace, int64_t workspace_elems,
                                 hipStream_t stream);
 
+/* The bf16 FC1 calls start with this: the GEMM tile schedule of the block table, written to
+ * `workspace` (each expert's row-contiguous blocks cut into 128-row pieces, paired into
+ * 256-row tiles; the GEMMs' work counters cleared).  Exposed so that it can be timed apart
+ * from the GEMM; calling it is never required.  Arguments as for moe_expert_ffn. */
+moe_status_t moe_expert_ffn_tile_schedule(const int32_t* blocks, const int32_t* n_blocks,
+                                          int max_blocks, int E_loc, int32_t* workspace,
+                                          int64_t workspace_elems, hipStream_t stream);
+
 /* moe_expert_ffn with the dispatch gather folded into FC1's loads: row p of the GEMM input is
  * x[row_token[p]] instead of xp[p] ([MF §2.1]: dispatch, FC1, FC2 and combine form one
  * pipeline; the permuted copy of x is a layout choice, not part of the result).  Results

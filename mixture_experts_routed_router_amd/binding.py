@@ -48,6 +48,7 @@ _SIGNATURES = {
                                      _vp, _i32, _vp, _vp, _i64, _vp, _i64, _vp]),
     "moe_expert_ffn_fc1_gather": (_i32, [_vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp, _vp,
                                          _i32, _vp, _i64, _vp, _i64, _vp]),
+    "moe_expert_ffn_tile_schedule": (_i32, [_vp, _vp, _i32, _i32, _vp, _i64, _vp]),
     "moe_combine": (_i32, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
 }
 
@@ -187,6 +188,16 @@ def moe_expert_ffn(xp, w1, w2, blocks, n_blocks, act, yp, workspace, stream=None
                                 xp.shape[0], _ptr(workspace, torch.int32, "workspace"),
                                 workspace.numel(), _stream(stream)),
            "moe_expert_ffn")
+
+
+def moe_expert_ffn_tile_schedule(blocks, n_blocks, E_loc, workspace, stream=None):
+    """The GEMM tile schedule that the bf16 FC1 calls compute first (for timing it alone)."""
+    _check(lib().moe_expert_ffn_tile_schedule(_ptr(blocks, torch.int32, "blocks"),
+                                              _ptr(n_blocks, torch.int32, "n_blocks"),
+                                              blocks.shape[0], E_loc,
+                                              _ptr(workspace, torch.int32, "workspace"),
+                                              workspace.numel(), _stream(stream)),
+           "moe_expert_ffn_tile_schedule")
 
 
 def moe_expert_ffn_gather(x, row_token, w1, w2, blocks, n_blocks, act, yp, workspace,
@@ -343,6 +354,10 @@ class RoutedExperts:
     def expert_ffn_fc2(self, w2, stream=None):
         moe_expert_ffn_fc2(self.act, w2, self.blocks, self.n_blocks, self.yp, self.ffn_workspace,
                            stream)
+
+    def tile_schedule(self, stream=None):
+        moe_expert_ffn_tile_schedule(self.blocks, self.n_blocks, self.E_loc, self.ffn_workspace,
+                                     stream)
 
     def combine(self, stream=None):
         moe_combine(self.yp, self.topk_w, self.entry_pos, self.out, stream)

@@ -122,6 +122,17 @@ int64_t moe_ffn_workspace_elems(int max_blocks) {
     return moe_ffn_workspace_elems_impl(max_blocks);
 }
 
+moe_status_t moe_expert_ffn_tile_schedule(const int32_t* blocks, const int32_t* n_blocks,
+                                          int max_blocks, int E_loc, int32_t* workspace,
+                                          int64_t workspace_elems, hipStream_t stream) {
+    if (!blocks || !n_blocks || !workspace || max_blocks < 1 || E_loc < 1)
+        return MOE_ERR_INVALID;
+    if (workspace_elems < moe_ffn_workspace_elems(max_blocks)) return MOE_ERR_INVALID;
+    if (E_loc > 256) return MOE_ERR_UNSUPPORTED;
+    return launched(moe_launch_ffn_schedule(blocks, n_blocks, max_blocks, E_loc, workspace,
+                                            stream));
+}
+
 moe_status_t moe_expert_ffn_fc1(const void* xp, const void* w1, moe_dtype_t dt, int H, int I,
                                 int E_loc, const int32_t* blocks, const int32_t* n_blocks,
                                 int max_blocks, void* act, int64_t max_rows,

@@ -186,78 +186,102 @@ __device__ __forceinline__ void wait_copies_and_barrier(int n) {
 // thread per expert) touch LDS only; larger tables are walked in global memory.
 constexpr int kSchedLds = 3072;
 
-__global__ void __launch_bounds__(256)
-ffn_schedule_kernel(const int32_t* __restrict__ blocks, const int32_t* __restrict__ n_blocks_ptr,
-                    int max_blocks, int E_loc, int32_t* __restrict__ ws) {
-    __shared__ int cnt[256];
-    __shared__ int bstart[257];
-    __shared__ int npieces[256];
-    __shared__ int tstart[257];
-    __shared__ int running[256];
-    __shared__ unsigned long long mask[4][256];
-    __shared__ int s_l[kSchedLds], s_first[kSchedLds], s_rows[kSchedLds], s_sorted[kSchedLds];
+// Exclusive prefix sum of v over the 256 threads of the workgroup (thread order); *total gets
+// the sum.  part holds one int per wave.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* part, int* total) {
+    const int lane = moe_lane_id(), wave = threadIdx.x / MOE_WAVE;
+    int incl = v;
+#pragma unroll
+    for (int d = 1; d < MOE_WAVE; d <<= 1) {
+        const int o = __shfl_up(incl, d, MOE_WAVE);
+        if (lane >= d) incl += o;
+    }
+    if (lane == MOE_WAVE - 1) part[wave] = incl;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const int pw = part[w];
+        before += w < wave ? pw : 0;
+        all += pw;
+    }
+    *total = all;
+    __syncthreads();  // part may be reused
+    return before + incl - v;
+}
+
+struct SchedShared {
+    int sum_rows[256];
+    int min_first[256];
+    int max_end[256];
+    int cnt[256];
+    int bstart[257];
+    int npieces[256];
+    int tstart[257];
+    int running[256];
+    unsigned long long mask[4][256];
+    int s_l[kSchedLds], s_first[kSchedLds], s_rows[kSchedLds], s_sorted[kSchedLds];
+    int scan_part[4];
+};
+
+// kLds: the table (nb <= kSchedLds blocks) has been staged in sh.s_*; otherwise it is read
+// from global memory.  Two instantiations, so that neither path carries the other's loads.
+template <bool kLds>
+__device__ __forceinline__ void schedule_body(const int32_t* __restrict__ blocks, int nb,
+                                              int max_blocks, int E_loc,
+                                              int32_t* __restrict__ ws, SchedShared& sh) {
     const int tid = threadIdx.x, lane = moe_lane_id(), wave = tid / MOE_WAVE;
     int32_t* sorted_g = ws + WS_HEAD;
     int32_t* tiles = ws + WS_HEAD + max_blocks;
-    int nb = *n_blocks_ptr;
-    nb = nb < max_blocks ? nb : max_blocks;
-    const bool in_lds = nb <= kSchedLds;
-    if (tid >= WS_CTR_FC1 && tid < WS_HEAD) ws[tid] = 0;  // item and finished counters
-    for (int l = tid; l < E_loc; l += 256) {
-        cnt[l] = 0;
-        running[l] = 0;
-    }
-    if (in_lds) {
-        for (int b = tid; b < nb; b += 256) {
-            const int4 v = reinterpret_cast<const int4*>(blocks)[b];
-            s_l[b] = v.y;
-            s_first[b] = v.z;
-            s_rows[b] = v.w;
-        }
-    }
-    __syncthreads();
-    auto blk_l = [&](int b) { return in_lds ? s_l[b] : blocks[4 * b + 1]; };
-    auto blk_first = [&](int b) { return in_lds ? s_first[b] : blocks[4 * b + 2]; };
-    auto blk_rows = [&](int b) { return in_lds ? s_rows[b] : blocks[4 * b + 3]; };
-    auto sorted_at = [&](int i) { return in_lds ? s_sorted[i] : sorted_g[i]; };
+    auto blk_l = [&](int b) {
+        if constexpr (kLds) return sh.s_l[b]; else return blocks[4 * b + 1];
+    };
+    auto blk_first = [&](int b) {
+        if constexpr (kLds) return sh.s_first[b]; else return blocks[4 * b + 2];
+    };
+    auto blk_rows = [&](int b) {
+        if constexpr (kLds) return sh.s_rows[b]; else return blocks[4 * b + 3];
+    };
+    auto sorted_at = [&](int i) {
+        if constexpr (kLds) return sh.s_sorted[i]; else return sorted_g[i];
+    };
 
-    for (int b = tid; b < nb; b += 256) atomicAdd(&cnt[blk_l(b)], 1);
+    for (int b = tid; b < nb; b += 256) atomicAdd(&sh.cnt[blk_l(b)], 1);
     __syncthreads();
-    if (tid == 0) {
-        int acc = 0;
-        for (int l = 0; l < E_loc; ++l) {
-            bstart[l] = acc;
-            acc += cnt[l];
-        }
-        bstart[E_loc] = acc;
+    {
+        int total;
+        const int ex = block_exclusive_scan(tid < E_loc ? sh.cnt[tid] : 0, sh.scan_part, &total);
+        if (tid < E_loc) sh.bstart[tid] = ex;
+        if (tid == 0) sh.bstart[E_loc] = total;
     }
     __syncthreads();
     // stable counting sort of the blocks by expert, 256 blocks per round
     for (int b0 = 0; b0 < nb; b0 += 256) {
-        for (int i = tid; i < 4 * 256; i += 256) mask[i / 256][i % 256] = 0ull;
+        for (int i = tid; i < 4 * 256; i += 256) sh.mask[i / 256][i % 256] = 0ull;
         __syncthreads();
         const int b = b0 + tid;
         const int l = b < nb ? blk_l(b) : -1;
-        if (l >= 0) atomicOr(&mask[wave][l], 1ull << lane);
+        if (l >= 0) atomicOr(&sh.mask[wave][l], 1ull << lane);
         __syncthreads();
         if (l >= 0) {
-            int pos = running[l] + __popcll(mask[wave][l] & ((1ull << lane) - 1ull));
-            for (int w = 0; w < wave; ++w) pos += __popcll(mask[w][l]);
-            if (in_lds)
-                s_sorted[bstart[l] + pos] = b;
+            int pos = sh.running[l] + __popcll(sh.mask[wave][l] & ((1ull << lane) - 1ull));
+            for (int w = 0; w < wave; ++w) pos += __popcll(sh.mask[w][l]);
+            if constexpr (kLds)
+                sh.s_sorted[sh.bstart[l] + pos] = b;
             else
-                sorted_g[bstart[l] + pos] = b;
+                sorted_g[sh.bstart[l] + pos] = b;
         }
         __syncthreads();
         for (int e = tid; e < E_loc; e += 256)
-            running[e] += __popcll(mask[0][e]) + __popcll(mask[1][e]) + __popcll(mask[2][e]) +
-                          __popcll(mask[3][e]);
+            sh.running[e] += __popcll(sh.mask[0][e]) + __popcll(sh.mask[1][e]) +
+                             __popcll(sh.mask[2][e]) + __popcll(sh.mask[3][e]);
         __syncthreads();
     }
+    if constexpr (!kLds) __threadfence_block();  // sorted_g written above, read below
     // pieces per expert: walk its blocks, joining row-contiguous ones into runs
     for (int l = tid; l < E_loc; l += 256) {
         int pieces = 0, run_first = 0, run_rows = 0;
-        for (int i = bstart[l]; i < bstart[l + 1]; ++i) {
+        for (int i = sh.bstart[l]; i < sh.bstart[l + 1]; ++i) {
             const int b = sorted_at(i);
             const int first = blk_first(b), rows = blk_rows(b);
             if (run_rows > 0 && first == run_first + run_rows) {
@@ -269,25 +293,27 @@ ffn_schedule_kernel(const int32_t* __restrict__ blocks, const int32_t* __restric
             }
         }
         pieces += (run_rows + HALF - 1) / HALF;
-        npieces[l] = pieces;
+        sh.npieces[l] = pieces;
     }
     __syncthreads();
-    if (tid == 0) {
-        int acc = 0;
-        for (int l = 0; l < E_loc; ++l) {
-            tstart[l] = acc;
-            acc += (npieces[l] + 1) / 2;
+    {
+        int total;
+        const int ex = block_exclusive_scan(tid < E_loc ? (sh.npieces[tid] + 1) / 2 : 0,
+                                            sh.scan_part, &total);
+        if (tid < E_loc) sh.tstart[tid] = ex;
+        if (tid == 0) {
+            sh.tstart[E_loc] = total;
+            ws[WS_NTILES] = total;
         }
-        tstart[E_loc] = acc;
-        ws[WS_NTILES] = acc;
     }
     __syncthreads();
     // emit the tiles: pieces of an expert in order, two per tile
     for (int l = tid; l < E_loc; l += 256) {
+        const int t0 = sh.tstart[l], tcount = sh.tstart[l + 1] - t0;
         int piece = 0, run_first = 0, run_rows = 0;
         auto emit_run = [&]() {
             for (int off = 0; off < run_rows; off += HALF, ++piece) {
-                int32_t* t = tiles + TILE_INTS * (tstart[l] + piece / 2);
+                int32_t* t = tiles + TILE_INTS * (t0 + piece / 2);
                 const int rows = run_rows - off < HALF ? run_rows - off : HALF;
                 if ((piece & 1) == 0) {
                     t[0] = l;
@@ -295,15 +321,15 @@ ffn_schedule_kernel(const int32_t* __restrict__ blocks, const int32_t* __restric
                     t[2] = rows;
                     t[3] = 0;
                     t[4] = 0;
-                    t[5] = tstart[l];
-                    t[6] = tstart[l + 1] - tstart[l];
+                    t[5] = t0;
+                    t[6] = tcount;
                 } else {
                     t[3] = run_first + off;
                     t[4] = rows;
                 }
             }
         };
-        for (int i = bstart[l]; i < bstart[l + 1]; ++i) {
+        for (int i = sh.bstart[l]; i < sh.bstart[l + 1]; ++i) {
             const int b = sorted_at(i);
             const int first = blk_first(b), rows = blk_rows(b);
             if (run_rows > 0 && first == run_first + run_rows) {
@@ -315,6 +341,87 @@ ffn_schedule_kernel(const int32_t* __restrict__ blocks, const int32_t* __restric
             }
         }
         emit_run();
+    }
+}
+
+// Common case: every expert's blocks cover one contiguous row range (a moe_plan table: an
+// expert's shares are consecutive ranges of its segment).  Then its pieces are 128-row cuts
+// of that range and each tile follows from the expert's first row and row count alone.
+__device__ __forceinline__ bool schedule_contiguous(const int32_t* __restrict__ blocks, int nb,
+                                                    int max_blocks, int E_loc,
+                                                    int32_t* __restrict__ ws, SchedShared& sh) {
+    const int tid = threadIdx.x;
+    for (int b = tid; b < nb; b += 256) {
+        const int4 v = reinterpret_cast<const int4*>(blocks)[b];
+        atomicAdd(&sh.sum_rows[v.y], v.w);
+        atomicMin(&sh.min_first[v.y], v.z);
+        atomicMax(&sh.max_end[v.y], v.z + v.w);
+    }
+    __syncthreads();
+    // blocks never overlap, so the union is one range exactly when its span equals the sum
+    const bool ok = tid >= E_loc || sh.sum_rows[tid] == 0 ||
+                    sh.sum_rows[tid] == sh.max_end[tid] - sh.min_first[tid];
+    if (!__syncthreads_and(ok)) return false;
+    int total;
+    const int pieces = tid < E_loc ? (sh.sum_rows[tid] + HALF - 1) / HALF : 0;
+    const int ex = block_exclusive_scan((pieces + 1) / 2, sh.scan_part, &total);
+    if (tid < E_loc) sh.tstart[tid] = ex;
+    if (tid == 0) {
+        sh.tstart[E_loc] = total;
+        ws[WS_NTILES] = total;
+    }
+    __syncthreads();
+    int32_t* tiles = ws + WS_HEAD + max_blocks;
+    for (int t = tid; t < total; t += 256) {
+        int lo = 0, hi = E_loc - 1;  // the expert l with tstart[l] <= t < tstart[l + 1]
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (sh.tstart[mid] <= t) lo = mid; else hi = mid - 1;
+        }
+        const int l = lo, j = t - sh.tstart[l];
+        const int n = sh.sum_rows[l], first = sh.min_first[l] + j * 2 * HALF;
+        const int left = n - j * 2 * HALF;  // rows of the expert from this tile on
+        int32_t* o = tiles + TILE_INTS * t;
+        o[0] = l;
+        o[1] = first;
+        o[2] = left < HALF ? left : HALF;
+        o[3] = left > HALF ? first + HALF : 0;
+        o[4] = left > HALF ? (left - HALF < HALF ? left - HALF : HALF) : 0;
+        o[5] = sh.tstart[l];
+        o[6] = sh.tstart[l + 1] - sh.tstart[l];
+    }
+    return true;
+}
+
+__global__ void __launch_bounds__(256)
+ffn_schedule_kernel(const int32_t* __restrict__ blocks, const int32_t* __restrict__ n_blocks_ptr,
+                    int max_blocks, int E_loc, int32_t* __restrict__ ws) {
+    __shared__ SchedShared sh;
+    const int tid = threadIdx.x;
+    int nb = *n_blocks_ptr;
+    nb = nb < max_blocks ? nb : max_blocks;
+    if (tid >= WS_CTR_FC1 && tid < WS_HEAD) ws[tid] = 0;  // item and finished counters
+    for (int l = tid; l < E_loc; l += 256) {
+        sh.cnt[l] = 0;
+        sh.running[l] = 0;
+        sh.sum_rows[l] = 0;
+        sh.min_first[l] = 0x7FFFFFFF;
+        sh.max_end[l] = 0;
+    }
+    __syncthreads();
+    if (schedule_contiguous(blocks, nb, max_blocks, E_loc, ws, sh)) return;
+    if (nb <= kSchedLds) {
+        for (int b = tid; b < nb; b += 256) {
+            const int4 v = reinterpret_cast<const int4*>(blocks)[b];
+            sh.s_l[b] = v.y;
+            sh.s_first[b] = v.z;
+            sh.s_rows[b] = v.w;
+        }
+        __syncthreads();
+        schedule_body<true>(blocks, nb, max_blocks, E_loc, ws, sh);
+    } else {
+        __syncthreads();
+        schedule_body<false>(blocks, nb, max_blocks, E_loc, ws, sh);
     }
 }
 

@@ -65,7 +65,7 @@ plan_kernel(const int32_t* __restrict__ counts, int begin, int stride, int E_loc
     __shared__ int off_s[257];
     __shared__ int q_s[kMaxSlices];      // [l * P + r]
     __shared__ int start_s[kMaxSlices];  // first row of slice (l, r), then its first block
-    __shared__ int part[kThreads];
+    __shared__ int part[kThreads / MOE_WAVE];
     __shared__ int err_s;
 
     const int tid = threadIdx.x;
@@ -201,16 +201,23 @@ plan_kernel(const int32_t* __restrict__ counts, int begin, int stride, int E_loc
         int r = s / E_loc, l = s - r * E_loc;
         cnt += (q_s[l * P + r] + beta - 1) / beta;
     }
-    part[tid] = cnt;
-    __syncthreads();
-    for (int dd = 1; dd < kThreads; dd <<= 1) {
-        int add = tid >= dd ? part[tid - dd] : 0;
-        __syncthreads();
-        part[tid] += add;
-        __syncthreads();
+    // exclusive scan of the per-thread block counts: within each wave by shuffles, across
+    // the four waves through LDS
+    int incl = cnt;
+#pragma unroll
+    for (int dd = 1; dd < MOE_WAVE; dd <<= 1) {
+        const int o = __shfl_up(incl, dd, MOE_WAVE);
+        if (lane >= dd) incl += o;
     }
-    int b = part[tid] - cnt;
-    const int total = part[kThreads - 1];
+    const int wave = tid / MOE_WAVE;
+    if (lane == MOE_WAVE - 1) part[wave] = incl;
+    __syncthreads();
+    int b = incl - cnt, total = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / MOE_WAVE; ++w) {
+        b += w < wave ? part[w] : 0;
+        total += part[w];
+    }
     for (int s = s_begin; s < s_end; ++s) {
         int r = s / E_loc, l = s - r * E_loc;
         int take = q_s[l * P + r];

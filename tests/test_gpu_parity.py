@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import oracle
-from mixture_experts_routed_router_amd import inputs
+from mixture_experts_routed_router_amd import binding, inputs
 from parity_helpers import (check_index_parity, check_xp, host, oracle_index, random_case,
                             rel_frob, row_experts, run_gpu, sample_rows, to_f64, workload_case)
 
@@ -154,6 +154,47 @@ def test_graph_replay_matches_eager():
         assert torch.equal(layer.blocks[:nb], ref_blocks), (skew, "blocks")
         assert torch.equal(layer.yp[valid], ref_yp), (skew, "yp")
     del graph
+
+
+@pytest.mark.parametrize("name,kw,drop", [
+    # every other block: each expert's blocks no longer cover one row range (table in LDS)
+    ("every_other", dict(seed=1, T=600, H=128, E=12, K=3, I=192, P=4, block_m=32), 2),
+    # a quarter of 4130 blocks dropped: 3098 blocks, walked in global memory
+    ("many_blocks", dict(seed=15, T=8192, H=64, E=64, K=8, I=64, P=8, block_m=16), 4),
+])
+def test_ffn_arbitrary_block_table(name, kw, drop):
+    """moe_expert_ffn on a block table that is not a moe_plan table (some blocks left out):
+    covered rows against the oracle, the other rows untouched."""
+    _announce(f"ffn on a partial block table: {name}")
+    c = random_case(**kw)
+    layer = run_gpu(c)
+    ref = oracle_index(c)
+    nb = int(layer.n_blocks.item())
+    full = host(layer.blocks[:nb])
+    keep = np.array([i % drop != drop - 1 for i in range(nb)])
+    sub = np.ascontiguousarray(full[keep])
+    dev = layer.blocks.device
+    sub_buf = torch.zeros_like(layer.blocks)
+    sub_buf[: len(sub)] = torch.from_numpy(sub).to(dev)
+    n_sub = torch.tensor([len(sub)], dtype=torch.int32, device=dev)
+    act = torch.zeros_like(layer.act)
+    yp = torch.zeros_like(layer.yp)
+    _, _, W1, W2 = layer._inputs
+    binding.moe_expert_ffn(layer.xp, W1, W2, sub_buf, n_sub, act, yp, layer.ffn_workspace)
+    torch.cuda.synchronize()
+    x = inputs.as_oracle_array(c.x)
+    _, _, _, xp = oracle.permute(ref.ids, ref.counts, c.E, c.begin, c.stride, c.n_local,
+                                 c.block_m, x)
+    act_o, yp_o = oracle.ffn_blocks(xp, inputs.as_oracle_array(c.W1),
+                                    inputs.as_oracle_array(c.W2), sub)
+    covered = np.zeros(xp.shape[0], bool)
+    for _, _, first, rows in sub:
+        covered[first:first + rows] = True
+    g_act, g_yp = host(act)[: len(covered)], host(yp)[: len(covered)]
+    e_act = rel_frob(to_f64(g_act[covered]), to_f64(act_o[covered]))
+    e_yp = rel_frob(to_f64(g_yp[covered]), to_f64(yp_o[covered]))
+    assert e_act <= c.tol and e_yp <= c.tol, (e_act, e_yp)
+    assert not to_f64(g_act[~covered]).any() and not to_f64(g_yp[~covered]).any(), "untouched"
 
 
 # ------------------------------------------------- gather-on-load expert FFN ---
