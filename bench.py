@@ -177,13 +177,19 @@ def cpu_baseline(w, skew, T_s, target_s=12.0):
         return time.perf_counter() - t0
 
     t_probe = run(T_s)
-    n = int(T_s * target_s / max(t_probe, 1e-6))
-    n = max(w.P, min(w.T, n) // w.P * w.P)
-    dt = run(n) if n != T_s else t_probe
-    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
+    want = int(T_s * target_s / max(t_probe, 1e-6))
+    n = max(w.P, min(w.T, want) // w.P * w.P)
+    # a whole batch that takes less than the target is run again until the target is reached
+    reps, dt = 0, 0.0
+    while reps == 0 or (n == w.T and dt < target_s):
+        dt += run(n)
+        reps += 1
+    what = (f"first {n} of {w.T} tokens of the same batch" if reps == 1 else
+            f"the whole batch of {w.T} tokens, {reps} times")
+    return {"value": round(n * reps / dt, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"first {n} of {w.T} tokens of the same batch, whole path (route, permute, "
-                      f"plan, FFN, combine), float64 plain C with OpenMP, {dt:.1f} s"}
+            "sample": f"{what}, whole path (route, permute, plan, FFN, combine), float64 plain C "
+                      f"with OpenMP, {dt:.1f} s"}
 
 
 def main():

@@ -688,49 +688,76 @@ ffn_bf16_kernel(const uint16_t* __restrict__ A, int64_t a_rows, int Kdim,
     }
 }
 
-// float32 path (small layers): one thread per output element, sequential K loop.
+// float32 path (small layers): C[p][c] = A[p] . B[l][c] over the block table (FC1: SiLU of
+// the gate product times the up product, B rows c and I + c).  One workgroup per (block, 64
+// output columns), grid-stride over those items; K is staged 64 at a time through LDS: the
+// block's A rows (64 rows per pass, gathered through `gather` when given) and the 64
+// columns' B rows.  Thread (rg, c) accumulates rows rg, rg+4, ..., rg+60 of column c with
+// fmaf in ascending K order.  Rows of 65 floats keep the B reads conflict-free (lane c reads
+// row c); A reads are wave-uniform broadcasts.
+template <bool kSwiGLU>
 __global__ void __launch_bounds__(256)
-ffn_f32_gateup_kernel(const float* __restrict__ xp, const float* __restrict__ w1, int H, int I,
-                      const int32_t* __restrict__ blocks, const int32_t* __restrict__ n_blocks_ptr,
-                      int max_blocks, float* __restrict__ act,
-                      const int32_t* __restrict__ gather) {
+ffn_f32_kernel(const float* __restrict__ A, const int32_t* __restrict__ gather, int Kdim,
+               const float* __restrict__ B, int64_t b_expert_stride, int I,
+               float* __restrict__ C, int ldc, int n_cols, const int32_t* __restrict__ blocks,
+               const int32_t* __restrict__ n_blocks_ptr, int max_blocks) {
+    constexpr int TC = 64, TK = 64, TR = 64, RPT = TR / 4;
+    __shared__ float a_s[TR][TK + 1];
+    __shared__ float g_s[TC][TK + 1];
+    __shared__ float u_s[kSwiGLU ? TC : 1][TK + 1];
     int nb = *n_blocks_ptr;
     nb = nb < max_blocks ? nb : max_blocks;
-    for (int b = blockIdx.x; b < nb; b += gridDim.x) {
+    const int nct = (n_cols + TC - 1) / TC;
+    const int tid = threadIdx.x, c = tid & (TC - 1), rg = tid / TC;
+    for (int item = blockIdx.x; item < nb * nct; item += gridDim.x) {
+        const int b = item / nct, ct = item - b * nct;
         const int l = blocks[4 * b + 1], row0 = blocks[4 * b + 2], m = blocks[4 * b + 3];
-        const float* wg = w1 + (int64_t)l * 2 * I * H;
-        for (int idx = threadIdx.x; idx < m * I; idx += blockDim.x) {
-            const int r = idx / I, i = idx - r * I;
-            const int64_t arow = gather ? gather[row0 + r] : row0 + r;
-            const float* x = xp + arow * H;
-            const float* g_row = wg + (int64_t)i * H;
-            const float* u_row = wg + (int64_t)(I + i) * H;
-            float g = 0.f, u = 0.f;
-            for (int h = 0; h < H; ++h) {
-                g = fmaf(x[h], g_row[h], g);
-                u = fmaf(x[h], u_row[h], u);
+        const float* Bl = B + (int64_t)l * b_expert_stride;
+        const int col = ct * TC + c;
+        for (int r0 = 0; r0 < m; r0 += TR) {
+            float ag[RPT], au[RPT];
+#pragma unroll
+            for (int j = 0; j < RPT; ++j) ag[j] = au[j] = 0.f;
+            for (int k0 = 0; k0 < Kdim; k0 += TK) {
+                __syncthreads();  // the previous slice's LDS reads are done
+                for (int e = tid; e < TR * TK; e += 256) {
+                    const int rr = e / TK, kk = e - rr * TK, r = r0 + rr;
+                    float v = 0.f;
+                    if (r < m && k0 + kk < Kdim) {
+                        const int64_t arow = gather ? gather[row0 + r] : row0 + r;
+                        v = A[arow * Kdim + k0 + kk];
+                    }
+                    a_s[rr][kk] = v;
+                }
+                for (int e = tid; e < TC * TK; e += 256) {
+                    const int cc = e / TK, kk = e - cc * TK, cl = ct * TC + cc;
+                    const bool in = cl < n_cols && k0 + kk < Kdim;
+                    g_s[cc][kk] = in ? Bl[(int64_t)cl * Kdim + k0 + kk] : 0.f;
+                    if (kSwiGLU) u_s[cc][kk] = in ? Bl[(int64_t)(I + cl) * Kdim + k0 + kk] : 0.f;
+                }
+                __syncthreads();
+                const int kn = Kdim - k0 < TK ? Kdim - k0 : TK;
+                for (int kk = 0; kk < kn; ++kk) {
+                    const float wg = g_s[c][kk];
+                    const float wu = kSwiGLU ? u_s[c][kk] : 0.f;
+#pragma unroll
+                    for (int j = 0; j < RPT; ++j) {
+                        const float av = a_s[rg + 4 * j][kk];
+                        ag[j] = fmaf(av, wg, ag[j]);
+                        if (kSwiGLU) au[j] = fmaf(av, wu, au[j]);
+                    }
+                }
             }
-            act[(int64_t)(row0 + r) * I + i] = g / (1.f + expf(-g)) * u;
-        }
-    }
-}
-
-__global__ void __launch_bounds__(256)
-ffn_f32_down_kernel(const float* __restrict__ act, const float* __restrict__ w2, int H, int I,
-                    const int32_t* __restrict__ blocks, const int32_t* __restrict__ n_blocks_ptr,
-                    int max_blocks, float* __restrict__ yp) {
-    int nb = *n_blocks_ptr;
-    nb = nb < max_blocks ? nb : max_blocks;
-    for (int b = blockIdx.x; b < nb; b += gridDim.x) {
-        const int l = blocks[4 * b + 1], row0 = blocks[4 * b + 2], m = blocks[4 * b + 3];
-        const float* w = w2 + (int64_t)l * H * I;
-        for (int idx = threadIdx.x; idx < m * H; idx += blockDim.x) {
-            const int r = idx / H, h = idx - r * H;
-            const float* a = act + (int64_t)(row0 + r) * I;
-            const float* w_row = w + (int64_t)h * I;
-            float y = 0.f;
-            for (int i = 0; i < I; ++i) y = fmaf(a[i], w_row[i], y);
-            yp[(int64_t)(row0 + r) * H + h] = y;
+            if (col < n_cols) {
+#pragma unroll
+                for (int j = 0; j < RPT; ++j) {
+                    const int r = r0 + rg + 4 * j;
+                    if (r < m) {
+                        const float g = ag[j];
+                        C[(int64_t)(row0 + r) * ldc + col] = kSwiGLU ? g / (1.f + expf(-g)) * au[j] : g;
+                    }
+                }
+            }
         }
     }
 }
@@ -762,10 +789,11 @@ hipError_t moe_launch_ffn_fc1(const void* a, const void* w1, moe_dtype_t dt, int
                               int32_t* ws, void* act, int64_t a_rows, const int32_t* gather,
                               hipStream_t stream) {
     if (dt == MOE_F32) {
-        int grid = max_blocks < 1024 ? max_blocks : 1024;
-        ffn_f32_gateup_kernel<<<grid, 256, 0, stream>>>(
-            static_cast<const float*>(a), static_cast<const float*>(w1), H, I, blocks, n_blocks,
-            max_blocks, static_cast<float*>(act), gather);
+        const int64_t items = (int64_t)max_blocks * ((I + 63) / 64);
+        const int grid = items < 2048 ? (int)items : 2048;
+        ffn_f32_kernel<true><<<grid, 256, 0, stream>>>(
+            static_cast<const float*>(a), gather, H, static_cast<const float*>(w1),
+            (int64_t)2 * I * H, I, static_cast<float*>(act), I, I, blocks, n_blocks, max_blocks);
         return hipGetLastError();
     }
     ffn_bf16_kernel<true><<<persistent_grid(), kThreads, 0, stream>>>(
@@ -780,10 +808,11 @@ hipError_t moe_launch_ffn_fc2(const void* act, const void* w2, moe_dtype_t dt, i
                               int32_t* ws, void* yp, int64_t max_rows,
                               hipStream_t stream) {
     if (dt == MOE_F32) {
-        int grid = max_blocks < 1024 ? max_blocks : 1024;
-        ffn_f32_down_kernel<<<grid, 256, 0, stream>>>(
-            static_cast<const float*>(act), static_cast<const float*>(w2), H, I, blocks,
-            n_blocks, max_blocks, static_cast<float*>(yp));
+        const int64_t items = (int64_t)max_blocks * ((H + 63) / 64);
+        const int grid = items < 2048 ? (int)items : 2048;
+        ffn_f32_kernel<false><<<grid, 256, 0, stream>>>(
+            static_cast<const float*>(act), nullptr, I, static_cast<const float*>(w2),
+            (int64_t)H * I, I, static_cast<float*>(yp), H, H, blocks, n_blocks, max_blocks);
         return hipGetLastError();
     }
     ffn_bf16_kernel<false><<<persistent_grid(), kThreads, 0, stream>>>(
