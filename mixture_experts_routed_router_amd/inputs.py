@@ -14,6 +14,7 @@ Seeds: numpy PCG64 streams from SeedSequence([seed_id, stream, slot, ...]):
   logits  -> [seed_id, 0, logit_slot]
   x       -> [seed_id, 1, x_slot]
   W1[l]   -> [seed_id, 2, l],   W2[l] -> [seed_id, 3, l]   (l = local expert index)
+  W_r     -> [seed_id, 4, 0]   (linear router rows, all E experts)
 """
 from __future__ import annotations
 
@@ -133,6 +134,14 @@ def make_weights(w: Workload, experts=None, threads: int = 8):
     with ThreadPoolExecutor(max(1, threads)) as ex:
         list(ex.map(fill, range(len(experts))))
     return W1, W2
+
+
+def make_router_weights(w: Workload) -> torch.Tensor:
+    """Linear router rows W_r [E, H] on the CPU: N(0, 0.02^2), rounded to bf16 for bf16
+    workloads (router scores x . W_r^T then have a spread of about 0.02 sqrt(H))."""
+    a = _rng(w.seed_id, 4, 0).standard_normal((w.E, w.H), dtype=np.float32)
+    a *= np.float32(WEIGHT_STD)
+    return _to_dtype(a, w.dtype)
 
 
 def as_oracle_array(t: torch.Tensor) -> np.ndarray:

@@ -138,6 +138,84 @@ int oracle_route(const float* logits, int T, int E, int K, int renormalize,
     return ORACLE_OK;
 }
 
+/* Top-k with a reference set.  [RN]: the top k_1 experts are activated while their weights
+ * are normalised by the probability mass of the top k_2 experts; k_2 = k_1 is the usual
+ * renormalisation over the picks and dropping renormalisation is the plain softmax over all
+ * experts.  Here K = k_1 and k_ref = k_2, K <= k_ref <= E.
+ *
+ * ids and counts exactly as oracle_route.  With m the largest logit of the token,
+ * w[t][k] = exp(l[ids[t][k]] - m) / sum over the first k_ref experts of the token's ranking of
+ * exp(l - m).  For k_ref = E that set is every expert, summed in expert order.
+ * Pinned by: an argsort-based float64 computation of the same ratio (every k_ref); equality
+ * with oracle_route at k_ref = K and k_ref = E. */
+int oracle_route_ref(const float* logits, int T, int E, int K, int k_ref, int32_t* ids,
+                     float* w, int32_t* counts) {
+    if (T < 1 || E < 1 || K < 1 || K > E || k_ref < K || k_ref > E) return ORACLE_ERR_ARG;
+    const int picks = k_ref < E ? k_ref : K;
+    int bad = 0;
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        const float* row = logits + (int64_t)t * E;
+        unsigned char* taken = (unsigned char*)calloc((size_t)E, 1);
+        int* order = (int*)malloc(sizeof(int) * (size_t)picks);
+        if (!taken || !order) {
+            bad = 1;
+            free(taken);
+            free(order);
+            continue;
+        }
+        /* selection passes under (larger logit, smaller id), as in oracle_route */
+        for (int k = 0; k < picks; ++k) {
+            int best = -1;
+            for (int e = 0; e < E; ++e) {
+                if (taken[e]) continue;
+                if (best < 0 || row[e] > row[best]) best = e;
+            }
+            taken[best] = 1;
+            order[k] = best;
+        }
+        for (int k = 0; k < K; ++k) ids[(int64_t)t * K + k] = order[k];
+        double m = (double)row[order[0]];
+        double denom = 0.0;
+        if (k_ref < E) {
+            for (int k = 0; k < k_ref; ++k) denom += exp((double)row[order[k]] - m);
+        } else {
+            for (int e = 0; e < E; ++e) denom += exp((double)row[e] - m);
+        }
+        for (int k = 0; k < K; ++k)
+            w[(int64_t)t * K + k] = (float)(exp((double)row[order[k]] - m) / denom);
+        free(taken);
+        free(order);
+    }
+    if (bad) return ORACLE_ERR_DATA;
+    for (int e = 0; e < E; ++e) counts[e] = 0;
+    for (int64_t i = 0; i < (int64_t)T * K; ++i) counts[ids[i]] += 1;
+    return ORACLE_OK;
+}
+
+/* Router scores.  [TM] (the TritonMoE abstract): the forward pass starts with router scoring;
+ * a linear router scores token t against expert e with the dot product of the token's
+ * activation row and the expert's router row:
+ *   logits[t][e] = sum over h of x[t][h] * w_r[e][h],
+ * x [T, H] and w_r [E, H] of dtype dt (0 = float32, 1 = bf16), accumulated in double in
+ * ascending h and rounded once to float32.
+ * Pinned by: one-hot router rows reproduce columns of x exactly; scaling x by 2 scales the
+ * logits by 2 exactly; a float64 library matrix product rounded to float32. */
+int oracle_router_logits(const void* x, int dt, const void* w_r, int T, int H, int E,
+                         float* logits) {
+    if (T < 1 || H < 1 || E < 1 || (dt != 0 && dt != 1)) return ORACLE_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        for (int e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int h = 0; h < H; ++h)
+                acc += load_elem(x, (int64_t)t * H + h, dt) * load_elem(w_r, (int64_t)e * H + h, dt);
+            logits[(int64_t)t * E + e] = (float)acc;
+        }
+    }
+    return ORACLE_OK;
+}
+
 /* ---------------------------------------------------------------------- permute --- */
 
 /* Local index of global expert e in the set { begin + j*stride : 0 <= j < E_loc }, or -1. */

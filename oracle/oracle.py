@@ -5,7 +5,9 @@ CPU-baseline leg of ``bench.py``; never by the product package.  It shares no co
 HIP library.  Arrays are numpy; bf16 data travels as ``np.uint16`` bit patterns.
 
 Every function is the plain definition of its step (see the citations in ``oracle.c``):
-route  -- top-k by (larger logit, smaller id), softmax weights renormalised over the picks;
+route  -- top-k by (larger logit, smaller id), softmax weights renormalised over the picks
+          (route_ref: normalised by the mass of the top k_ref experts);
+router_logits -- linear router scores x . w_r^T in double, rounded to float32;
 permute -- stable expert-major order by flat index, beta-aligned segments;
 plan   -- the greedy donor->receiver balance to exact per-rank capacity, then <=beta blocks;
 ffn    -- SwiGLU expert FFN in double with bf16 rounding at act and yp;
@@ -46,8 +48,8 @@ def _load():
         lib.oracle_double_to_bf16.restype = ctypes.c_uint16
         lib.oracle_double_to_bf16.argtypes = [ctypes.c_double]
         lib.oracle_num_threads.restype = ctypes.c_int
-        for name in ("oracle_route", "oracle_permute", "oracle_plan", "oracle_ffn_rows",
-                     "oracle_ffn_blocks", "oracle_combine"):
+        for name in ("oracle_route", "oracle_route_ref", "oracle_router_logits", "oracle_permute",
+                     "oracle_plan", "oracle_ffn_rows", "oracle_ffn_blocks", "oracle_combine"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -89,6 +91,33 @@ def route(logits: np.ndarray, K: int, renormalize: bool = True):
     _check(_load().oracle_route(_p(logits), T, E, K, int(bool(renormalize)), _p(ids), _p(w),
                                 _p(counts)), "route")
     return ids, w, counts
+
+
+def route_ref(logits: np.ndarray, K: int, k_ref: int):
+    """Top-K ids with weights normalised by the mass of the top k_ref experts (K <= k_ref <=
+    E).  -> ids [T,K] int32, w [T,K] float32, counts [E] int32."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    ids = np.empty((T, K), np.int32)
+    w = np.empty((T, K), np.float32)
+    counts = np.empty((E,), np.int32)
+    _check(_load().oracle_route_ref(_p(logits), T, E, K, k_ref, _p(ids), _p(w), _p(counts)),
+           "route_ref")
+    return ids, w, counts
+
+
+def router_logits(x: np.ndarray, w_r: np.ndarray) -> np.ndarray:
+    """Linear router scores x . w_r^T -> [T, E] float32 (x, w_r: float32, or bf16 bits as
+    uint16)."""
+    x = np.ascontiguousarray(x)
+    w_r = np.ascontiguousarray(w_r)
+    dt = _dt_code(x)
+    assert _dt_code(w_r) == dt and x.shape[1] == w_r.shape[1]
+    T, H = x.shape
+    E = w_r.shape[0]
+    logits = np.empty((T, E), np.float32)
+    _check(_load().oracle_router_logits(_p(x), dt, _p(w_r), T, H, E, _p(logits)), "router_logits")
+    return logits
 
 
 def max_rows(T: int, K: int, E_loc: int, beta: int) -> int:

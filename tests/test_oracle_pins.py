@@ -83,6 +83,59 @@ def test_route_ties_and_k1(oracle_mod):
     assert sorted(idsE[1].tolist()) == list(range(6))
 
 
+@pytest.mark.parametrize("name", ["tiny_f32", "olmoe_shaped", "gpt_oss_120b_decode"])
+def test_route_ref_matches_sorted_mass(oracle_mod, name):
+    """Weights normalised by the mass of the top k_ref experts, for every k_ref from K to E,
+    against an argsort-based float64 computation of the same ratio; the two ends are the
+    renormalised and the plain softmax."""
+    w = inputs.WORKLOADS[name]
+    L = inputs.make_logits(w, w.skews[-1])[:256]
+    order = np.argsort(-L, axis=1, kind="stable")
+    Ld = L.astype(np.float64)
+    p = np.exp(Ld - Ld.max(1, keepdims=True))
+    ps = np.take_along_axis(p, order, 1)
+    for k_ref in sorted({w.K, w.K + 1, 2 * w.K, min(w.E, 16), w.E}):
+        if k_ref > w.E:
+            continue
+        ids, wt, counts = oracle_mod.route_ref(L, w.K, k_ref)
+        assert np.array_equal(ids, order[:, : w.K])
+        ref = ps[:, : w.K] / ps[:, :k_ref].sum(1, keepdims=True)
+        assert np.max(np.abs(wt - ref)) <= 1e-7, k_ref
+        assert np.array_equal(counts, np.bincount(ids.ravel(), minlength=w.E))
+    # the two ends are exactly the two modes of oracle_route
+    for k_ref, renorm in ((w.K, True), (w.E, False)):
+        a = oracle_mod.route_ref(L, w.K, k_ref)
+        b = oracle_mod.route(L, w.K, renormalize=renorm)
+        assert all(np.array_equal(x, y) for x, y in zip(a, b))
+    # a larger reference set never raises a weight
+    w1 = oracle_mod.route_ref(L, w.K, w.K)[1]
+    w2 = oracle_mod.route_ref(L, w.K, min(w.E, 2 * w.K))[1]
+    assert np.all(w2 <= w1)
+
+
+def test_router_logits_pins(oracle_mod):
+    """Linear router scores: one-hot router rows pick columns of x exactly; scaling x by 2
+    scales every score by 2 exactly; against a float64 library product rounded once."""
+    rng = np.random.default_rng(5)
+    T, H, E = 40, 96, 12
+    for dt in ("f32", "bf16"):
+        x = torch.from_numpy(rng.standard_normal((T, H), dtype=np.float32))
+        wr = torch.from_numpy(rng.standard_normal((E, H), dtype=np.float32) * 0.05)
+        if dt == "bf16":
+            x, wr = x.to(torch.bfloat16), wr.to(torch.bfloat16)
+        xo, wo = inputs.as_oracle_array(x), inputs.as_oracle_array(wr)
+        L = oracle_mod.router_logits(xo, wo)
+        ref = (x.double() @ wr.double().T).float().numpy()
+        assert np.max(np.abs(L - ref) / (np.abs(ref) + 1e-30)) <= 2 ** -23, dt
+        L2 = oracle_mod.router_logits(inputs.as_oracle_array(x * 2), wo)
+        assert np.array_equal(L2, 2 * L), dt
+        perm = rng.permutation(H)[:E]
+        onehot = torch.zeros((E, H), dtype=x.dtype)
+        onehot[np.arange(E), perm] = 1
+        Lo = oracle_mod.router_logits(xo, inputs.as_oracle_array(onehot))
+        assert np.array_equal(Lo, x.float().numpy()[:, perm]), dt
+
+
 def test_hot4_share(oracle_mod):
     w = inputs.WORKLOADS["qwen3_30b_a3b_shaped"]
     _, _, counts = oracle_mod.route(inputs.make_logits(w, "hot4"), w.K)
