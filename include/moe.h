@@ -3,7 +3,9 @@
  * (gfx950).  Library: libmoe.so (mixture_experts_routed_router_amd/libmoe.so).
  *
  * The path, in call order (one layer, one GPU, one stream):
- *   moe_route       router top-k over precomputed logits, routing weights, expert counts
+ *   moe_route       router top-k over precomputed logits, routing weights, expert counts;
+ *                   moe_route_ref with a top-k_ref reference mass; moe_router_topk computes
+ *                   the logits (linear router, bf16 MFMA) and fuses the top-k behind them
  *   moe_permute     dispatch permutation into expert-contiguous, beta-aligned row segments
  *   moe_plan        greedy skew-balancing plan over P logical rank partitions + block table
  *   moe_expert_ffn  SwiGLU expert FFN over the block table (grouped GEMMs on bf16 MFMA);
@@ -16,6 +18,7 @@
  *   [MEP] "MoonEP routing flow -- live", sections "Per-expert breakdown", "The greedy
  *         balance, step by step", "Memory: reserved once, breathing never".
  *   [RN]  Daily Papers listing: the abstract on top-k probability renormalisation.
+ *   [TM]  Daily Papers listing: the TritonMoE abstract (router scoring in the fused pass).
  *
  * Conventions shared by every call:
  *   - All data pointers are DEVICE pointers (hipMalloc'd or torch CUDA tensors); sizes are
@@ -92,6 +95,30 @@ int64_t moe_ffn_workspace_elems(int max_blocks);
 moe_status_t moe_route(const float* logits, int T, int E, int K, int renormalize,
                        int32_t* topk_ids, float* topk_w, int32_t* expert_counts,
                        hipStream_t stream);
+
+/* Top-k with a reference set ([RN]: activate the top k_1 experts, normalise their weights by
+ * the probability mass of the top k_2): ids and counts as moe_route; with m the token's
+ * largest logit, topk_w[t][k] = exp(l_k - m) / sum of exp(l - m) over the token's top k_ref
+ * experts (the same ranking).  k_ref = K is moe_route with renormalize = 1, k_ref = E with
+ * renormalize = 0.  K <= k_ref <= E; k_ref <= 16 unless k_ref = E (MOE_ERR_UNSUPPORTED). */
+moe_status_t moe_route_ref(const float* logits, int T, int E, int K, int k_ref,
+                           int32_t* topk_ids, float* topk_w, int32_t* expert_counts,
+                           hipStream_t stream);
+
+/* Linear router scores with the top-k fused behind them ([TM]: router scoring opens the
+ * fused forward pass; [MF §1]: the top-k experts take the token):
+ *   logits[t][e] = sum over h of x[t][h] * w_router[e][h]      (float32 accumulation)
+ * then ids / weights / counts as moe_route_ref on those logits.
+ *   x         [T, H] activations (dtype dt); w_router [E, H] router rows (dtype dt).
+ *   logits    [T, E] float32 out, or NULL: the scores the top-k was taken on (bf16 inputs
+ *             are multiplied exactly and summed in float32, in an order of the library's
+ *             choosing).
+ *   topk_ids, topk_w, expert_counts as moe_route (counts zeroed by the callee).
+ * bf16 needs H a multiple of 64 and T * H * 2 < 4 GiB; float32 needs H a multiple of 4.
+ * E <= 256; K <= 16; k_ref as for moe_route_ref. */
+moe_status_t moe_router_topk(const void* x, moe_dtype_t dt, const void* w_router, int T, int H,
+                             int E, int K, int k_ref, float* logits, int32_t* topk_ids,
+                             float* topk_w, int32_t* expert_counts, hipStream_t stream);
 
 /* ---------------------------------------------------------------------- permute --- */
 

@@ -49,6 +49,9 @@ _SIGNATURES = {
     "moe_expert_ffn_fc1_gather": (_i32, [_vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp, _vp,
                                          _i32, _vp, _i64, _vp, _i64, _vp]),
     "moe_expert_ffn_tile_schedule": (_i32, [_vp, _vp, _i32, _i32, _vp, _i64, _vp]),
+    "moe_route_ref": (_i32, [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "moe_router_topk": (_i32, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
+                               _vp]),
     "moe_combine": (_i32, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
 }
 
@@ -139,6 +142,33 @@ def moe_route(logits, K, topk_ids, topk_w, expert_counts, renormalize=True, stre
                            _ptr(topk_w, torch.float32, "topk_w"),
                            _ptr(expert_counts, torch.int32, "expert_counts"), _stream(stream)),
            "moe_route")
+
+
+def moe_route_ref(logits, K, k_ref, topk_ids, topk_w, expert_counts, stream=None):
+    T, E = logits.shape
+    _check(lib().moe_route_ref(_ptr(logits, torch.float32, "logits"), T, E, K, k_ref,
+                               _ptr(topk_ids, torch.int32, "topk_ids"),
+                               _ptr(topk_w, torch.float32, "topk_w"),
+                               _ptr(expert_counts, torch.int32, "expert_counts"),
+                               _stream(stream)),
+           "moe_route_ref")
+
+
+def moe_router_topk(x, w_router, K, k_ref, topk_ids, topk_w, expert_counts, logits=None,
+                    stream=None):
+    """Router scores x . w_router^T (float32 accumulation) and the top-k on them; logits
+    ([T, E] float32) receives the scores when given."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    if w_router.shape[1] != H:
+        raise MoeError("moe_router_topk: w_router must be [E, H]")
+    _check(lib().moe_router_topk(_ptr(x, None, "x"), _dt(x), _ptr(w_router, x.dtype, "w_router"),
+                                 T, H, E, K, k_ref, _ptr(logits, torch.float32, "logits"),
+                                 _ptr(topk_ids, torch.int32, "topk_ids"),
+                                 _ptr(topk_w, torch.float32, "topk_w"),
+                                 _ptr(expert_counts, torch.int32, "expert_counts"),
+                                 _stream(stream)),
+           "moe_router_topk")
 
 
 def moe_permute(x, topk_ids, expert_counts, E, expert_begin, expert_stride, E_loc, block_m,

@@ -61,8 +61,35 @@ moe_status_t moe_route(const float* logits, int T, int E, int K, int renormalize
     if (!logits || !topk_ids || !topk_w || !expert_counts) return MOE_ERR_INVALID;
     if (T < 1 || E < 1 || K < 1 || K > E || (int64_t)T * E > 0x7FFFFFFFLL) return MOE_ERR_INVALID;
     if (E > 256 || K > MOE_MAX_K) return MOE_ERR_UNSUPPORTED;
-    return launched(moe_launch_route(logits, T, E, K, renormalize, topk_ids, topk_w,
+    return launched(moe_launch_route(logits, T, E, K, renormalize ? K : E, topk_ids, topk_w,
                                      expert_counts, stream));
+}
+
+moe_status_t moe_route_ref(const float* logits, int T, int E, int K, int k_ref,
+                           int32_t* topk_ids, float* topk_w, int32_t* expert_counts,
+                           hipStream_t stream) {
+    if (!logits || !topk_ids || !topk_w || !expert_counts) return MOE_ERR_INVALID;
+    if (T < 1 || E < 1 || K < 1 || K > E || (int64_t)T * E > 0x7FFFFFFFLL) return MOE_ERR_INVALID;
+    if (k_ref < K || k_ref > E) return MOE_ERR_INVALID;
+    if (E > 256 || K > MOE_MAX_K || (k_ref > MOE_MAX_K && k_ref < E)) return MOE_ERR_UNSUPPORTED;
+    return launched(moe_launch_route(logits, T, E, K, k_ref, topk_ids, topk_w, expert_counts,
+                                     stream));
+}
+
+moe_status_t moe_router_topk(const void* x, moe_dtype_t dt, const void* w_router, int T, int H,
+                             int E, int K, int k_ref, float* logits, int32_t* topk_ids,
+                             float* topk_w, int32_t* expert_counts, hipStream_t stream) {
+    if (!x || !w_router || !topk_ids || !topk_w || !expert_counts) return MOE_ERR_INVALID;
+    if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID;
+    if (T < 1 || H < 1 || E < 1 || K < 1 || K > E || k_ref < K || k_ref > E) return MOE_ERR_INVALID;
+    if ((int64_t)T * E > 0x7FFFFFFFLL) return MOE_ERR_INVALID;
+    if (!aligned16(x) || !aligned16(w_router)) return MOE_ERR_INVALID;
+    if (E > 256 || K > MOE_MAX_K || (k_ref > MOE_MAX_K && k_ref < E)) return MOE_ERR_UNSUPPORTED;
+    if (dt == MOE_BF16 && (H % 64 != 0 || (int64_t)T * H * 2 > 0xFFFFFFFFLL - 16))
+        return MOE_ERR_UNSUPPORTED;
+    if (dt == MOE_F32 && H % 4 != 0) return MOE_ERR_UNSUPPORTED;
+    return launched(moe_launch_router_topk(x, dt, w_router, T, H, E, K, k_ref, logits, topk_ids,
+                                           topk_w, expert_counts, stream));
 }
 
 moe_status_t moe_permute(const void* x, moe_dtype_t dt, int T, int H, int K, int E,

@@ -7,9 +7,15 @@
 #define MOE_PERMUTE_CHUNK 16  // tokens per permutation chunk
 #define MOE_MAX_K 16          // largest top-k
 
-hipError_t moe_launch_route(const float* logits, int T, int E, int K, int renormalize,
+// k_ref: weights over the mass of the top k_ref experts (k_ref >= E: plain softmax)
+hipError_t moe_launch_route(const float* logits, int T, int E, int K, int k_ref,
                             int32_t* topk_ids, float* topk_w, int32_t* counts,
                             hipStream_t stream);
+hipError_t moe_launch_zero_counts(int32_t* counts, int E, hipStream_t stream);
+hipError_t moe_launch_router_topk(const void* x, moe_dtype_t dt, const void* w_router, int T,
+                                  int H, int E, int K, int k_ref, float* logits,
+                                  int32_t* topk_ids, float* topk_w, int32_t* counts,
+                                  hipStream_t stream);
 
 hipError_t moe_launch_permute(const void* x, int64_t row_bytes, int T, int K,
                               const int32_t* ids, const int32_t* counts, int begin, int stride,

@@ -67,6 +67,20 @@ def test_route_rejects(lib):
     assert lib.moe_route(P[0], 8, 64, 17, 1, P[1], P[2], P[3], NULL) == UNSUPPORTED
 
 
+def test_route_ref_and_router_reject(lib):
+    assert lib.moe_route_ref(P[0], 8, 64, 4, 3, P[1], P[2], P[3], NULL) == INVALID   # k_ref < K
+    assert lib.moe_route_ref(P[0], 8, 64, 4, 65, P[1], P[2], P[3], NULL) == INVALID  # k_ref > E
+    assert lib.moe_route_ref(P[0], 8, 64, 4, 20, P[1], P[2], P[3], NULL) == UNSUPPORTED
+    rt = lambda x=P[0], dt=1, T=64, H=128, E=64, K=4, k_ref=4: lib.moe_router_topk(
+        x, dt, P[1], T, H, E, K, k_ref, NULL, P[2], P[3], P[4], NULL)
+    assert rt(x=NULL) == INVALID
+    assert rt(dt=3) == INVALID
+    assert rt(k_ref=2) == INVALID
+    assert rt(x=ctypes.c_void_p(0x1008)) == INVALID   # misaligned
+    assert rt(H=100) == UNSUPPORTED                   # bf16 needs H % 64 == 0
+    assert rt(E=300, K=4) == UNSUPPORTED
+
+
 def _permute(lib, **kw):
     a = dict(x=P[0], dt=1, T=64, H=128, K=2, E=8, ids=P[1], counts=P[2], begin=0, stride=1,
              E_loc=8, bm=128, offsets=P[3], entry_pos=P[4], row_token=P[5], xp=P[6],
