@@ -354,70 +354,269 @@ ffn_schedule_kernel(const int32_t* __restrict__ blocks, const int32_t* __restric
 // One item: C rows of tile (h_row0, h_rows) x column tile nt of expert B (see ffn_bf16_kernel).
 // Wave (wm, wn) = (wave >> 2, wave & 3) computes kRowBlocks 32-row blocks starting at tile row
 // wm * kRowsA / 2, against 64 B rows (FC1: 32 gate rows and the 32 matching up rows).
-template <bool kSwiGLU, int kRowsA>
-__device__ __forceinline__ void gemm_item(const uint16_t* __restrict__ A, int64_t a_rows, int Kdim,
-                                          const uint16_t* __restrict__ Bexp, int b_rows,
-                                          uint16_t* __restrict__ C, int ldc, int n_cols, int I,
-                                          int nt, const int (&h_row0)[2], const int (&h_rows)[2],
-                                          uint8_t* smem, uint32_t smem_base, int wave, int lane,
-                                          int seg_row, int seg_lchunk,
-                                          const int32_t* __restrict__ gather) {
+// Kernel-wide arguments of one grouped GEMM launch.
+struct GemmArgs {
+    const uint16_t* A;       // [a_rows, Kdim], or the token rows of x with `gather`
+    int64_t a_rows;
+    int Kdim;
+    const uint16_t* B;       // [E_loc][b_rows, Kdim]
+    int64_t b_expert_stride;
+    int b_rows;
+    uint16_t* C;             // [rows, ldc]
+    int ldc, n_cols, I, NT;
+    const int32_t* tiles;    // the schedule's tile records
+    int32_t* ctr;            // this GEMM's per-XCD item counters
+    int total, per_xcd_items, xcd;
+    const int32_t* gather;   // row_token (gather-on-load) or nullptr
+};
+
+// One item (tile, column tile): its wave-uniform description and this lane's A copy offsets
+// (byte offsets from the item's A base pointers: row * Kdim * 2 + chunk * 16, < 4 GiB; the B
+// offsets follow from nt and are formed per copy).
+struct Item {
+    int rows_a;  // A rows staged per slice: 256, 128 or 64; 0 = no item (the queues are drained)
+    int l, nt;
+    int h_row0[2], h_rows[2];
+    int it, ts, cnt;
+    uint32_t offa[4];  // with gather (decode step 4 leaves the token rows here, step 5 the offsets)
+};
+
+// Thread 0's queue state: the queue being tried (own XCD first, then the others in turn) and
+// the value of its last counter increment.
+struct Queue {
+    int q;
+    int raw;
+};
+
+// Two floats -> packed bf16x2 (low half = a), nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+__device__ __forceinline__ int rows_mode(int h_rows1, int h_rows0) {
+    return h_rows1 > 0 ? 256 : (h_rows0 > 64 ? 128 : 64);
+}
+
+// The item's wave-uniform fields as scalars.  They are uniform by construction (decoded from
+// one LDS word), but the decode's joins with thread 0's queue branch hide that from the
+// compiler, which would otherwise keep them (and the copy base pointers) in vector registers.
+__device__ __forceinline__ Item uniform_item(const Item& it) {
+    Item u = it;
+    u.rows_a = __builtin_amdgcn_readfirstlane(it.rows_a);
+    u.l = __builtin_amdgcn_readfirstlane(it.l);
+    u.nt = __builtin_amdgcn_readfirstlane(it.nt);
+    u.h_row0[0] = __builtin_amdgcn_readfirstlane(it.h_row0[0]);
+    u.h_row0[1] = __builtin_amdgcn_readfirstlane(it.h_row0[1]);
+    u.h_rows[0] = __builtin_amdgcn_readfirstlane(it.h_rows[0]);
+    u.h_rows[1] = __builtin_amdgcn_readfirstlane(it.h_rows[1]);
+    return u;
+}
+
+__device__ __forceinline__ const uint8_t* base_a(const GemmArgs& g, const Item& it, int h) {
+    const int row0 = h ? it.h_row0[1] : it.h_row0[0];
+    return reinterpret_cast<const uint8_t*>(g.gather ? g.A : g.A + (int64_t)row0 * g.Kdim);  // gather: rows of x
+}
+
+__device__ __forceinline__ const uint8_t* base_b(const GemmArgs& g, const Item& it) {
+    return reinterpret_cast<const uint8_t*>(g.B + (int64_t)it.l * g.b_expert_stride);
+}
+
+// Decoding the next item takes six steps, each using what the step before loaded, so that
+// the loads' latency hides behind the current item's last K slices (one step per slice
+// boundary).  A copy q of wave w fills tile rows 64q + 8w + (0..7) (half q / 2).
+//   0: thread 0 increments its queue's counter          3: load the tile record
+//   1: thread 0 resolves the item (trying the other     4: with gather, load the token row
+//      queues when its own is drained), publishes it       of each of this lane's A copies
+//      in LDS                                            5: this lane's copy offsets
+//   2: read the item; load its tile group's first tile and tile count
+// Steps 1 and 2 must be separated by a barrier (the slice boundaries are).
+template <bool kSwiGLU, bool kGather>
+__device__ __forceinline__ void decode_step(int s, Item& n, const GemmArgs& g, Queue& qs,
+                                            int* item_s, int tid, int wave, int seg_row,
+                                            int seg_lchunk) {
+    switch (s) {
+        case 0:
+            if (tid == 0 && qs.q < kXcds) qs.raw = atomicAdd(&g.ctr[(g.xcd + qs.q) % kXcds], 1);
+            break;
+        case 1:
+            if (tid == 0) {
+                int got = -1;
+                while (qs.q < kXcds) {
+                    const int x = (g.xcd + qs.q) % kXcds;
+                    const int it = x * g.per_xcd_items + qs.raw;
+                    if (qs.raw < g.per_xcd_items && it < g.total) {
+                        got = it;
+                        break;
+                    }
+                    if (++qs.q < kXcds) qs.raw = atomicAdd(&g.ctr[(g.xcd + qs.q) % kXcds], 1);
+                }
+                *item_s = got;
+            }
+            break;
+        case 2: {
+            n.it = __builtin_amdgcn_readfirstlane(*item_s);
+            n.rows_a = 0;
+            if (n.it >= 0) {
+                const int32_t* tg = g.tiles + TILE_INTS * (n.it / g.NT);
+                n.ts = __builtin_amdgcn_readfirstlane(tg[5]);
+                n.cnt = __builtin_amdgcn_readfirstlane(tg[6]);
+            }
+            break;
+        }
+        case 3:
+            if (n.it >= 0) {
+                // item -> (tile, column tile): the expert's items [ts * NT, (ts + cnt) * NT) in
+                // groups of kGroupTiles tiles, column-tile-major inside a group
+                const int local = n.it - n.ts * g.NT;
+                const int grp = local / (kGroupTiles * g.NT);
+                const int r = local - grp * (kGroupTiles * g.NT);
+                const int rest = n.cnt - grp * kGroupTiles;
+                const int ct = rest < kGroupTiles ? rest : kGroupTiles;
+                n.nt = r / ct;
+                const int t = n.ts + grp * kGroupTiles + (r - n.nt * ct);
+                const int32_t* tl = g.tiles + TILE_INTS * t;
+                n.l = __builtin_amdgcn_readfirstlane(tl[0]);
+                n.h_row0[0] = __builtin_amdgcn_readfirstlane(tl[1]);
+                n.h_rows[0] = __builtin_amdgcn_readfirstlane(tl[2]);
+                n.h_row0[1] = __builtin_amdgcn_readfirstlane(tl[3]);
+                n.h_rows[1] = __builtin_amdgcn_readfirstlane(tl[4]);
+            }
+            break;
+        case 4:
+            if (n.it >= 0) {
+                n.rows_a = rows_mode(n.h_rows[1], n.h_rows[0]);
+                if (kGather) {
+                    const int copies = n.rows_a / 64;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        if (q < copies) {
+                            const int h = q >> 1;
+                            int rr = ((q & 1) * 8 + wave) * SEG_ROWS + seg_row;
+                            const int hr = h ? n.h_rows[1] : n.h_rows[0];
+                            if (rr > hr - 1) rr = hr - 1;  // read, unused
+                            n.offa[q] = (uint32_t)g.gather[(h ? n.h_row0[1] : n.h_row0[0]) + rr];
+                        }
+                    }
+                }
+            }
+            break;
+        case 5:
+            if (kGather && n.it >= 0) {
+                const int copies = n.rows_a / 64;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int tok = q < copies && (int)n.offa[q] >= 0 ? (int)n.offa[q] : 0;
+                    n.offa[q] = (uint32_t)tok * (uint32_t)g.Kdim * 2u + seg_lchunk * 16u;
+                }
+            }
+            break;
+        default:
+            break;
+    }
+}
+
+// Copies of K slice kt of item `it` into ring slot kt % kStages (this wave's share).
+// This lane's byte offset for B copy q of an item: B tile row (q * 8 + w) * 8 + seg_row is
+// W1 row nt * 128 + r (gate, r < 128) or I + nt * 128 + r - 128 (up) for FC1, W2 row
+// nt * 256 + r for FC2; rows past the end are clamped (read, not stored).
+template <bool kSwiGLU>
+__device__ __forceinline__ uint32_t b_offset(const GemmArgs& g, int nt, int q, int wave,
+                                             int seg_row, uint32_t lane_chunk) {
+    const int r0 = (q * 8 + wave) * SEG_ROWS;
+    const int base = kSwiGLU ? (q < 2 ? nt * (BN / 2) + r0 : g.I + nt * (BN / 2) + r0 - BN / 2)
+                             : nt * BN + r0;
+    int br = base + seg_row;
+    if (br > g.b_rows - 1) br = g.b_rows - 1;
+    return (uint32_t)br * (uint32_t)g.Kdim * 2u + lane_chunk;
+}
+
+// This lane's byte offset for A copy q of an item without gather: row ((q & 1) * 8 + w) * 8 +
+// seg_row of half q / 2, clamped to the last row of A (read, unused), from that half's base.
+__device__ __forceinline__ uint32_t a_offset(const GemmArgs& g, const Item& it, int q, int wave,
+                                             int seg_row, uint32_t lane_chunk) {
+    const int h = q >> 1;
+    const int row0 = h ? it.h_row0[1] : it.h_row0[0];
+    int rr = ((q & 1) * 8 + wave) * SEG_ROWS + seg_row;
+    if (row0 + rr > g.a_rows - 1) rr = (int)(g.a_rows - 1 - row0);
+    return (uint32_t)rr * (uint32_t)g.Kdim * 2u + lane_chunk;
+}
+
+template <bool kSwiGLU, bool kGather, int kRowsA>
+__device__ __forceinline__ void issue_slice(const GemmArgs& g, const Item& it, int kt,
+                                            uint32_t smem_base, int wave, int seg_row,
+                                            uint32_t lane_chunk) {
     using M = Mode<kRowsA>;
+    const uint32_t st = smem_base + (kt % M::kStages) * M::kStageBytes;
+    const uint32_t koff = (uint32_t)kt * (BK * 2);
+    const uint32_t ma = st + wave * (M::kACopies * 1024);
+    const uint8_t* a0 = base_a(g, it, 0);
+    const uint8_t* bx = base_b(g, it);
+    uint32_t oa[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        oa[q] = (kGather ? it.offa[q] : a_offset(g, it, q, wave, seg_row, lane_chunk)) + koff;
+    if constexpr (kRowsA == 256) {
+        const uint8_t* a1 = base_a(g, it, 1);
+        four_copies(ma, a0, a0 - 1024, a1 - 2048, a1 - 3072, oa[0], oa[1], oa[2], oa[3], true);
+    } else if constexpr (kRowsA == 128) {
+        four_copies(ma, a0, a0 - 1024, a0, a0, oa[0], oa[1], 0, 0, false);
+    } else {
+        one_copy(ma, a0, oa[0]);
+    }
+    four_copies(st + M::kARegion + wave * 4096, bx, bx - 1024, bx - 2048, bx - 3072,
+                b_offset<kSwiGLU>(g, it.nt, 0, wave, seg_row, lane_chunk) + koff,
+                b_offset<kSwiGLU>(g, it.nt, 1, wave, seg_row, lane_chunk) + koff,
+                b_offset<kSwiGLU>(g, it.nt, 2, wave, seg_row, lane_chunk) + koff,
+                b_offset<kSwiGLU>(g, it.nt, 3, wave, seg_row, lane_chunk) + koff, true);
+}
+
+template <bool kSwiGLU, bool kGather, int kRowsA>
+__device__ __forceinline__ void issue_prologue_m(const GemmArgs& g, const Item& it,
+                                                 uint32_t smem_base, int wave, int seg_row,
+                                                 uint32_t lane_chunk) {
+    const int nk = g.Kdim / BK;
+    const int pre = nk < Mode<kRowsA>::kStages ? nk : Mode<kRowsA>::kStages;
+    for (int s = 0; s < pre; ++s)
+        issue_slice<kSwiGLU, kGather, kRowsA>(g, it, s, smem_base, wave, seg_row, lane_chunk);
+}
+
+// The first kStages slices of an item (the ring must be free).
+template <bool kSwiGLU, bool kGather>
+__device__ __forceinline__ void issue_prologue(const GemmArgs& g, const Item& item,
+                                               uint32_t smem_base, int wave, int seg_row,
+                                               uint32_t lane_chunk) {
+    const Item it = uniform_item(item);
+    if (it.rows_a == 256)
+        issue_prologue_m<kSwiGLU, kGather, 256>(g, it, smem_base, wave, seg_row, lane_chunk);
+    else if (it.rows_a == 128)
+        issue_prologue_m<kSwiGLU, kGather, 128>(g, it, smem_base, wave, seg_row, lane_chunk);
+    else if (it.rows_a == 64)
+        issue_prologue_m<kSwiGLU, kGather, 64>(g, it, smem_base, wave, seg_row, lane_chunk);
+}
+
+// One item whose first slices are already issued: the K loop; meanwhile the next item is
+// decoded (decode_step, over the last slice boundaries); then the next item's first slices
+// are issued, and this item's results are written from registers while they land.
+template <bool kSwiGLU, bool kGather, int kRowsA>
+__device__ __forceinline__ void gemm_item(const GemmArgs& g, const Item& cur_in, Item& nxt,
+                                          Queue& qs, int* item_s, uint8_t* smem,
+                                          uint32_t smem_base, int tid, int wave, int lane,
+                                          int seg_row, int seg_lchunk) {
+    using M = Mode<kRowsA>;
+    const Item cur = uniform_item(cur_in);
     constexpr int RB = M::kRowBlocks;
+    constexpr int kDecodeSteps = 6;
     const int wm = wave >> 2;
     const int wn = wave & 3;
     const int wrow = wm * (kRowsA / 2);  // first tile row of this wave
-    const bool active = kRowsA != 64 || wrow < h_rows[0];  // 64-row items: idle past the rows
-    const int nk = Kdim / BK;
-
-    // per copy: a wave-uniform base (A half 0, A half 1, or the expert's B) and this lane's
-    // byte offset from it (row * Kdim * 2 + chunk * 16; < 4 GiB).  A copy q fills segment
-    // wave + 8q: tile rows 64q + 8 wave + (0..7), i.e. half q / 2.  With `gather`, tile row p
-    // is row gather[p] of A (the token's row of x) and every A copy uses the base A.
-    const uint8_t* a0 = reinterpret_cast<const uint8_t*>(gather ? A : A + (int64_t)h_row0[0] * Kdim);
-    const uint8_t* a1 = reinterpret_cast<const uint8_t*>(gather ? A : A + (int64_t)h_row0[1] * Kdim);
-    const uint8_t* bx = reinterpret_cast<const uint8_t*>(Bexp);
-    uint32_t offa[M::kACopies], offb[4];
-#pragma unroll
-    for (int q = 0; q < M::kACopies; ++q) {
-        const int h = q >> 1;
-        int rr = ((q & 1) * 8 + wave) * SEG_ROWS + seg_row;  // row within half h
-        int64_t arow;
-        if (gather) {
-            if (rr > h_rows[h] - 1) rr = h_rows[h] - 1;  // rows past the piece: read, unused
-            const int tok = gather[h_row0[h] + rr];
-            arow = tok < 0 ? 0 : tok;
-        } else {
-            if (h_row0[h] + rr > a_rows - 1) rr = (int)(a_rows - 1 - h_row0[h]);  // read, unused
-            arow = rr;
-        }
-        offa[q] = (uint32_t)arow * (uint32_t)Kdim * 2u + seg_lchunk * 16u;
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int rr = (q * 8 + wave) * SEG_ROWS + seg_row;  // B row in the tile
-        int br;
-        if (kSwiGLU)
-            br = rr < BN / 2 ? nt * (BN / 2) + rr : I + nt * (BN / 2) + (rr - BN / 2);
-        else
-            br = nt * BN + rr;
-        if (br > b_rows - 1) br = b_rows - 1;  // columns past the end: read, not stored
-        offb[q] = (uint32_t)br * (uint32_t)Kdim * 2u + seg_lchunk * 16u;
-    }
-    auto issue = [&](int kt) {
-        const uint32_t st = smem_base + (kt % M::kStages) * M::kStageBytes;
-        const uint32_t koff = (uint32_t)kt * (BK * 2);
-        const uint32_t ma = st + wave * (M::kACopies * 1024);
-        if constexpr (kRowsA == 256)
-            four_copies(ma, a0, a0 - 1024, a1 - 2048, a1 - 3072, offa[0] + koff, offa[1] + koff,
-                        offa[2] + koff, offa[3] + koff, true);
-        else if constexpr (kRowsA == 128)
-            four_copies(ma, a0, a0 - 1024, a0, a0, offa[0] + koff, offa[1] + koff, 0, 0, false);
-        else
-            one_copy(ma, a0, offa[0] + koff);
-        four_copies(st + M::kARegion + wave * 4096, bx, bx - 1024, bx - 2048, bx - 3072,
-                    offb[0] + koff, offb[1] + koff, offb[2] + koff, offb[3] + koff, true);
-    };
+    const bool active = kRowsA != 64 || wrow < cur.h_rows[0];  // 64-row items: idle past the rows
+    const int nk = g.Kdim / BK;
+    const int pre = nk < M::kStages ? nk : M::kStages;
+    // the decode steps run at the boundaries after slices first_step .. first_step + 5
+    const int first_step = nk - 1 - kDecodeSteps > 0 ? nk - 1 - kDecodeSteps : 0;
 
     f32x16_t acc[RB][2];
 #pragma unroll
@@ -443,75 +642,113 @@ __device__ __forceinline__ void gemm_item(const uint16_t* __restrict__ A, int64_
             fa[buf][i] = lds_frag<kRowsA>(st, wrow + i * 32 + (lane & 31), false, ch);
     };
 
-    __syncthreads();  // the previous item's last LDS reads are done
-    const int pre = nk < M::kStages ? nk : M::kStages;  // every slot filled before the loop
-    for (int s = 0; s < pre; ++s) issue(s);
+    // slice 0 in LDS everywhere (stores of the previous item may still be counted: stricter)
     wait_copies_and_barrier((pre - 1) * M::kCopies);
     if (active) load_frags(0, 0, 0);
 
+    int step = 0;
     for (int kt = 0; kt < nk; ++kt) {
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
-            const int cur = kk & 1;
+            const int cur_buf = kk & 1;
             if (active) {
-                if (kk + 1 < BK / 16) load_frags(kt, kk + 1, cur ^ 1);
+                if (kk + 1 < BK / 16) load_frags(kt, kk + 1, cur_buf ^ 1);
                 // D = B-rows x A-rows: lane keeps one A row and 4 consecutive columns per
-                // register group, so the epilogue stores 8 bytes at a time
+                // register group
 #pragma unroll
                 for (int i = 0; i < RB; ++i)
 #pragma unroll
                     for (int j = 0; j < 2; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cur][j], fa[cur][i],
-                                                                            acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            fb[cur_buf][j], fa[cur_buf][i], acc[i][j], 0, 0, 0);
             }
             if (kk + 1 == BK / 16 && kt + 1 < nk) {
                 // behind slice kt's last MFMAs: wait for slice kt+1 everywhere (slices up to
-                // kt+kStages-1 are issued); then slice kt's slot is free for slice
-                // kt+kStages; first fragments of slice kt+1
+                // kt+kStages-1 are issued); one decode step of the next item (its loads go
+                // out before the next copies); slice kt's slot then takes slice kt+kStages;
+                // first fragments of slice kt+1
                 const int issued = kt + M::kStages - 1 < nk ? kt + M::kStages - 1 : nk - 1;
                 wait_copies_and_barrier((issued - (kt + 1)) * M::kCopies);
-                if (kt + M::kStages < nk) issue(kt + M::kStages);
-                if (active) load_frags(kt + 1, 0, cur ^ 1);
+                if (kt >= first_step && step < kDecodeSteps)
+                    decode_step<kSwiGLU, kGather>(step++, nxt, g, qs, item_s, tid, wave, seg_row, seg_lchunk);
+                if (kt + M::kStages < nk)
+                    issue_slice<kSwiGLU, kGather, kRowsA>(g, cur, kt + M::kStages, smem_base, wave, seg_row,
+                                                 seg_lchunk * 16u);
+                if (active) load_frags(kt + 1, 0, cur_buf ^ 1);
             }
         }
     }
 
-    // epilogue: acc[i][j][4g + e] = C[tile row wrow + i*32 + lane%32][col + 8g + 4(lane/32) + e]
+    // every wave is done with the ring; finish decoding the next item and start its slices
+    wait_copies_and_barrier(0);
+    if (step < 2) {
+        if (step == 0) decode_step<kSwiGLU, kGather>(0, nxt, g, qs, item_s, tid, wave, seg_row, seg_lchunk);
+        decode_step<kSwiGLU, kGather>(1, nxt, g, qs, item_s, tid, wave, seg_row, seg_lchunk);
+        __syncthreads();
+        step = 2;
+    }
+    for (; step < kDecodeSteps; ++step)
+        decode_step<kSwiGLU, kGather>(step, nxt, g, qs, item_s, tid, wave, seg_row, seg_lchunk);
+    issue_prologue<kSwiGLU, kGather>(g, nxt, smem_base, wave, seg_row, seg_lchunk * 16u);
+
+    // epilogue: acc[i][j][4c + e] = C[tile row wrow + i*32 + lane%32][col + 8c + 4(lane/32) + e].
+    // Lanes l and l + 32 hold one row; after an exchange of half their packed values, lane l
+    // holds columns 0..15 and lane l + 32 columns 16..31 of each 32-column block, stored as
+    // two 16-byte pieces.
     if (active) {
+        const bool hi = lane >= 32;
 #pragma unroll
         for (int i = 0; i < RB; ++i) {
             const int tr = wrow + i * 32 + (lane & 31);
-            const int h = tr >> 7, rl = tr & (HALF - 1);
-            if (rl >= h_rows[h]) continue;
-            uint16_t* crow = C + (int64_t)(h_row0[h] + rl) * ldc;
+            const int rl = tr & (HALF - 1);
+            // selects, not an indexed load: the item stays in registers
+            const bool h1 = tr >= HALF;
+            const bool row_ok = rl < (h1 ? cur.h_rows[1] : cur.h_rows[0]);
+            uint16_t* crow = g.C + (int64_t)((h1 ? cur.h_row0[1] : cur.h_row0[0]) + rl) * g.ldc;
+            constexpr int NJ = kSwiGLU ? 1 : 2;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int c4 = 8 * g + 4 * (lane >> 5);
-                if (kSwiGLU) {
-                    const int col = nt * (BN / 2) + wn * 32 + c4;
-                    if (col < n_cols) {  // n_cols is a multiple of 64: all 4 or none
-                        float v[4];
+            for (int j = 0; j < NJ; ++j) {
+                uint32_t pk[4][2];  // [register group c][half]: columns 8c + 4(lane/32) + 0..3
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float gt = acc[i][0][4 * g + e];
-                            const float up = acc[i][1][4 * g + e];
-                            v[e] = gt / (1.f + expf(-gt)) * up;
+                for (int c = 0; c < 4; ++c) {
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if (kSwiGLU) {
+                            const float gt = acc[i][0][4 * c + e];
+                            const float up = acc[i][1][4 * c + e];
+                            // SiLU(g) * u = g * u / (1 + 2^(-g log2 e))
+                            const float den = 1.f + __builtin_amdgcn_exp2f(gt * -1.4426950408889634f);
+                            v[e] = gt * __builtin_amdgcn_rcpf(den) * up;
+                        } else {
+                            v[e] = acc[i][j][4 * c + e];
                         }
-                        uint2 o;
-                        o.x = moe_pack_bf16x2(v[0], v[1]);
-                        o.y = moe_pack_bf16x2(v[2], v[3]);
-                        *reinterpret_cast<uint2*>(crow + col) = o;
                     }
-                } else {
+                    pk[c][0] = pack_bf16x2(v[0], v[1]);
+                    pk[c][1] = pack_bf16x2(v[2], v[3]);
+                }
+                // lane < 32 keeps groups 0, 1 and takes its partner's; lane >= 32 keeps 2, 3
+                uint32_t mine[2][2], theirs[2][2];
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const int col = nt * BN + wn * 64 + j * 32 + c4;
-                        if (col < n_cols) {
-                            uint2 o;
-                            o.x = moe_pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]);
-                            o.y = moe_pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-                            *reinterpret_cast<uint2*>(crow + col) = o;
+                for (int c = 0; c < 2; ++c)
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) {
+                        const uint32_t send = hi ? pk[c][s] : pk[c + 2][s];
+                        mine[c][s] = hi ? pk[c + 2][s] : pk[c][s];
+                        theirs[c][s] = (uint32_t)__shfl_xor((int)send, 32, MOE_WAVE);
+                    }
+                const int col0 = kSwiGLU ? cur.nt * (BN / 2) + wn * 32
+                                         : cur.nt * BN + wn * 64 + j * 32;
+                if (row_ok && col0 < g.n_cols) {  // n_cols is a multiple of 64: all or none
+#pragma unroll
+                    for (int c = 0; c < 2; ++c) {
+                        uint4 o;
+                        if (hi) {  // columns 16 + 8c .. : partner's 4, then own 4
+                            o.x = theirs[c][0]; o.y = theirs[c][1]; o.z = mine[c][0]; o.w = mine[c][1];
+                        } else {   // columns 8c .. : own 4, then partner's 4
+                            o.x = mine[c][0]; o.y = mine[c][1]; o.z = theirs[c][0]; o.w = theirs[c][1];
                         }
+                        *reinterpret_cast<uint4*>(crow + col0 + (hi ? 16 : 0) + 8 * c) = o;
                     }
                 }
             }
@@ -525,7 +762,14 @@ __device__ __forceinline__ void gemm_item(const uint16_t* __restrict__ A, int64_
 // A is [a_rows, Kdim], B per expert [b_rows, Kdim]; both K-contiguous.  With `gather`
 // (row_token of the dispatch permutation), A[p] above means A[gather[p]]: the rows are read
 // straight from the token rows of x and no permuted copy is needed.
-template <bool kSwiGLU>
+//
+// Items (tile, column tile) are cut into 8 contiguous ranges, one per XCD (workgroup w runs
+// on XCD w % 8), so the items in flight on an XCD share A rows and B rows in its L2.
+// Workgroups take items from their XCD's range through an atomic counter (in order,
+// self-balancing); a workgroup whose range is drained helps the others.  Items are
+// pipelined: the next one is claimed and decoded during the current one's last K slices and
+// its first slices are in flight while the current one's results are written.
+template <bool kSwiGLU, bool kGather>
 __global__ void __launch_bounds__(kThreads, 1)
 ffn_bf16_kernel(const uint16_t* __restrict__ A, int64_t a_rows, int Kdim,
                 const uint16_t* __restrict__ B, int64_t b_expert_stride, int b_rows,
@@ -533,80 +777,56 @@ ffn_bf16_kernel(const uint16_t* __restrict__ A, int64_t a_rows, int Kdim,
                 int max_blocks, int32_t* __restrict__ ws, const int32_t* __restrict__ gather) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM_BYTES];
     __shared__ int item_s;
-    const int32_t* tiles = ws + WS_HEAD + max_blocks;
-    int32_t* ctr = ws + (kSwiGLU ? WS_CTR_FC1 : WS_CTR_FC2);
+
+    GemmArgs g;
+    g.A = A; g.a_rows = a_rows; g.Kdim = Kdim;
+    g.B = B; g.b_expert_stride = b_expert_stride; g.b_rows = b_rows;
+    g.C = C; g.ldc = ldc; g.n_cols = n_cols; g.I = I; g.NT = NT;
+    g.tiles = ws + WS_HEAD + max_blocks;
+    g.ctr = ws + (kSwiGLU ? WS_CTR_FC1 : WS_CTR_FC2);
+    g.total = ws[WS_NTILES] * NT;
+    g.per_xcd_items = (g.total + kXcds - 1) / kXcds;
+    g.xcd = blockIdx.x % kXcds;
+    g.gather = gather;
 
     const int tid = threadIdx.x;
     const int lane = moe_lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(tid / MOE_WAVE);
     const uint32_t smem_base = (uint32_t)(uintptr_t)(lds_u8_t*)smem;
-
-    const int total = ws[WS_NTILES] * NT;
-    // Items (tile, column tile) are cut into 8 contiguous ranges, one per XCD (workgroup w
-    // runs on XCD w % 8), so the items in flight on an XCD share A rows and B rows in its
-    // L2.  Workgroups take items from their XCD's range through an atomic counter (in order,
-    // self-balancing); a workgroup whose range is drained helps the others.
-    const int xcd = blockIdx.x % kXcds;
-    const int per_xcd_items = (total + kXcds - 1) / kXcds;
-
     // A copy fills one 8-row segment: lane j writes physical chunk j%8 of segment row j/8 and
     // so fetches the logical chunk stored there.  This wave's segments all have the parity of
     // w, which is the only part of the segment index that enters the swizzle.
     const int seg_row = lane >> 3;
     const int seg_lchunk = swz_chunk((wave & 1) * 8 + seg_row, lane & 7);
 
-    int q = 0;  // queues tried: own XCD first, then the others in turn
+    Queue qs{0, 0};
+    Item cur;
+    decode_step<kSwiGLU, kGather>(0, cur, g, qs, &item_s, tid, wave, seg_row, seg_lchunk);
+    decode_step<kSwiGLU, kGather>(1, cur, g, qs, &item_s, tid, wave, seg_row, seg_lchunk);
+    __syncthreads();
+    for (int s = 2; s < 6; ++s) decode_step<kSwiGLU, kGather>(s, cur, g, qs, &item_s, tid, wave, seg_row, seg_lchunk);
+    issue_prologue<kSwiGLU, kGather>(g, cur, smem_base, wave, seg_row, seg_lchunk * 16u);
+
     for (;;) {
-        if (tid == 0) {
-            int got = -1;
-            for (; q < kXcds; ++q) {
-                const int x = (xcd + q) % kXcds;
-                const int k = atomicAdd(&ctr[x], 1);
-                const int it = x * per_xcd_items + k;
-                if (k < per_xcd_items && it < total) {
-                    got = it;
-                    break;
-                }
-            }
-            item_s = got;
-        }
-        __syncthreads();
-        const int it = item_s;
-        if (it < 0) break;
-        // item -> (tile, column tile): the expert's items [ts * NT, (ts + cnt) * NT) in groups
-        // of kGroupTiles tiles, column-tile-major inside a group
-        const int32_t* tg = tiles + TILE_INTS * (it / NT);
-        const int ts = tg[5], cnt = tg[6];
-        const int local = it - ts * NT;
-        const int grp = local / (kGroupTiles * NT);
-        const int r = local - grp * (kGroupTiles * NT);
-        const int ct = cnt - grp * kGroupTiles < kGroupTiles ? cnt - grp * kGroupTiles : kGroupTiles;
-        const int nt = r / ct;
-        const int t = ts + grp * kGroupTiles + (r - nt * ct);
-        const int32_t* tl = tiles + TILE_INTS * t;
-        const int l = tl[0];
-        const int h_row0[2] = {tl[1], tl[3]};
-        const int h_rows[2] = {tl[2], tl[4]};
-        const uint16_t* Bexp = B + (int64_t)l * b_expert_stride;
-        if (h_rows[1] > 0)
-            gemm_item<kSwiGLU, 256>(A, a_rows, Kdim, Bexp, b_rows, C, ldc, n_cols, I, nt, h_row0,
-                                    h_rows, smem, smem_base, wave, lane, seg_row, seg_lchunk,
-                                    gather);
-        else if (h_rows[0] > 64)
-            gemm_item<kSwiGLU, 128>(A, a_rows, Kdim, Bexp, b_rows, C, ldc, n_cols, I, nt, h_row0,
-                                    h_rows, smem, smem_base, wave, lane, seg_row, seg_lchunk,
-                                    gather);
+        const int rows_a = __builtin_amdgcn_readfirstlane(cur.rows_a);
+        if (rows_a == 0) break;
+        Item nxt;
+        if (rows_a == 256)
+            gemm_item<kSwiGLU, kGather, 256>(g, cur, nxt, qs, &item_s, smem, smem_base, tid, wave, lane,
+                                    seg_row, seg_lchunk);
+        else if (rows_a == 128)
+            gemm_item<kSwiGLU, kGather, 128>(g, cur, nxt, qs, &item_s, smem, smem_base, tid, wave, lane,
+                                    seg_row, seg_lchunk);
         else
-            gemm_item<kSwiGLU, 64>(A, a_rows, Kdim, Bexp, b_rows, C, ldc, n_cols, I, nt, h_row0,
-                                   h_rows, smem, smem_base, wave, lane, seg_row, seg_lchunk,
-                                    gather);
-        __syncthreads();  // everyone has read item_s before thread 0 takes the next item
+            gemm_item<kSwiGLU, kGather, 64>(g, cur, nxt, qs, &item_s, smem, smem_base, tid, wave, lane,
+                                   seg_row, seg_lchunk);
+        cur = nxt;
     }
     // the last workgroup out clears this GEMM's counters so the kernel can run again
     if (tid == 0) {
         int32_t* done = ws + (kSwiGLU ? WS_DONE_FC1 : WS_DONE_FC2);
         if (atomicAdd(done, 1) == (int)gridDim.x - 1) {
-            for (int x = 0; x < kXcds; ++x) atomicExch(&ctr[x], 0);
+            for (int x = 0; x < kXcds; ++x) atomicExch(&g.ctr[x], 0);
             atomicExch(done, 0);
         }
     }
@@ -720,10 +940,16 @@ hipError_t moe_launch_ffn_fc1(const void* a, const void* w1, moe_dtype_t dt, int
             (int64_t)2 * I * H, I, static_cast<float*>(act), I, I, blocks, n_blocks, max_blocks);
         return hipGetLastError();
     }
-    ffn_bf16_kernel<true><<<persistent_grid(), kThreads, 0, stream>>>(
-        static_cast<const uint16_t*>(a), a_rows, H, static_cast<const uint16_t*>(w1),
-        (int64_t)2 * I * H, 2 * I, static_cast<uint16_t*>(act), I, I, I,
-        (I + BN / 2 - 1) / (BN / 2), max_blocks, ws, gather);
+    if (gather)
+        ffn_bf16_kernel<true, true><<<persistent_grid(), kThreads, 0, stream>>>(
+            static_cast<const uint16_t*>(a), a_rows, H, static_cast<const uint16_t*>(w1),
+            (int64_t)2 * I * H, 2 * I, static_cast<uint16_t*>(act), I, I, I,
+            (I + BN / 2 - 1) / (BN / 2), max_blocks, ws, gather);
+    else
+        ffn_bf16_kernel<true, false><<<persistent_grid(), kThreads, 0, stream>>>(
+            static_cast<const uint16_t*>(a), a_rows, H, static_cast<const uint16_t*>(w1),
+            (int64_t)2 * I * H, 2 * I, static_cast<uint16_t*>(act), I, I, I,
+            (I + BN / 2 - 1) / (BN / 2), max_blocks, ws, nullptr);
     return hipGetLastError();
 }
 
@@ -739,7 +965,7 @@ hipError_t moe_launch_ffn_fc2(const void* act, const void* w2, moe_dtype_t dt, i
             (int64_t)H * I, I, static_cast<float*>(yp), H, H, blocks, n_blocks, max_blocks);
         return hipGetLastError();
     }
-    ffn_bf16_kernel<false><<<persistent_grid(), kThreads, 0, stream>>>(
+    ffn_bf16_kernel<false, false><<<persistent_grid(), kThreads, 0, stream>>>(
         static_cast<const uint16_t*>(act), max_rows, I, static_cast<const uint16_t*>(w2),
         (int64_t)H * I, H, static_cast<uint16_t*>(yp), H, H, I, (H + BN - 1) / BN, max_blocks,
         ws, nullptr);
