@@ -692,11 +692,11 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& g, const Item& cur_in,
     issue_prologue<kSwiGLU, kGather>(g, nxt, smem_base, wave, seg_row, seg_lchunk * 16u);
 
     // epilogue: acc[i][j][4c + e] = C[tile row wrow + i*32 + lane%32][col + 8c + 4(lane/32) + e].
-    // Lanes l and l + 32 hold one row; after an exchange of half their packed values, lane l
-    // holds columns 0..15 and lane l + 32 columns 16..31 of each 32-column block, stored as
-    // two 16-byte pieces.
+    // Lanes l and l + 32 hold one row.  One v_permlane32_swap per pair of packed registers
+    // (groups c and c + 2) leaves lane l with columns 0..15 and lane l + 32 with columns
+    // 16..31 of each 32-column block, each as two 16-byte pieces in column order.
     if (active) {
-        const bool hi = lane >= 32;
+        const int hi16 = lane >= 32 ? 16 : 0;
 #pragma unroll
         for (int i = 0; i < RB; ++i) {
             const int tr = wrow + i * 32 + (lane & 31);
@@ -727,15 +727,17 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& g, const Item& cur_in,
                     pk[c][0] = pack_bf16x2(v[0], v[1]);
                     pk[c][1] = pack_bf16x2(v[2], v[3]);
                 }
-                // lane < 32 keeps groups 0, 1 and takes its partner's; lane >= 32 keeps 2, 3
-                uint32_t mine[2][2], theirs[2][2];
+                // swap(x, y) exchanges lanes 32..63 of x with lanes 0..31 of y: afterwards x
+                // holds (lane l: own group c; lane l + 32: lane l's group c + 2) and y holds
+                // (lane l: lane l + 32's group c; lane l + 32: own group c + 2)
+                uint32_t xs[2][2], ys[2][2];
 #pragma unroll
                 for (int c = 0; c < 2; ++c)
 #pragma unroll
                     for (int s = 0; s < 2; ++s) {
-                        const uint32_t send = hi ? pk[c][s] : pk[c + 2][s];
-                        mine[c][s] = hi ? pk[c + 2][s] : pk[c][s];
-                        theirs[c][s] = (uint32_t)__shfl_xor((int)send, 32, MOE_WAVE);
+                        const auto r = __builtin_amdgcn_permlane32_swap(pk[c][s], pk[c + 2][s], false, false);
+                        xs[c][s] = r[0];
+                        ys[c][s] = r[1];
                     }
                 const int col0 = kSwiGLU ? cur.nt * (BN / 2) + wn * 32
                                          : cur.nt * BN + wn * 64 + j * 32;
@@ -743,12 +745,11 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& g, const Item& cur_in,
 #pragma unroll
                     for (int c = 0; c < 2; ++c) {
                         uint4 o;
-                        if (hi) {  // columns 16 + 8c .. : partner's 4, then own 4
-                            o.x = theirs[c][0]; o.y = theirs[c][1]; o.z = mine[c][0]; o.w = mine[c][1];
-                        } else {   // columns 8c .. : own 4, then partner's 4
-                            o.x = mine[c][0]; o.y = mine[c][1]; o.z = theirs[c][0]; o.w = theirs[c][1];
-                        }
-                        *reinterpret_cast<uint4*>(crow + col0 + (hi ? 16 : 0) + 8 * c) = o;
+                        o.x = xs[c][0];
+                        o.y = xs[c][1];
+                        o.z = ys[c][0];
+                        o.w = ys[c][1];
+                        *reinterpret_cast<uint4*>(crow + col0 + hi16 + 8 * c) = o;
                     }
                 }
             }
