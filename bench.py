@@ -141,13 +141,20 @@ def ffn_traffic(workload: str):
     """HBM bytes per FC1 launch from committed rocprofv3 counter runs, if they were taken on
     the current FC1 kernel source; else None."""
     path = os.path.join(ROOT, "profiles", f"fc1_{workload}_traffic.json")
-    src = os.path.join(ROOT, "mixture_experts_routed_router_amd", "csrc", "ffn.hip")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("ffn_hip_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+    if rec.get("ffn_source_sha256") != ffn_source_sha256():
         return None
     return rec.get("bytes_per_launch")
+
+
+def ffn_source_sha256() -> str:
+    """SHA-256 over the FC1 kernel's sources (ffn.hip, then the staging header it includes)."""
+    h = hashlib.sha256()
+    for f in ("ffn.hip", "moe_lds.h"):
+        h.update(open(os.path.join(ROOT, "mixture_experts_routed_router_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
 
 
 def cpu_baseline(w, skew, T_s, target_s=12.0):
@@ -251,15 +258,19 @@ def main():
     combine_bytes = (N + w.T) * w.H * eb + 8 * w.T * w.K
     traffic = ffn_traffic(w.name)
     t_roof, touched, wbytes, bound = ffn_roofline(w, loc.tolist(), eb)
+    fc1_kernel = ("ffn_bf16_kernel<true, false>, the FC1 GEMM of moe_expert_ffn_fc1 (gate/up + SwiGLU)"
+                  if args.materialize else
+                  "ffn_bf16_kernel<true, true>, the FC1 GEMM of moe_expert_ffn_fc1_gather (gate/up + SwiGLU, "
+                  "rows gathered from x)")
     if bound == "hbm":
         # weight-read bound (decode): FC1 streams the gate/up weights of every touched expert
         fc1_bytes = wbytes * 2.0 / 3.0
-        roofline = {"kernel": "ffn_bf16_kernel<true>, the FC1 GEMM of moe_expert_ffn_fc1 (gate/up + SwiGLU)",
+        roofline = {"kernel": fc1_kernel,
                     "bound": "hbm", "achieved": round(fc1_bytes / fc1_s / 1e9, 1),
                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": round(fc1_bytes / fc1_s / 1e9 / PEAK_HBM_GBS, 4), "traffic": traffic}
     else:
-        roofline = {"kernel": "ffn_bf16_kernel<true>, the FC1 GEMM of moe_expert_ffn_fc1 (gate/up + SwiGLU)",
+        roofline = {"kernel": fc1_kernel,
                     "bound": "mfma", "achieved": round(achieved, 1),
                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
