@@ -390,6 +390,287 @@ done:
     return rc;
 }
 
+/* ------------------------------------------------------- block-granular plan --- */
+
+/* The block-granular planner of MegaFlux ([MF §3.1 "Problem formulation", "Bounded greedy
+ * search"; App. A.1 "Candidate construction", "Refinement"]), over the same P logical ranks
+ * and expert ownership as oracle_plan (rank r owns local experts r*G .. r*G + G - 1).
+ *
+ * Expert l's rows, in their stable order, are cut into b_l = ceil(n_l / beta) blocks of
+ * beta rows (the last may be partial); load L_r counts blocks; tau = ceil(sum b_l / P).
+ * Four searches start from the no-replica assignment q[l][owner(l)] = b_l.  A search runs
+ * rounds; a round visits every rank that is over tau at its start once, in donor-priority
+ * order (overload L_r - tau, or the rank's largest remaining home-expert block count;
+ * larger first, lower rank on ties).  A visit scans the donor's home experts with blocks
+ * left at home, most blocks first (lower id on ties), and ends when the donor is at tau or
+ * the scan is done.  For each expert it moves single blocks while the donor is over tau and
+ * the expert has blocks at home: to the least-loaded rank that already holds a copy of the
+ * expert and is under tau, else to the least-loaded rank under tau with a free replica slot
+ * (fewer than s copies of foreign experts), opening a new copy there -- in "one copy" mode
+ * at most one new copy per expert per round, in "many copies" mode any number; ties go to
+ * the lower rank.  The expert's fan-out stops when no receiver qualifies.  A search ends
+ * after s + 2 rounds or a round that moved nothing.  Candidate order: (overload, one copy),
+ * (overload, many), (home load, one copy), (home load, many).
+ *
+ * The candidate with the smallest maximum load wins, then the fewest replicas, then the
+ * first in that order.  Refinement, at that maximum Lmax: replicas (copies of an expert on a
+ * rank that does not own it), in increasing allocation at pass entry (then expert, then
+ * rank), are removed when their whole allocation fits under Lmax on the owner or else on
+ * the least-loaded other copy; then, at most sum b_l times, one block moves from the
+ * most-loaded rank to the least-loaded rank (lowest rank on ties) while their loads differ
+ * by more than one and both hold a copy of some expert with blocks on the former (the
+ * owner always holds its experts; lowest such expert).
+ *
+ * Outputs as oracle_plan: q[l*P + r] = rows of expert l on rank r (the ranks holding l take
+ * consecutive runs of its blocks in ascending rank order, so only the expert's last block is
+ * partial); moves = one entry (owner, rank, expert, rows) per replica, expert then rank
+ * ascending; blocks = (rank, expert, first row, rows), rank by rank, then expert by expert,
+ * in block order.  Pinned by hand-worked plans (tests/golden/megaflux_plan_cases.json),
+ * closed forms (no budget or a balanced start keep the no-replica assignment; an ample
+ * budget reaches tau) and invariants (conservation, budget, one partial block per expert,
+ * the refinement never raising the maximum). */
+static void bp_search(const int64_t* b, int E_loc, int P, int G, int64_t tau, int s,
+                      int by_overload, int many, int64_t* q, int64_t* L, int* repl,
+                      unsigned char* opened, unsigned char* visited, int64_t* key, int* order) {
+    for (int64_t i = 0; i < (int64_t)E_loc * P; ++i) q[i] = 0;
+    for (int r = 0; r < P; ++r) { L[r] = 0; repl[r] = 0; }
+    for (int l = 0; l < E_loc; ++l) {
+        q[(int64_t)l * P + l / G] = b[l];
+        L[l / G] += b[l];
+    }
+    for (int round = 0; round < s + 2; ++round) {
+        int moved = 0;
+        for (int l = 0; l < E_loc; ++l) opened[l] = 0;
+        for (int r = 0; r < P; ++r) {
+            visited[r] = 0;
+            key[r] = -1;
+            if (L[r] > tau) {
+                if (by_overload) {
+                    key[r] = L[r] - tau;
+                } else {
+                    key[r] = 0;
+                    for (int l = r * G; l < (r + 1) * G; ++l)
+                        if (q[(int64_t)l * P + r] > key[r]) key[r] = q[(int64_t)l * P + r];
+                }
+            }
+        }
+        for (;;) {
+            int d = -1;
+            for (int r = 0; r < P; ++r)
+                if (!visited[r] && key[r] >= 0 && (d < 0 || key[r] > key[d])) d = r;
+            if (d < 0) break;
+            visited[d] = 1;
+            if (L[d] <= tau) continue;
+            /* the scan order is fixed at the start of the visit */
+            int ns = 0;
+            for (int l = d * G; l < (d + 1) * G; ++l)
+                if (q[(int64_t)l * P + d] > 0) order[ns++] = l;
+            for (int i = 1; i < ns; ++i) {  /* insertion sort: most blocks first, then lower id */
+                int v = order[i], j = i;
+                while (j > 0 && q[(int64_t)order[j - 1] * P + d] < q[(int64_t)v * P + d]) {
+                    order[j] = order[j - 1];
+                    --j;
+                }
+                order[j] = v;
+            }
+            for (int i = 0; i < ns && L[d] > tau; ++i) {
+                const int l = order[i];
+                int64_t* ql = q + (int64_t)l * P;
+                while (ql[d] > 0 && L[d] > tau) {
+                    int rcv = -1;
+                    for (int r = 0; r < P; ++r)
+                        if (r != d && ql[r] > 0 && L[r] < tau && (rcv < 0 || L[r] < L[rcv])) rcv = r;
+                    if (rcv < 0 && (many || !opened[l])) {
+                        for (int r = 0; r < P; ++r)
+                            if (r != d && ql[r] == 0 && repl[r] < s && L[r] < tau &&
+                                (rcv < 0 || L[r] < L[rcv]))
+                                rcv = r;
+                        if (rcv >= 0) {
+                            repl[rcv] += 1;
+                            opened[l] = 1;
+                        }
+                    }
+                    if (rcv < 0) break;
+                    ql[d] -= 1;
+                    ql[rcv] += 1;
+                    L[d] -= 1;
+                    L[rcv] += 1;
+                    moved = 1;
+                }
+            }
+        }
+        if (!moved) break;
+    }
+}
+
+static int64_t bp_max(const int64_t* L, int P) {
+    int64_t m = L[0];
+    for (int r = 1; r < P; ++r) if (L[r] > m) m = L[r];
+    return m;
+}
+
+static int64_t bp_replicas(const int64_t* q, int E_loc, int P, int G) {
+    int64_t n = 0;
+    for (int l = 0; l < E_loc; ++l)
+        for (int r = 0; r < P; ++r)
+            if (r != l / G && q[(int64_t)l * P + r] > 0) ++n;
+    return n;
+}
+
+static int bp_key_cmp(const void* a, const void* b) {
+    const int64_t* x = (const int64_t*)a;
+    const int64_t* y = (const int64_t*)b;
+    for (int i = 0; i < 3; ++i)
+        if (x[i] != y[i]) return x[i] < y[i] ? -1 : 1;
+    return 0;
+}
+
+int oracle_plan_blocks(const int32_t* counts, int E, int begin, int stride, int E_loc, int P,
+                       int beta, int s, int32_t* q_out, int32_t* moves, int32_t* n_moves,
+                       int max_moves, int32_t* blocks, int32_t* n_blocks, int max_blocks) {
+    if (E_loc < 1 || P < 1 || E_loc % P != 0 || beta < 1 || stride < 1 || s < 0) return ORACLE_ERR_ARG;
+    if (begin < 0 || begin + (int64_t)(E_loc - 1) * stride >= E) return ORACLE_ERR_ARG;
+    const int G = E_loc / P;
+    const int64_t EP = (int64_t)E_loc * P;
+    int rc = ORACLE_OK;
+    int64_t* n = (int64_t*)calloc((size_t)E_loc, sizeof(int64_t));
+    int64_t* b = (int64_t*)calloc((size_t)E_loc, sizeof(int64_t));
+    int64_t* q = (int64_t*)calloc((size_t)(4 * EP), sizeof(int64_t));
+    int64_t* L = (int64_t*)calloc((size_t)(4 * P), sizeof(int64_t));
+    int* repl = (int*)calloc((size_t)(4 * P), sizeof(int));
+    unsigned char* opened = (unsigned char*)calloc((size_t)E_loc, 1);
+    unsigned char* visited = (unsigned char*)calloc((size_t)P, 1);
+    int64_t* key = (int64_t*)calloc((size_t)P, sizeof(int64_t));
+    int* order = (int*)calloc((size_t)(G > 0 ? G : 1), sizeof(int));
+    int64_t* rep = (int64_t*)calloc((size_t)(3 * EP), sizeof(int64_t));
+    int32_t* off = (int32_t*)calloc((size_t)E_loc + 1, sizeof(int32_t));
+    if (!n || !b || !q || !L || !repl || !opened || !visited || !key || !order || !rep || !off) {
+        rc = ORACLE_ERR_DATA;
+        goto done;
+    }
+
+    int64_t sum_b = 0;
+    for (int l = 0; l < E_loc; ++l) {
+        n[l] = counts[begin + l * stride];
+        b[l] = (n[l] + beta - 1) / beta;
+        sum_b += b[l];
+    }
+    const int64_t tau = (sum_b + P - 1) / P;
+
+    /* the four searches */
+    int best = 0;
+    int64_t best_max = 0, best_rep = 0;
+    for (int c = 0; c < 4; ++c) {
+        bp_search(b, E_loc, P, G, tau, s, c < 2, c & 1, q + c * EP, L + c * P, repl + c * P,
+                  opened, visited, key, order);
+        const int64_t m = bp_max(L + c * P, P), nr = bp_replicas(q + c * EP, E_loc, P, G);
+        if (c == 0 || m < best_max || (m == best_max && nr < best_rep)) {
+            best = c;
+            best_max = m;
+            best_rep = nr;
+        }
+    }
+    int64_t* qb = q + best * EP;
+    int64_t* Lb = L + best * P;
+    const int64_t Lmax = best_max;
+
+    /* refinement 1: remove replicas whose allocation fits on the owner or another copy */
+    int64_t nrep = 0;
+    for (int l = 0; l < E_loc; ++l)
+        for (int r = 0; r < P; ++r)
+            if (r != l / G && qb[(int64_t)l * P + r] > 0) {
+                rep[3 * nrep + 0] = qb[(int64_t)l * P + r];
+                rep[3 * nrep + 1] = l;
+                rep[3 * nrep + 2] = r;
+                ++nrep;
+            }
+    qsort(rep, (size_t)nrep, 3 * sizeof(int64_t), bp_key_cmp);
+    for (int64_t i = 0; i < nrep; ++i) {
+        const int l = (int)rep[3 * i + 1], r = (int)rep[3 * i + 2], h = l / G;
+        int64_t* ql = qb + (int64_t)l * P;
+        const int64_t a = ql[r];
+        if (a == 0) continue;
+        int tgt = -1;
+        if (Lb[h] + a <= Lmax) {
+            tgt = h;
+        } else {
+            for (int r2 = 0; r2 < P; ++r2)
+                if (r2 != r && r2 != h && ql[r2] > 0 && Lb[r2] + a <= Lmax &&
+                    (tgt < 0 || Lb[r2] < Lb[tgt]))
+                    tgt = r2;
+        }
+        if (tgt >= 0) {
+            ql[tgt] += a;
+            Lb[tgt] += a;
+            ql[r] = 0;
+            Lb[r] -= a;
+        }
+    }
+    /* refinement 2: single blocks from the most- to the least-loaded rank */
+    for (int64_t it = 0; it < sum_b; ++it) {
+        int rmax = 0, rmin = 0;
+        for (int r = 1; r < P; ++r) {
+            if (Lb[r] > Lb[rmax]) rmax = r;
+            if (Lb[r] < Lb[rmin]) rmin = r;
+        }
+        if (Lb[rmax] - Lb[rmin] <= 1) break;
+        int lm = -1;
+        for (int l = 0; l < E_loc && lm < 0; ++l)
+            if (qb[(int64_t)l * P + rmax] > 0 && (rmin == l / G || qb[(int64_t)l * P + rmin] > 0)) lm = l;
+        if (lm < 0) break;
+        qb[(int64_t)lm * P + rmax] -= 1;
+        qb[(int64_t)lm * P + rmin] += 1;
+        Lb[rmax] -= 1;
+        Lb[rmin] += 1;
+    }
+
+    /* rows per (expert, rank), replicas, and the block table */
+    padded_offsets(counts, begin, stride, E_loc, beta, off);
+    int nm = 0;
+    for (int l = 0; l < E_loc; ++l) {
+        int64_t pre = 0;
+        for (int r = 0; r < P; ++r) {
+            const int64_t k = qb[(int64_t)l * P + r];
+            int64_t lo = pre * beta, hi = (pre + k) * beta;
+            if (lo > n[l]) lo = n[l];
+            if (hi > n[l]) hi = n[l];
+            q_out[(int64_t)l * P + r] = (int32_t)(hi - lo);
+            if (k > 0 && r != l / G) {
+                if (nm >= max_moves) { rc = ORACLE_ERR_DATA; goto done; }
+                moves[4 * nm + 0] = l / G;
+                moves[4 * nm + 1] = r;
+                moves[4 * nm + 2] = l;
+                moves[4 * nm + 3] = (int32_t)(hi - lo);
+                ++nm;
+            }
+            pre += k;
+        }
+    }
+    *n_moves = nm;
+    int nb = 0;
+    for (int r = 0; r < P; ++r) {
+        for (int l = 0; l < E_loc; ++l) {
+            int64_t pre = 0;
+            for (int r2 = 0; r2 < r; ++r2) pre += qb[(int64_t)l * P + r2];
+            const int64_t k = qb[(int64_t)l * P + r];
+            for (int64_t j = pre; j < pre + k; ++j) {
+                if (nb >= max_blocks) { rc = ORACLE_ERR_DATA; goto done; }
+                const int64_t rows = n[l] - j * beta < beta ? n[l] - j * beta : beta;
+                blocks[4 * nb + 0] = r;
+                blocks[4 * nb + 1] = l;
+                blocks[4 * nb + 2] = (int32_t)(off[l] + j * beta);
+                blocks[4 * nb + 3] = (int32_t)rows;
+                ++nb;
+            }
+        }
+    }
+    *n_blocks = nb;
+done:
+    free(n); free(b); free(q); free(L); free(repl); free(opened); free(visited); free(key);
+    free(order); free(rep); free(off);
+    return rc;
+}
+
 /* ------------------------------------------------------------------- expert FFN --- */
 
 /* SwiGLU expert FFN for a list of rows.  [MF §2.1, §4.1]: FC1 produces gate and up

@@ -10,6 +10,7 @@ route  -- top-k by (larger logit, smaller id), softmax weights renormalised over
 router_logits -- linear router scores x . w_r^T in double, rounded to float32;
 permute -- stable expert-major order by flat index, beta-aligned segments;
 plan   -- the greedy donor->receiver balance to exact per-rank capacity, then <=beta blocks;
+plan_blocks -- the block-granular replica planner: four greedy searches, the best, refined;
 ffn    -- SwiGLU expert FFN in double with bf16 rounding at act and yp;
 combine -- routing-weight sum in double, k ascending.
 """
@@ -49,7 +50,8 @@ def _load():
         lib.oracle_double_to_bf16.argtypes = [ctypes.c_double]
         lib.oracle_num_threads.restype = ctypes.c_int
         for name in ("oracle_route", "oracle_route_ref", "oracle_router_logits", "oracle_permute",
-                     "oracle_plan", "oracle_ffn_rows", "oracle_ffn_blocks", "oracle_combine"):
+                     "oracle_plan", "oracle_plan_blocks", "oracle_ffn_rows", "oracle_ffn_blocks",
+                     "oracle_combine"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -166,6 +168,25 @@ def plan(counts: np.ndarray, E: int, begin: int, stride: int, E_loc: int, P: int
     _check(_load().oracle_plan(_p(counts), E, begin, stride, E_loc, P, beta, _p(q), _p(moves),
                                ctypes.byref(nm), max_moves, _p(blocks), ctypes.byref(nb),
                                max(max_blocks, 1)), "plan")
+    return q, moves[: nm.value].copy(), blocks[: nb.value].copy()
+
+
+def plan_blocks(counts: np.ndarray, E: int, begin: int, stride: int, E_loc: int, P: int,
+                beta: int, s: int):
+    """Block-granular replica plan with replica budget s per rank.  -> q [E_loc, P] rows,
+    moves [n_replicas, 4] (owner, rank, expert, rows), blocks [n_blocks, 4]."""
+    counts = np.ascontiguousarray(counts, dtype=np.int32)
+    N = int(sum(int(counts[begin + l * stride]) for l in range(E_loc)))
+    max_moves = E_loc * P
+    max_blocks = (N + beta - 1) // beta + E_loc * P
+    q = np.empty((E_loc, P), np.int32)
+    moves = np.empty((max_moves, 4), np.int32)
+    blocks = np.empty((max(max_blocks, 1), 4), np.int32)
+    nm = ctypes.c_int32(0)
+    nb = ctypes.c_int32(0)
+    _check(_load().oracle_plan_blocks(_p(counts), E, begin, stride, E_loc, P, beta, s, _p(q),
+                                      _p(moves), ctypes.byref(nm), max_moves, _p(blocks),
+                                      ctypes.byref(nb), max(max_blocks, 1)), "plan_blocks")
     return q, moves[: nm.value].copy(), blocks[: nb.value].copy()
 
 

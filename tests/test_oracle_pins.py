@@ -2,7 +2,8 @@
 
 Each test checks the oracle against something other than itself: a library routine on a
 special case (stable sort, torch.softmax / torch.matmul in float64), a closed form, an
-invariant the pages state, or a plan worked out by hand (tests/golden/plan_cases.json).
+invariant the pages state, or a plan worked out by hand (tests/golden/plan_cases.json,
+tests/golden/megaflux_plan_cases.json).
 """
 import json
 import math
@@ -434,3 +435,106 @@ def test_combine_k1_and_nonlocal(oracle_mod):
     assert np.all(oracle_mod.bf16_to_f64(out[0]) == 0)
     ref = 0.5 * oracle_mod.bf16_to_f64(yp[1])
     assert np.array_equal(oracle_mod.bf16_to_f64(out[1]), ref)  # exact: scaling by 1/2
+
+
+# ------------------------------------------------------------ block-granular plan ---
+
+def _check_plan_blocks(counts, E, begin, stride, E_loc, P, beta, s, q, moves, blocks):
+    """Invariants of the block-granular plan; returns the per-rank block loads."""
+    n = np.array([counts[begin + l * stride] for l in range(E_loc)], np.int64)
+    G = E_loc // P
+    b = (n + beta - 1) // beta
+    tau = -(-int(b.sum()) // P)
+    # selections preserved: every expert's rows are all assigned
+    assert np.array_equal(q.sum(1), n)
+    assert np.all(q >= 0)
+    # blocks: the expert's stable order cut into beta-row blocks, each block on one rank,
+    # ranks taking consecutive runs in ascending rank order, rank-major table
+    off = np.concatenate([[0], np.cumsum(b * beta)])
+    seen = np.zeros(int(off[-1]), np.int64)
+    load = np.zeros(P, np.int64)
+    per = np.zeros((E_loc, P), np.int64)
+    last_rank = {}
+    prev = (-1, -1, -1)
+    for r, l, b0, m in blocks.tolist():
+        assert (r, l, b0) > prev
+        prev = (r, l, b0)
+        j = (b0 - off[l]) // beta
+        assert b0 == off[l] + j * beta and 0 <= j < b[l]
+        assert m == min(beta, n[l] - j * beta)  # only an expert's last block is partial
+        assert last_rank.get(l, -1) <= r
+        last_rank[l] = r
+        seen[b0:b0 + m] += 1
+        load[r] += 1
+        per[l, r] += m
+    for l in range(E_loc):
+        assert np.all(seen[off[l]:off[l] + n[l]] == 1)
+    assert np.array_equal(per, q)
+    # replicas: at most s foreign experts per rank; moves list them (owner, rank, expert, rows)
+    rep = [(l // G, r, l, int(q[l, r])) for l in range(E_loc) for r in range(P)
+           if r != l // G and q[l, r] > 0]
+    assert moves.tolist() == [list(t) for t in rep]
+    for r in range(P):
+        assert sum(1 for (_, rr, _, _) in rep if rr == r) <= s
+    # the busiest rank: at least tau blocks, never more than without replicas
+    home = np.array([b[r * G:(r + 1) * G].sum() for r in range(P)])
+    assert tau <= load.max() <= home.max()
+    return load, tau, home
+
+
+def test_plan_blocks_golden_hand_worked(oracle_mod):
+    cases = json.load(open(os.path.join(GOLDEN, "megaflux_plan_cases.json")))["cases"]
+    for c in cases:
+        cnt = np.array(c["counts"], np.int32)
+        E = len(cnt)
+        q, moves, blocks = oracle_mod.plan_blocks(cnt, E, 0, 1, E, c["P"], c["beta"], c["s"])
+        assert q.tolist() == c["q"], c["name"]
+        assert moves.tolist() == c["moves"], c["name"]
+        if "blocks" in c:
+            assert blocks.tolist() == c["blocks"], c["name"]
+        _check_plan_blocks(cnt, E, 0, 1, E, c["P"], c["beta"], c["s"], q, moves, blocks)
+
+
+def test_plan_blocks_closed_forms(oracle_mod):
+    """No replica budget, one rank, or a start at or under tau everywhere: the no-replica
+    assignment.  A budget of E_loc replicas per rank: the busiest rank holds exactly tau
+    blocks (the many-copies search fills every receiver to tau in its first round)."""
+    rng = np.random.default_rng(11)
+    for trial in range(60):
+        P = int(rng.choice([2, 3, 4, 8]))
+        G = int(rng.integers(1, 5))
+        E = P * G
+        beta = int(rng.choice([1, 2, 4, 16]))
+        cnt = rng.zipf(1.6, size=E).astype(np.int64) * int(rng.integers(1, 20))
+        cnt = np.minimum(cnt, 5000).astype(np.int32)
+        b = (cnt.astype(np.int64) + beta - 1) // beta
+        home = np.array([b[r * G:(r + 1) * G].sum() for r in range(P)])
+        tau = -(-int(b.sum()) // P)
+        q0, m0, bl0 = oracle_mod.plan_blocks(cnt, E, 0, 1, E, P, beta, 0)
+        load0, _, _ = _check_plan_blocks(cnt, E, 0, 1, E, P, beta, 0, q0, m0, bl0)
+        assert len(m0) == 0 and np.array_equal(load0, home)
+        q1, m1, bl1 = oracle_mod.plan_blocks(cnt, E, 0, 1, E, P, beta, E)
+        load1, _, _ = _check_plan_blocks(cnt, E, 0, 1, E, P, beta, E, q1, m1, bl1)
+        assert load1.max() == tau, (trial, load1, tau)
+        if home.max() <= tau:
+            assert len(m1) == 0
+    # one rank
+    cnt = np.array([7, 0, 3], np.int32)
+    q, m, bl = oracle_mod.plan_blocks(cnt, 3, 0, 1, 3, 1, 2, 4)
+    assert q[:, 0].tolist() == [7, 0, 3] and len(m) == 0
+
+
+@pytest.mark.parametrize("name", list(inputs.WORKLOADS))
+def test_plan_blocks_invariants_all_workloads(oracle_mod, name):
+    """Every workload and skew at the pages' budget s = E/(4P) (E = local experts here), and
+    at s = 0 and s = 2: the invariants; s = 0 keeps the no-replica loads."""
+    w = inputs.WORKLOADS[name]
+    for skew in w.skews:
+        _, _, counts = oracle_mod.route(inputs.make_logits(w, skew), w.K)
+        for s in (0, w.n_local // (4 * w.P), 2):
+            q, moves, blocks = oracle_mod.plan_blocks(counts, w.E, w.expert_begin,
+                                                      w.expert_stride, w.n_local, w.P, w.beta, s)
+            load, tau, home = _check_plan_blocks(counts, w.E, w.expert_begin, w.expert_stride,
+                                                 w.n_local, w.P, w.beta, s, q, moves, blocks)
+            if s == 0:
+                assert np.array_equal(load, home)
