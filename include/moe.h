@@ -7,7 +7,8 @@
  *                   moe_route_ref with a top-k_ref reference mass; moe_router_topk computes
  *                   the logits (linear router, bf16 MFMA) and fuses the top-k behind them
  *   moe_permute     dispatch permutation into expert-contiguous, beta-aligned row segments
- *   moe_plan        greedy skew-balancing plan over P logical rank partitions + block table
+ *   moe_plan        greedy skew-balancing plan over P logical rank partitions + block table;
+ *                   moe_plan_blocks: the block-granular replica plan instead, same outputs
  *   moe_expert_ffn  SwiGLU expert FFN over the block table (grouped GEMMs on bf16 MFMA);
  *                   moe_expert_ffn_gather reads the token rows of x directly
  *   moe_combine     routing-weight combine of each token's expert outputs
@@ -173,6 +174,42 @@ moe_status_t moe_plan(const int32_t* expert_counts, int E, int expert_begin,
                       int32_t* q, int32_t* moves, int32_t* n_moves, int max_moves,
                       int32_t* blocks, int32_t* n_blocks, int max_blocks,
                       int32_t* err_word, hipStream_t stream);
+
+/* Block-granular replica plan ([MF §3.1 "Bounded greedy search"; App. A.1]) over the same P
+ * logical ranks and ownership as moe_plan.  Local expert l's rows, in the stable order of
+ * moe_permute's segment, are cut into b_l = ceil(n_l / block_m) blocks (only the last may be
+ * partial); a rank's load counts blocks; tau = ceil(sum_l b_l / P).  Four greedy searches
+ * start from every block at its owner:
+ *   rounds: each round visits the ranks over tau at its start once, larger key first (lowest
+ *     rank on ties), key = load - tau (searches 0, 1) or the rank's largest home-expert block
+ *     count still at home (searches 2, 3); a visit scans the donor's home experts with blocks
+ *     at home, most blocks first (lowest id on ties), and ends when the donor is at tau;
+ *   single-block moves: each block of the expert goes to the least-loaded rank under tau that
+ *     already holds a copy (not the donor), else to the least-loaded rank under tau holding
+ *     fewer than replica_budget foreign copies, which opens a copy (searches 0 and 2: at most
+ *     one new copy per expert per round; 1 and 3: any number); ties to the lowest rank; the
+ *     expert's fan-out ends when it has no block at home or no rank qualifies;
+ *   a search ends after replica_budget + 2 rounds or a round that moved no block.
+ * The search with the smallest maximum load wins, then the fewest replicas, then the lowest
+ * index.  At that maximum M: replicas (copies on non-owners) are visited by allocation at
+ * pass entry, then expert, then rank, and each is removed if its blocks fit (load + blocks
+ * <= M) on the owner, else on the least-loaded other copy (lowest rank on ties); then, up to
+ * sum b_l times, while the most- and least-loaded ranks (lowest on ties) differ by more than
+ * one, one block of the lowest expert with blocks on the former and held by the latter (the
+ * owner always holds its experts) moves between them.
+ *   q        [E_loc, P] int32 out: rows of local expert l computed by rank r (the ranks
+ *            holding l take consecutive runs of its blocks in ascending rank order).
+ *   moves    [max_moves, 4] int32 out: (owner, rank, l, rows), one per replica, by expert then
+ *            rank; *n_moves (device int32) = count.
+ *   blocks   as moe_plan: (rank, l, first row, rows), by rank, then expert, then block.
+ *   err_word as moe_plan.
+ * Limits: P divides E_loc, 1 <= P <= 64, E_loc / P <= 64, E_loc <= 256, E_loc * P <= 4096,
+ * 0 <= replica_budget <= 65536 (the pages' setting is E_loc / (4 P)). */
+moe_status_t moe_plan_blocks(const int32_t* expert_counts, int E, int expert_begin,
+                             int expert_stride, int E_loc, int P, int block_m, int replica_budget,
+                             int32_t* q, int32_t* moves, int32_t* n_moves, int max_moves,
+                             int32_t* blocks, int32_t* n_blocks, int max_blocks,
+                             int32_t* err_word, hipStream_t stream);
 
 /* ------------------------------------------------------------------- expert FFN --- */
 

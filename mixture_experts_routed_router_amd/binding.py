@@ -49,6 +49,8 @@ _SIGNATURES = {
     "moe_expert_ffn_fc1_gather": (_i32, [_vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp, _vp,
                                          _i32, _vp, _i64, _vp, _i64, _vp]),
     "moe_expert_ffn_tile_schedule": (_i32, [_vp, _vp, _i32, _i32, _vp, _i64, _vp]),
+    "moe_plan_blocks": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32,
+                               _vp, _vp, _i32, _vp, _vp]),
     "moe_route_ref": (_i32, [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
     "moe_router_topk": (_i32, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
                                _vp]),
@@ -202,6 +204,19 @@ def moe_plan(expert_counts, E, expert_begin, expert_stride, E_loc, P, block_m, q
            "moe_plan")
 
 
+def moe_plan_blocks(expert_counts, E, expert_begin, expert_stride, E_loc, P, block_m,
+                    replica_budget, q, moves, n_moves, blocks, n_blocks, err_word=None,
+                    stream=None):
+    _check(lib().moe_plan_blocks(_ptr(expert_counts, torch.int32, "expert_counts"), E,
+                                 expert_begin, expert_stride, E_loc, P, block_m, replica_budget,
+                                 _ptr(q, torch.int32, "q"), _ptr(moves, torch.int32, "moves"),
+                                 _ptr(n_moves, torch.int32, "n_moves"), moves.shape[0],
+                                 _ptr(blocks, torch.int32, "blocks"),
+                                 _ptr(n_blocks, torch.int32, "n_blocks"), blocks.shape[0],
+                                 _ptr(err_word, torch.int32, "err_word"), _stream(stream)),
+           "moe_plan_blocks")
+
+
 def moe_expert_ffn(xp, w1, w2, blocks, n_blocks, act, yp, workspace, stream=None):
     E_loc, two_I, H = w1.shape
     I = two_I // 2
@@ -319,8 +334,16 @@ class RoutedExperts:
     """
 
     def __init__(self, T, H, E, K, I, P, dtype=torch.bfloat16, E_loc=None, expert_begin=0,
-                 expert_stride=1, block_m=128, renormalize=True, device="cuda", gather=False):
+                 expert_stride=1, block_m=128, renormalize=True, device="cuda", gather=False,
+                 planner="moonep", replica_budget=None):
         self.T, self.H, self.E, self.K, self.I, self.P = T, H, E, K, I, P
+        if planner not in ("moonep", "megaflux"):
+            raise MoeError(f"unknown planner {planner!r} (moonep or megaflux)")
+        # moonep: moe_plan (exact per-rank entry capacity); megaflux: moe_plan_blocks
+        # (block-granular replicas under a per-rank budget, E_loc / (4 P) by default)
+        self.planner = planner
+        self.replica_budget = (replica_budget if replica_budget is not None
+                               else (E_loc or E) // (4 * P))
         self.gather = gather  # FC1 reads x rows through row_token; xp is never written
         self.E_loc = E_loc or E
         self.begin, self.stride, self.block_m = expert_begin, expert_stride, block_m
@@ -361,6 +384,11 @@ class RoutedExperts:
                     self.workspace, stream)
 
     def plan(self, stream=None):
+        if self.planner == "megaflux":
+            moe_plan_blocks(self.counts, self.E, self.begin, self.stride, self.E_loc, self.P,
+                            self.block_m, self.replica_budget, self.q, self.moves, self.n_moves,
+                            self.blocks, self.n_blocks, self.err_word, stream)
+            return
         moe_plan(self.counts, self.E, self.begin, self.stride, self.E_loc, self.P, self.block_m,
                  self.q, self.moves, self.n_moves, self.blocks, self.n_blocks, self.err_word,
                  stream)

@@ -149,6 +149,23 @@ int64_t moe_ffn_workspace_elems(int max_blocks) {
     return moe_ffn_workspace_elems_impl(max_blocks);
 }
 
+moe_status_t moe_plan_blocks(const int32_t* expert_counts, int E, int expert_begin,
+                             int expert_stride, int E_loc, int P, int block_m, int replica_budget,
+                             int32_t* q, int32_t* moves, int32_t* n_moves, int max_moves,
+                             int32_t* blocks, int32_t* n_blocks, int max_blocks,
+                             int32_t* err_word, hipStream_t stream) {
+    if (!expert_counts || !q || !moves || !n_moves || !blocks || !n_blocks)
+        return MOE_ERR_INVALID;
+    if (!valid_local_set(E, expert_begin, expert_stride, E_loc) || P < 1 || E_loc % P != 0 ||
+        !valid_block_m(block_m) || max_moves < 0 || max_blocks < 1 || replica_budget < 0)
+        return MOE_ERR_INVALID;
+    if (P > 64 || E_loc / P > 64 || E_loc > 256 || E_loc * P > 4096 || replica_budget > 65536)
+        return MOE_ERR_UNSUPPORTED;
+    return launched(moe_launch_plan_blocks(expert_counts, expert_begin, expert_stride, E_loc, P,
+                                           block_m, replica_budget, q, moves, n_moves, max_moves,
+                                           blocks, n_blocks, max_blocks, err_word, stream));
+}
+
 moe_status_t moe_expert_ffn_tile_schedule(const int32_t* blocks, const int32_t* n_blocks,
                                           int max_blocks, int E_loc, int32_t* workspace,
                                           int64_t workspace_elems, hipStream_t stream) {

@@ -29,6 +29,10 @@ hipError_t moe_launch_plan(const int32_t* counts, int begin, int stride, int E_l
 
 int64_t moe_ffn_workspace_elems_impl(int max_blocks);
 
+hipError_t moe_launch_plan_blocks(const int32_t* counts, int begin, int stride, int E_loc, int P,
+                                  int beta, int s, int32_t* q, int32_t* moves, int32_t* n_moves,
+                                  int max_moves, int32_t* blocks, int32_t* n_blocks,
+                                  int max_blocks, int32_t* err_word, hipStream_t stream);
 hipError_t moe_launch_ffn_schedule(const int32_t* blocks, const int32_t* n_blocks, int max_blocks,
                                    int E_loc, int32_t* ws, hipStream_t stream);
 

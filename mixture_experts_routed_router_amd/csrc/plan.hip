@@ -15,45 +15,12 @@
 // reduce with DPP lane swaps inside a row, larger ones add cross-row shuffles.  The block
 // table is then emitted by all threads from a scan of per-(rank, expert) block counts.
 #include "moe_launch.h"
+#include "moe_wave.h"
 
 namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxSlices = 4096;  // E_loc * P
-
-// value of lane (lane ^ 1), (lane ^ 2), (7 - lane within 8), (15 - lane within 16): after
-// reductions over the smaller groups, each step pairs a lane with the other half of its group
-template <int kStep>
-__device__ __forceinline__ int dpp_partner(int v) {
-    constexpr int ctrl = kStep == 0 ? 0xB1 : kStep == 1 ? 0x4E : kStep == 2 ? 0x141 : 0x140;
-    return __builtin_amdgcn_update_dpp(v, v, ctrl, 0xF, 0xF, false);
-}
-
-// Best (v, i) over the aligned group of 2^levels lanes containing this lane (levels <= 6);
-// every lane of the group ends with the result.  kMax: larger v wins, else smaller v; equal
-// v: smaller i.
-template <bool kMax>
-__device__ __forceinline__ void group_best(int& v, int& i, int levels) {
-    auto take = [&](int ov, int oi) {
-        const bool better = kMax ? (ov > v || (ov == v && oi < i)) : (ov < v || (ov == v && oi < i));
-        if (better) {
-            v = ov;
-            i = oi;
-        }
-    };
-    if (levels > 0) take(dpp_partner<0>(v), dpp_partner<0>(i));
-    if (levels > 1) take(dpp_partner<1>(v), dpp_partner<1>(i));
-    if (levels > 2) take(dpp_partner<2>(v), dpp_partner<2>(i));
-    if (levels > 3) take(dpp_partner<3>(v), dpp_partner<3>(i));
-    if (levels > 4) take(__shfl_xor(v, 16, MOE_WAVE), __shfl_xor(i, 16, MOE_WAVE));
-    if (levels > 5) take(__shfl_xor(v, 32, MOE_WAVE), __shfl_xor(i, 32, MOE_WAVE));
-}
-
-__device__ __forceinline__ int ceil_log2(int n) {
-    int l = 0;
-    while ((1 << l) < n) ++l;
-    return l;
-}
 
 __global__ void __launch_bounds__(kThreads)
 plan_kernel(const int32_t* __restrict__ counts, int begin, int stride, int E_loc, int P,

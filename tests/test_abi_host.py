@@ -117,6 +117,21 @@ def test_plan_rejects(lib):
     assert plan(E=512, E_loc=512, Pn=8) == UNSUPPORTED
 
 
+def test_plan_blocks_rejects(lib):
+    def plan(E=8, begin=0, stride=1, E_loc=8, Pn=4, bm=128, s=1, max_moves=32, max_blocks=16,
+             counts=P[0]):
+        return lib.moe_plan_blocks(counts, E, begin, stride, E_loc, Pn, bm, s, P[1], P[2], P[3],
+                                   max_moves, P[4], P[5], max_blocks, NULL, NULL)
+    assert plan(counts=NULL) == INVALID
+    assert plan(Pn=3) == INVALID            # P must divide E_loc
+    assert plan(bm=48) == INVALID
+    assert plan(s=-1) == INVALID
+    assert plan(max_blocks=0) == INVALID
+    assert plan(E=256, E_loc=256, Pn=128) == UNSUPPORTED
+    assert plan(E=128, E_loc=128, Pn=1) == UNSUPPORTED    # 128 experts per rank
+    assert plan(s=70000) == UNSUPPORTED
+
+
 def test_ffn_and_combine_reject(lib):
     ffn = lambda dt, H, I, blocks=P[3], ws_elems=272: lib.moe_expert_ffn(
         P[0], P[1], P[2], dt, H, I, 8, blocks, P[4], 16, P[5], P[6], 1024, P[7], ws_elems, NULL)
