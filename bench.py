@@ -37,6 +37,9 @@ def parse():
     ap.add_argument("--workload", default="olmoe_shaped")
     ap.add_argument("--skew", default=None, help="Zipf exponent or 'hot4' (default: middle skew)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--planner", choices=("moonep", "megaflux"), default="moonep",
+                    help="moe_plan (exact per-rank entry capacity, the default) or moe_plan_blocks "
+                         "(block-granular replicas, budget E_loc / (4P))")
     ap.add_argument("--materialize", action="store_true",
                     help="write the permuted copy xp of x (moe_permute with xp, moe_expert_ffn) "
                          "instead of gathering x rows inside the gate/up GEMM")
@@ -157,6 +160,38 @@ def ffn_source_sha256() -> str:
     return h.hexdigest()
 
 
+def plan_comparison(layer, w, steps, torch):
+    """Both planners on the layer's current expert counts: plan kernel time (HIP events over
+    back-to-back calls), blocks in the table, the busiest rank's blocks and rows, partial
+    blocks, and weight copies (moe_plan: expert slices moved; moe_plan_blocks: replicas)."""
+    res = {}
+    saved = layer.planner
+    for name in ("moonep", "megaflux"):
+        layer.planner = name
+        layer.plan()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            layer.plan()
+        e1.record()
+        torch.cuda.synchronize()
+        nb = int(layer.n_blocks.item())
+        bl = layer.blocks[:nb].cpu().long()
+        per_blocks = torch.bincount(bl[:, 0], minlength=w.P)
+        per_rows = torch.zeros(w.P, dtype=torch.long).index_add_(0, bl[:, 0], bl[:, 3])
+        res[name] = {"plan_us": round(e0.elapsed_time(e1) / steps * 1e3, 2), "blocks": nb,
+                     "max_rank_blocks": int(per_blocks.max()),
+                     "max_rank_rows": int(per_rows.max()),
+                     "partial_blocks": int((bl[:, 3] < w.beta).sum()),
+                     "weight_copies": int(layer.n_moves.item())}
+    res["megaflux"]["replica_budget"] = layer.replica_budget
+    layer.planner = saved
+    layer.plan()
+    torch.cuda.synchronize()
+    return res
+
+
 def cpu_baseline(w, skew, T_s, target_s=12.0):
     """The CPU oracle, as it stands, over the first tokens of the same batch (whole path).
     A first pass over T_s tokens sizes the measured sample to about target_s seconds of CPU
@@ -222,7 +257,8 @@ def main():
     x = inputs.make_x(w).to(dev)
     layer = binding.RoutedExperts(w.T, w.H, w.E, w.K, w.I, w.P, dtype=dt, E_loc=w.n_local,
                                   expert_begin=w.expert_begin, expert_stride=w.expert_stride,
-                                  block_m=w.beta, gather=not args.materialize)
+                                  block_m=w.beta, gather=not args.materialize,
+                                  planner=args.planner)
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
@@ -293,7 +329,8 @@ def main():
         "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "E_loc": w.n_local,
                    "K": w.K, "I": w.I, "P": w.P, "block_m": w.beta,
                    "skew": w.skew_label(skew), "local_entries": N, "blocks": nb,
-                   "maxvio": round(maxvio, 3), "parallelism": "single GPU",
+                   "maxvio": round(maxvio, 3), "planner": args.planner,
+                   "parallelism": "single GPU",
                    "launch": "hip graph replay" if args.graph else "eager",
                    "dispatch": "materialised xp" if args.materialize else
                                "gather-on-load (FC1 reads x rows through row_token)"},
@@ -311,6 +348,8 @@ def main():
         "roofline": roofline,
         "roofline_kernel_us": round(fc1_s * 1e6, 2),
     }
+    if w.n_local // w.P <= 64 and w.n_local * w.P <= 4096:
+        line["plan_comparison"] = plan_comparison(layer, w, max(20, args.steps // 4), torch)
     if not args.no_all_skews:
         by = []
         for sk in w.skews:

@@ -73,32 +73,46 @@ __device__ void search(vint* q, const int* b_s, int E_loc, int P, int G, int tau
                 if (lane == j) scanned = true;
                 const int l = d * G + j;
                 int qc = rank_lane ? (int)q[l * P + lane] : 0;  // this lane's column of row l
+                int qd = __shfl(qc, d, MOE_WAVE);               // blocks of l still at home
                 bool opened = false;                            // a new copy of l this round
+                // Single-block moves, k at a time: the receiver stays the least-loaded eligible
+                // copy (lower rank on ties) until it passes the runner-up, reaches tau, the
+                // donor reaches tau or l runs out of blocks at home; a new copy is the only
+                // eligible copy after its first block.  So k single-block steps in a row pick
+                // the same receiver, and moving them at once gives the same plan.
                 for (;;) {
-                    const int qd = __shfl(qc, d, MOE_WAVE);
                     if (qd == 0 || Ld <= tau) break;
-                    int v3 = (rank_lane && lane != d && qc > 0 && L < tau) ? L : kBig, rcv = lane;
+                    const bool existing = rank_lane && lane != d && qc > 0 && L < tau;
+                    int v3 = existing ? L : kBig, rcv = lane;
                     wave_best<false>(v3, rcv, lp);
                     bool open_new = false;
-                    if (v3 == kBig) {
+                    int k = min(qd, Ld - tau);
+                    if (v3 != kBig) {
+                        int v5 = (existing && lane != rcv) ? L : kBig, r2 = lane;
+                        wave_best<false>(v5, r2, lp);
+                        k = min(k, tau - v3);
+                        if (v5 != kBig) k = min(k, rcv < r2 ? v5 - v3 + 1 : v5 - v3);
+                    } else {
                         if (!many && opened) break;
                         int v4 = (rank_lane && lane != d && qc == 0 && repl < s && L < tau) ? L : kBig;
                         rcv = lane;
                         wave_best<false>(v4, rcv, lp);
                         if (v4 == kBig) break;
                         open_new = true;
+                        k = min(k, tau - v4);
                     }
                     if (lane == d) {
-                        qc -= 1;
-                        L -= 1;
+                        qc -= k;
+                        L -= k;
                     }
                     if (lane == rcv) {
-                        qc += 1;
-                        L += 1;
+                        qc += k;
+                        L += k;
                         if (open_new) repl += 1;
                     }
                     if (open_new) opened = true;
-                    Ld -= 1;
+                    qd -= k;
+                    Ld -= k;
                     moved = true;
                 }
                 if (rank_lane) q[l * P + lane] = qc;
@@ -106,6 +120,29 @@ __device__ void search(vint* q, const int* b_s, int E_loc, int P, int G, int tau
         }
         if (!moved) break;
     }
+}
+
+// Exclusive prefix of per-thread values over the workgroup in thread order; *total gets the
+// sum.  part holds one int per wave.
+__device__ __forceinline__ int block_scan(int v, int* part, int* total) {
+    const int lane = moe_lane_id(), wave = threadIdx.x / MOE_WAVE;
+    int incl = v;
+#pragma unroll
+    for (int d = 1; d < MOE_WAVE; d <<= 1) {
+        const int o = __shfl_up(incl, d, MOE_WAVE);
+        if (lane >= d) incl += o;
+    }
+    if (lane == MOE_WAVE - 1) part[wave] = incl;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / MOE_WAVE; ++w) {
+        before += w < wave ? part[w] : 0;
+        all += part[w];
+    }
+    *total = all;
+    __syncthreads();  // part may be reused
+    return before + incl - v;
 }
 
 __device__ __forceinline__ int wave_max_i32(int v) {
@@ -126,7 +163,6 @@ plan_blocks_kernel(const int32_t* __restrict__ counts, int begin, int stride, in
     __shared__ int qb[4][kMaxCells];            // candidates' block counts [l * P + r]
     __shared__ unsigned long long keys[kMaxCells];  // replica keys; then two prefix tables
     __shared__ int cand_max[4], cand_rep[4];
-    __shared__ int rank_base[65];
     __shared__ int part[kThreads / MOE_WAVE];
     __shared__ int sum_b_s, err_s;
 
@@ -184,18 +220,28 @@ plan_blocks_kernel(const int32_t* __restrict__ counts, int begin, int stride, in
     const int Lmax = cand_max[best];
     vint* q = qb[best];
 
-    // pruning order: replicas by (allocation at pass entry, expert, rank); others sort last
+    // pruning order: replicas by (allocation at pass entry, expert, rank); compacted by
+    // wave 0, then sorted
+    const int n_rep = cand_rep[best];
     int n2 = 1;
-    while (n2 < cells) n2 <<= 1;
-    for (int i = tid; i < n2; i += kThreads) {
-        unsigned long long k = ~0ull;
-        if (i < cells) {
-            const int l = i / P, r = i - l * P;
-            const int a = q[i];
-            if (r != l / G && a > 0)
+    while (n2 < n_rep) n2 <<= 1;
+    if (wave == 0) {
+        int base = 0;
+        for (int c0 = 0; c0 < cells; c0 += MOE_WAVE) {
+            const int c = c0 + lane;
+            bool is_rep = false;
+            unsigned long long k = 0;
+            if (c < cells) {
+                const int l = c / P, r = c - l * P;
+                const int a = q[c];
+                is_rep = r != l / G && a > 0;
                 k = ((unsigned long long)a << 32) | ((unsigned long long)l << 16) | (unsigned)r;
+            }
+            const unsigned long long bal = __ballot(is_rep);
+            if (is_rep) keys[base + __popcll(bal & ((1ull << lane) - 1))] = k;
+            base += __popcll(bal);
         }
-        keys[i] = k;
+        for (int i = base + lane; i < n2; i += MOE_WAVE) keys[i] = ~0ull;
     }
     __syncthreads();
     for (int k = 2; k <= n2; k <<= 1) {
@@ -223,9 +269,8 @@ plan_blocks_kernel(const int32_t* __restrict__ counts, int begin, int stride, in
             for (int l = 0; l < E_loc; ++l) L += q[l * P + lane];
         // refinement 1: drop replicas whose whole allocation fits under Lmax on the owner,
         // else on the least-loaded other copy
-        for (int i = 0; i < cells; ++i) {
+        for (int i = 0; i < n_rep; ++i) {
             const unsigned long long k = keys[i];
-            if (k == ~0ull) break;
             const int l = (int)((k >> 16) & 0xFFFF), r = (int)(k & 0xFFFF), h = l / G;
             int qc = rank_lane ? (int)q[l * P + lane] : 0;
             const int a = __shfl(qc, r, MOE_WAVE);
@@ -277,63 +322,33 @@ plan_blocks_kernel(const int32_t* __restrict__ counts, int begin, int stride, in
     __syncthreads();
 
     // block table: expert l's blocks go to the ranks holding it in ascending rank order;
-    // rows listed rank by rank, then expert by expert
+    // rows listed rank by rank, then expert by expert.  Two scans over the cells, 16
+    // consecutive ones per thread: expert-major (each (l, r)'s first block within expert l,
+    // rows per (l, r), the replica list in (expert, rank) order), then rank-major (each
+    // (l, r)'s first position in the table); then one thread per table entry.
+    constexpr int kPer = kMaxCells / kThreads;
     int* pre_l = reinterpret_cast<int*>(keys);  // first block of (l, r) within expert l
-    int* pos_r = pre_l + kMaxCells;             // table position of that first block
-    for (int l = tid; l < E_loc; l += kThreads) {
-        int acc = 0;
-        for (int r = 0; r < P; ++r) {
-            pre_l[l * P + r] = acc;
-            acc += q[l * P + r];
-        }
+    const int c_lo = tid * kPer, c_hi = min(c_lo + kPer, cells);
+    int my_blocks = 0, my_reps = 0;
+    for (int c = c_lo; c < c_hi; ++c) {
+        const int l = c / P, r = c - l * P, k = q[c];
+        my_blocks += k;
+        my_reps += (r != l / G && k > 0) ? 1 : 0;
     }
-    if (tid < P) {
-        int tot = 0;
-        for (int l = 0; l < E_loc; ++l) tot += q[l * P + tid];
-        rank_base[tid + 1] = tot;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        rank_base[0] = 0;
-        for (int r = 0; r < P; ++r) rank_base[r + 1] += rank_base[r];
-    }
-    __syncthreads();
-    if (tid < P) {
-        int acc = rank_base[tid];
-        for (int l = 0; l < E_loc; ++l) {
-            pos_r[l * P + tid] = acc;
-            acc += q[l * P + tid];
-        }
-    }
-    __syncthreads();
-    // replicas listed expert by expert, then rank: exclusive count over the cells in order
-    constexpr int kPer = kMaxCells / kThreads;  // 16 consecutive cells per thread
-    int mine = 0;
-    for (int c = tid * kPer; c < (tid + 1) * kPer && c < cells; ++c) {
-        const int l = c / P, r = c - l * P;
-        mine += (r != l / G && q[c] > 0) ? 1 : 0;
-    }
-    int incl = mine;
-#pragma unroll
-    for (int d = 1; d < MOE_WAVE; d <<= 1) {
-        const int o = __shfl_up(incl, d, MOE_WAVE);
-        if (lane >= d) incl += o;
-    }
-    if (lane == MOE_WAVE - 1) part[wave] = incl;
-    __syncthreads();
-    int before = incl - mine;
-    for (int w = 0; w < wave; ++w) before += part[w];
-    const int total_moves = part[0] + part[1] + part[2] + part[3];
-    for (int c = tid * kPer; c < (tid + 1) * kPer && c < cells; ++c) {
-        const int l = c / P, r = c - l * P;
-        const int k = q[c];
-        const int pre = pre_l[c];
+    int total_blocks, total_moves;
+    int run_b = block_scan(my_blocks, part, &total_blocks);
+    int run_m = block_scan(my_reps, part, &total_moves);
+    for (int c = c_lo; c < c_hi; ++c) {
+        const int l = c / P, r = c - l * P, k = q[c];
+        const int pre = run_b - off_s[l] / beta;  // blocks of l on ranks below r
+        pre_l[c] = pre;
+        run_b += k;
         const int n = n_s[l];
         const int lo = min(n, pre * beta), hi = min(n, (pre + k) * beta);
         q_out[c] = hi - lo;
         if (r != l / G && k > 0) {
-            if (before < max_moves) {
-                int32_t* m = moves + 4 * before;
+            if (run_m < max_moves) {
+                int32_t* m = moves + 4 * run_m;
                 m[0] = l / G;
                 m[1] = r;
                 m[2] = l;
@@ -341,25 +356,47 @@ plan_blocks_kernel(const int32_t* __restrict__ counts, int begin, int stride, in
             } else {
                 atomicOr(&err_s, 2);
             }
-            ++before;
+            ++run_m;
         }
-        for (int j = 0; j < k; ++j) {
-            const int bi = pre + j, pos = pos_r[c] + j;
-            if (pos >= max_blocks) {
-                atomicOr(&err_s, 1);
-                break;
-            }
-            int32_t* bl = blocks + 4 * pos;
-            bl[0] = r;
-            bl[1] = l;
-            bl[2] = off_s[l] + bi * beta;
-            bl[3] = min(beta, n - bi * beta);
+    }
+    __syncthreads();
+    int my_rank_major = 0;
+    for (int i = c_lo; i < c_hi; ++i) {
+        const int r = i / E_loc, l = i - r * E_loc;
+        my_rank_major += q[l * P + r];
+    }
+    int unused;
+    int pos = block_scan(my_rank_major, part, &unused);
+    int* start_rm = pre_l + kMaxCells;  // first table position of rank-major cell r * E_loc + l
+    for (int i = c_lo; i < c_hi; ++i) {
+        const int r = i / E_loc, l = i - r * E_loc;
+        start_rm[i] = pos;
+        pos += q[l * P + r];
+    }
+    __syncthreads();
+    // one thread per table position: its cell is the last one starting at or before it
+    // (cells without blocks share the next cell's start and are skipped that way)
+    if (total_blocks > max_blocks && tid == 0) atomicOr(&err_s, 1);
+    const int nb_out = min(total_blocks, max_blocks);
+    for (int p = tid; p < nb_out; p += kThreads) {
+        int lo = 0, hi = cells - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (start_rm[mid] <= p) lo = mid;
+            else hi = mid - 1;
         }
+        const int r = lo / E_loc, l = lo - r * E_loc;
+        const int bi = pre_l[l * P + r] + (p - start_rm[lo]);
+        int32_t* bl = blocks + 4 * p;
+        bl[0] = r;
+        bl[1] = l;
+        bl[2] = off_s[l] + bi * beta;
+        bl[3] = min(beta, n_s[l] - bi * beta);
     }
     __syncthreads();
     if (tid == 0) {
         *n_moves = min(total_moves, max_moves);
-        *n_blocks = min(rank_base[P], max_blocks);
+        *n_blocks = min(total_blocks, max_blocks);
         if (err_word) *err_word = err_s;
     }
 }
