@@ -36,9 +36,14 @@ struct Geom {
     static constexpr int kLPT = kThreads / TM;                // top-k lanes per token
     static constexpr int kNE = kRowsB / kLPT;                 // experts per top-k lane
     static constexpr int kLdS = kRowsB + 1;                   // score tile row stride (floats)
+    static constexpr int kScoreBytes = TM * kLdS * 4;
+    // LDS: the ring, reused for the score tile once the slices are consumed
+    static constexpr int kSmem = kStages * kStageBytes > kScoreBytes ? kStages * kStageBytes
+                                                                     : kScoreBytes;
     static_assert(kSegs % 4 == 0, "whole copies per wave");
     static_assert(kStages >= 2, "ring depth");
-    static_assert(TM * kLdS * 4 <= kRingBytes, "score tile fits in the ring");
+    static_assert(kSmem <= 136 * 1024, "LDS");
+    static_assert(4 % kRB == 0, "every tile of a wave shares its row block");
 };
 
 // Stage layout: segment g (8 rows of 128 bytes) at g KB; segments 0 .. TM/8 - 1 hold token
@@ -60,7 +65,7 @@ router_bf16_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
                    int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
                    int32_t* __restrict__ counts) {
     using G = Geom<TM, NB>;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[kRingBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[G::kSmem];
     __shared__ int hist[256];
     const int tid = threadIdx.x;
     const int lane = moe_lane_id();
@@ -242,6 +247,15 @@ hipError_t launch_bf16(int km, const uint16_t* x, const uint16_t* wr, int T, int
     return hipGetLastError();
 }
 
+// 128-token tiles (E > 128 only): the router rows are staged once per 128 tokens
+hipError_t launch_tm128(int km, const uint16_t* x, const uint16_t* wr, int T, int H, int E, int K,
+                        int k_ref, float* logits, int32_t* ids, float* w, int32_t* counts,
+                        hipStream_t stream) {
+    if ((E + 31) / 32 <= 6)
+        return launch_bf16<128, 6>(km, x, wr, T, H, E, K, k_ref, logits, ids, w, counts, stream);
+    return launch_bf16<128, 8>(km, x, wr, T, H, E, K, k_ref, logits, ids, w, counts, stream);
+}
+
 template <int TM>
 hipError_t launch_tm(int km, const uint16_t* x, const uint16_t* wr, int T, int H, int E, int K,
                      int k_ref, float* logits, int32_t* ids, float* w, int32_t* counts,
@@ -291,7 +305,10 @@ hipError_t moe_launch_router_topk(const void* x, moe_dtype_t dt, const void* w_r
     }
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     const uint16_t* wb = static_cast<const uint16_t*>(w_router);
-    // 64-token tiles once there are enough of them to give every CU one, else 32
+    // the largest token tile that still gives every CU one (128 only pays for E > 128, where
+    // router rows dominate the staging), else 32
+    if (E > 128 && (T + 127) / 128 >= 256)
+        return launch_tm128(km, xb, wb, T, H, E, K, k_ref, logits, topk_ids, topk_w, counts, stream);
     if ((T + 63) / 64 >= 256)
         return launch_tm<64>(km, xb, wb, T, H, E, K, k_ref, logits, topk_ids, topk_w, counts, stream);
     return launch_tm<32>(km, xb, wb, T, H, E, K, k_ref, logits, topk_ids, topk_w, counts, stream);

@@ -86,6 +86,9 @@ SMALL = [
     ("bf16_k16", 300, 128, 96, 16, 16, torch.bfloat16),
     # 257 tiles of 64 tokens: the 64-token tile shape and the grid-stride loop
     ("bf16_tm64_stride", 16400, 64, 64, 8, 8, torch.bfloat16),
+    # 128-token tiles for E > 128 (192 and 256 router rows), ragged E and T, grid-stride
+    ("bf16_tm128_e160", 32768 + 77, 128, 160, 6, 7, torch.bfloat16),
+    ("bf16_tm128_e200", 32768, 64, 200, 8, 8, torch.bfloat16),
     ("f32_ragged_h", 200, 100, 40, 3, 40, torch.float32),
     ("f32_e256_k16", 130, 64, 256, 16, 16, torch.float32),
     ("f32_e8_kref3", 64, 128, 8, 2, 3, torch.float32),
