@@ -671,6 +671,176 @@ done:
     return rc;
 }
 
+/* -------------------------------------------------------------- MX formats --- */
+
+/* Microscaled low-precision formats for the expert FFN ([MF §2.1 "Persistent MoE execution"]
+ * and §4.1: MXFP4 weights, MXFP8 activations, FP32 accumulation, BF16 outputs; [MEP] cost
+ * model: packed 4-bit elements plus one scale per 32 elements).  The element and scale
+ * encodings are those of the OCP Microscaling Formats (MX) v1.0 specification:
+ *   a block of 32 consecutive values shares one E8M0 scale 2^(code - 127) (code 255 = NaN is
+ *   never produced), shared exponent = floor(log2(max |v|)) - emax_elem clamped to
+ *   [-127, 127] (-127 for an all-zero block);
+ *   elements: fmt 0 = FP8 E4M3 (bias 7, no infinities, max 448, emax 8), one byte each;
+ *             fmt 1 = FP4 E2M1 (bias 1, values 0, 0.5, 1, 1.5, 2, 3, 4, 6, emax 2), two per byte,
+ *             the lower-indexed element in the low nibble;
+ *   element = v / scale rounded to the nearest representable value, ties to the even code,
+ *   magnitudes beyond the largest value saturate to it.
+ * Codes here come from the definition: the value of every non-negative code is computed and
+ * the nearest is chosen. */
+static double mx_elem_value(int fmt, int code) {
+    const int s = fmt == 0 ? (code >> 7) & 1 : (code >> 3) & 1;
+    const int e = fmt == 0 ? (code >> 3) & 15 : (code >> 1) & 3;
+    const int m = fmt == 0 ? code & 7 : code & 1;
+    const int mbits = fmt == 0 ? 3 : 1, bias = fmt == 0 ? 7 : 1;
+    double v = e == 0 ? ldexp((double)m / (1 << mbits), 1 - bias)
+                      : ldexp(1.0 + (double)m / (1 << mbits), e - bias);
+    return s ? -v : v;
+}
+
+static int mx_max_code(int fmt) { return fmt == 0 ? 0x7E : 0x7; }  /* 448, 6 */
+
+/* the values of the non-negative codes, filled once before any parallel use */
+static double mx_table[2][128];
+static int mx_table_ready = 0;
+static void mx_fill_table(void) {
+    if (mx_table_ready) return;
+    for (int f = 0; f < 2; ++f)
+        for (int c = 0; c <= mx_max_code(f); ++c) mx_table[f][c] = mx_elem_value(f, c);
+    mx_table_ready = 1;
+}
+static int mx_emax(int fmt) { return fmt == 0 ? 8 : 2; }
+
+/* nearest non-negative code to |v| (ties to the even code), then the sign */
+static int mx_encode(int fmt, double v) {
+    const double a = fabs(v);
+    int best = 0;
+    for (int c = 1; c <= mx_max_code(fmt); ++c) {
+        const double dc = fabs(mx_table[fmt][c] - a), db = fabs(mx_table[fmt][best] - a);
+        if (dc < db || (dc == db && (c & 1) == 0)) best = c;
+    }
+    if (a > mx_table[fmt][mx_max_code(fmt)]) best = mx_max_code(fmt);
+    const int sign = v < 0 && best != 0 ? 1 : 0;
+    return best | (sign << (fmt == 0 ? 7 : 3));
+}
+
+/* src [rows, cols] (dt 0 = float32, 1 = bf16), cols a multiple of 32 ->
+ * codes [rows, cols] (fmt 0) or [rows, cols / 2] (fmt 1), scales [rows, cols / 32]. */
+int oracle_mx_quantize(const void* src, int dt, int64_t rows, int64_t cols, int fmt,
+                       uint8_t* codes, uint8_t* scales) {
+    if (rows < 0 || cols < 32 || cols % 32 != 0 || (dt != 0 && dt != 1) || (fmt != 0 && fmt != 1))
+        return ORACLE_ERR_ARG;
+    mx_fill_table();
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < cols / 32; ++b) {
+            double amax = 0.0;
+            for (int j = 0; j < 32; ++j) {
+                const double v = fabs(load_elem(src, r * cols + b * 32 + j, dt));
+                if (v > amax) amax = v;
+            }
+            int se = -127;
+            if (amax > 0.0) {
+                int ex;
+                frexp(amax, &ex);  /* amax = m * 2^ex, m in [0.5, 1): floor(log2 amax) = ex - 1 */
+                se = ex - 1 - mx_emax(fmt);
+                if (se < -127) se = -127;
+                if (se > 127) se = 127;
+            }
+            scales[r * (cols / 32) + b] = (uint8_t)(se + 127);
+            for (int j = 0; j < 32; ++j) {
+                const int64_t i = r * cols + b * 32 + j;
+                const int c = mx_encode(fmt, ldexp(load_elem(src, i, dt), -se));
+                if (fmt == 0) {
+                    codes[i] = (uint8_t)c;
+                } else {
+                    uint8_t* byte = codes + i / 2;
+                    *byte = (uint8_t)((i & 1) ? ((*byte & 0x0F) | (c << 4)) : ((*byte & 0xF0) | c));
+                }
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
+static double mx_value(const uint8_t* codes, const uint8_t* scales, int64_t cols, int fmt, int64_t r,
+                       int64_t c) {
+    const int64_t i = r * cols + c;
+    const int code = fmt == 0 ? codes[i] : ((codes[i / 2] >> ((i & 1) * 4)) & 0xF);
+    const int mag = code & (fmt == 0 ? 0x7F : 0x7), neg = code != mag;
+    const double v = ldexp(mx_table[fmt][mag], (int)scales[r * (cols / 32) + c / 32] - 127);
+    return neg ? -v : v;
+}
+
+int oracle_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                         int fmt, double* out) {
+    if (rows < 0 || cols < 32 || cols % 32 != 0 || (fmt != 0 && fmt != 1)) return ORACLE_ERR_ARG;
+    mx_fill_table();
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) out[r * cols + c] = mx_value(codes, scales, cols, fmt, r, c);
+    return ORACLE_OK;
+}
+
+/* SwiGLU expert FFN in the MX formats ([MF §4.1 Platform and configurations]: MXFP4 weights,
+ * MXFP8 activations, FP32 accumulation, BF16 outputs), for a list of rows.  xq/xs: the layer
+ * input rows in MXFP8 (E4M3 codes [*, H], scales [*, H/32]); w1q/w1s: W1 in MXFP4 ([E_loc, 2I,
+ * H/2] packed, scales [E_loc, 2I, H/32]; rows 0..I-1 gate, I..2I-1 up); w2q/w2s: W2 in MXFP4
+ * ([E_loc, H, I/2], [E_loc, H, I/32]).  Row j of the list is row rows[j] of xq, expert
+ * row_expert[j]:
+ *   g_i, u_i = dot products of the dequantized values in double;
+ *   a_i = g_i / (1 + exp(-g_i)) * u_i, quantized to MXFP8 per 32 columns -> actq [n, I], acts;
+ *   yp[j][h] = bf16(sum_i deq(actq)[i] * deq(W2[l][h][i]))  (double). */
+int oracle_ffn_mx_rows(const uint8_t* xq, const uint8_t* xs, int H, int I, const uint8_t* w1q,
+                       const uint8_t* w1s, const uint8_t* w2q, const uint8_t* w2s,
+                       const int32_t* rows, const int32_t* row_expert, int n, uint8_t* actq,
+                       uint8_t* acts, uint16_t* yp) {
+    if (H < 32 || I < 32 || H % 32 != 0 || I % 32 != 0 || n < 0) return ORACLE_ERR_ARG;
+    mx_fill_table();
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int j = 0; j < n; ++j) {
+        const int64_t p = rows[j], l = row_expert[j];
+        double* a = (double*)malloc(sizeof(double) * (size_t)I);
+        if (!a) { bad = 1; continue; }
+        const uint8_t* w1qe = w1q + l * 2 * I * (int64_t)(H / 2);
+        const uint8_t* w1se = w1s + l * 2 * I * (int64_t)(H / 32);
+        for (int i = 0; i < I; ++i) {
+            double g = 0.0, u = 0.0;
+            for (int h = 0; h < H; ++h) {
+                const double xv = mx_value(xq, xs, H, 0, p, h);
+                g += xv * mx_value(w1qe, w1se, H, 1, i, h);
+                u += xv * mx_value(w1qe, w1se, H, 1, I + i, h);
+            }
+            a[i] = g / (1.0 + exp(-g)) * u;
+        }
+        /* the activation row in MXFP8: the same rule as oracle_mx_quantize, from double */
+        for (int b = 0; b < I / 32; ++b) {
+            double amax = 0.0;
+            for (int k = 0; k < 32; ++k) if (fabs(a[b * 32 + k]) > amax) amax = fabs(a[b * 32 + k]);
+            int se = -127;
+            if (amax > 0.0) {
+                int ex;
+                frexp(amax, &ex);
+                se = ex - 1 - mx_emax(0);
+                if (se < -127) se = -127;
+                if (se > 127) se = 127;
+            }
+            acts[(int64_t)j * (I / 32) + b] = (uint8_t)(se + 127);
+            for (int k = 0; k < 32; ++k)
+                actq[(int64_t)j * I + b * 32 + k] = (uint8_t)mx_encode(0, ldexp(a[b * 32 + k], -se));
+        }
+        const uint8_t* w2qe = w2q + l * (int64_t)H * (I / 2);
+        const uint8_t* w2se = w2s + l * (int64_t)H * (I / 32);
+        for (int h = 0; h < H; ++h) {
+            double acc = 0.0;
+            for (int i = 0; i < I; ++i)
+                acc += mx_value(actq, acts, I, 0, j, i) * mx_value(w2qe, w2se, I, 1, h, i);
+            yp[(int64_t)j * H + h] = oracle_double_to_bf16(acc);
+        }
+        free(a);
+    }
+    return bad ? ORACLE_ERR_DATA : ORACLE_OK;
+}
+
 /* ------------------------------------------------------------------- expert FFN --- */
 
 /* SwiGLU expert FFN for a list of rows.  [MF §2.1, §4.1]: FC1 produces gate and up

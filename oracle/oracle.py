@@ -12,7 +12,8 @@ permute -- stable expert-major order by flat index, beta-aligned segments;
 plan   -- the greedy donor->receiver balance to exact per-rank capacity, then <=beta blocks;
 plan_blocks -- the block-granular replica planner: four greedy searches, the best, refined;
 ffn    -- SwiGLU expert FFN in double with bf16 rounding at act and yp;
-combine -- routing-weight sum in double, k ascending.
+combine -- routing-weight sum in double, k ascending;
+mx_*   -- OCP MX formats (MXFP8 E4M3 / MXFP4 E2M1, one E8M0 scale per 32 values) and the FFN in them.
 """
 from __future__ import annotations
 
@@ -51,7 +52,8 @@ def _load():
         lib.oracle_num_threads.restype = ctypes.c_int
         for name in ("oracle_route", "oracle_route_ref", "oracle_router_logits", "oracle_permute",
                      "oracle_plan", "oracle_plan_blocks", "oracle_ffn_rows", "oracle_ffn_blocks",
-                     "oracle_combine"):
+                     "oracle_combine", "oracle_mx_quantize", "oracle_mx_dequantize",
+                     "oracle_ffn_mx_rows"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -225,6 +227,48 @@ def ffn_blocks(xp: np.ndarray, w1: np.ndarray, w2: np.ndarray, blocks: np.ndarra
                                      _p(np.ascontiguousarray(w2)), _p(blocks), blocks.shape[0],
                                      _p(act), _p(yp)), "ffn_blocks")
     return act, yp
+
+
+MX_FP8, MX_FP4 = 0, 1
+
+
+def mx_quantize(a: np.ndarray, fmt: int):
+    """[rows, cols] float32 or bf16 bits -> (codes uint8 [rows, cols] (FP8) or [rows, cols/2] (FP4,
+    low nibble first), scales uint8 [rows, cols/32])."""
+    a = np.ascontiguousarray(a)
+    dt = _dt_code(a)
+    rows, cols = a.shape
+    codes = np.zeros((rows, cols if fmt == MX_FP8 else cols // 2), np.uint8)
+    scales = np.zeros((rows, cols // 32), np.uint8)
+    _check(_load().oracle_mx_quantize(_p(a), dt, ctypes.c_int64(rows), ctypes.c_int64(cols), fmt,
+                                      _p(codes), _p(scales)), "mx_quantize")
+    return codes, scales
+
+
+def mx_dequantize(codes: np.ndarray, scales: np.ndarray, cols: int, fmt: int) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    rows = codes.shape[0]
+    out = np.empty((rows, cols), np.float64)
+    _check(_load().oracle_mx_dequantize(_p(codes), _p(scales), ctypes.c_int64(rows),
+                                        ctypes.c_int64(cols), fmt, _p(out)), "mx_dequantize")
+    return out
+
+
+def ffn_mx_rows(xq, xs, w1q, w1s, w2q, w2s, H, I, rows, row_expert):
+    """MX SwiGLU FFN for selected rows. -> actq [n, I] uint8, acts [n, I/32] uint8, yp [n, H] bf16
+    bits (uint16)."""
+    rows = np.ascontiguousarray(rows, np.int32)
+    row_expert = np.ascontiguousarray(row_expert, np.int32)
+    n = rows.shape[0]
+    actq = np.zeros((n, I), np.uint8)
+    acts = np.zeros((n, I // 32), np.uint8)
+    yp = np.zeros((n, H), np.uint16)
+    args = [np.ascontiguousarray(v, np.uint8) for v in (xq, xs, w1q, w1s, w2q, w2s)]
+    _check(_load().oracle_ffn_mx_rows(_p(args[0]), _p(args[1]), H, I, _p(args[2]), _p(args[3]),
+                                      _p(args[4]), _p(args[5]), _p(rows), _p(row_expert), n,
+                                      _p(actq), _p(acts), _p(yp)), "ffn_mx_rows")
+    return actq, acts, yp
 
 
 def combine(yp: np.ndarray, w: np.ndarray, entry_pos: np.ndarray, T: int, K: int):

@@ -538,3 +538,117 @@ def test_plan_blocks_invariants_all_workloads(oracle_mod, name):
                                                  w.n_local, w.P, w.beta, s, q, moves, blocks)
             if s == 0:
                 assert np.array_equal(load, home)
+
+
+# -------------------------------------------------------------------- MX formats ---
+# Expected codes and values below are worked by hand from the OCP Microscaling Formats (MX)
+# v1.0 specification (FP8 E4M3: bias 7, max 448, no infinities; FP4 E2M1: bias 1, values 0,
+# 0.5, 1, 1.5, 2, 3, 4, 6; E8M0 scales; shared exponent floor(log2 amax) - emax; round to
+# nearest, ties to even; saturation).
+
+def _block(vals, fill=0.0):
+    return np.array([list(vals) + [fill] * (32 - len(vals))], np.float32)
+
+
+def test_mx_fp4_grid_ties_and_saturation(oracle_mod):
+    # block max 6 -> shared exponent floor(log2 6) - 2 = 0, scale code 127
+    v = _block([0, 0.5, 1, 1.5, 2, 3, 4, 6, -6, -0.5])
+    c, s = oracle_mod.mx_quantize(v, oracle_mod.MX_FP4)
+    assert s.tolist() == [[127]]
+    assert oracle_mod.mx_dequantize(c, s, 32, oracle_mod.MX_FP4)[0, :10].tolist() == \
+        [0, 0.5, 1, 1.5, 2, 3, 4, 6, -6, -0.5]
+    # E2M1 codes: 0.5 = 0b0001, 1 = 0b0010, 6 = 0b0111, -6 = 0b1111, -0.5 = 0b1001; two per
+    # byte, the lower-indexed element in the low nibble
+    assert c[0, :5].tolist() == [0x10, 0x32, 0x54, 0x76, 0x9F]
+    # ties to the even code: 2.5 -> 2, 5 -> 4, 0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2,
+    # 3.5 -> 4; beyond 6 saturates (7 -> 6)
+    v = _block([2.5, 5, 0.25, 0.75, 1.25, 1.75, 3.5, 7, -2.5, 6])
+    c, s = oracle_mod.mx_quantize(v, oracle_mod.MX_FP4)
+    assert s.tolist() == [[127]]
+    assert oracle_mod.mx_dequantize(c, s, 32, oracle_mod.MX_FP4)[0, :10].tolist() == \
+        [2, 4, 0, 1, 1, 2, 4, 6, -2, 6]
+    # scale from the block maximum: max 100 -> 2^(6 - 2) = 16
+    v = _block([100, 5, 7, 2.5])
+    c, s = oracle_mod.mx_quantize(v, oracle_mod.MX_FP4)
+    assert s.tolist() == [[131]]
+    assert oracle_mod.mx_dequantize(c, s, 32, oracle_mod.MX_FP4)[0, :4].tolist() == [96, 8, 8, 0]
+    # an all-zero block: scale code 0, codes 0
+    c, s = oracle_mod.mx_quantize(np.zeros((2, 64), np.float32), oracle_mod.MX_FP4)
+    assert s.tolist() == [[0, 0], [0, 0]] and not c.any()
+
+
+def test_mx_fp8_e4m3_codes(oracle_mod):
+    # 448 in the block -> shared exponent floor(log2 448) - 8 = 0
+    v = _block([448, 1.0, 0.5, -2.0, 3.0, 2.0 ** -9, 1.0625, 1.1875, 500.0, -2.0 ** -10])
+    c, s = oracle_mod.mx_quantize(v, oracle_mod.MX_FP8)
+    assert s.tolist() == [[127]]
+    # 448 = 0x7E, 1 = 0x38, 0.5 = 0x30, -2 = 0xC0, 3 = 0x44, 2^-9 = 0x01 (smallest subnormal);
+    # 1.0625 ties to 1.0 (0x38), 1.1875 ties to 1.25 (0x3A); 500 saturates to 448; -2^-10 ties
+    # to -0 (encoded as +0)
+    assert c[0, :10].tolist() == [0x7E, 0x38, 0x30, 0xC0, 0x44, 0x01, 0x38, 0x3A, 0x7E, 0x00]
+    # bf16 input, and the scale follows the block: max 1 -> 2^(0 - 8)
+    v = torch.from_numpy(_block([1.0, 0.75])).to(torch.bfloat16)
+    c, s = oracle_mod.mx_quantize(inputs.as_oracle_array(v), oracle_mod.MX_FP8)
+    assert s.tolist() == [[119]]
+    assert oracle_mod.mx_dequantize(c, s, 32, oracle_mod.MX_FP8)[0, :2].tolist() == [1.0, 0.75]
+
+
+def test_mx_quantize_error_bound_and_scale_invariance(oracle_mod):
+    rng = np.random.default_rng(3)
+    a = (rng.standard_normal((64, 256)) * np.exp(rng.uniform(-8, 8, (64, 1)))).astype(np.float32)
+    for fmt, mbits, maxv in ((oracle_mod.MX_FP8, 3, 448.0), (oracle_mod.MX_FP4, 1, 6.0)):
+        c, s = oracle_mod.mx_quantize(a, fmt)
+        d = oracle_mod.mx_dequantize(c, s, 256, fmt)
+        scale = np.repeat(np.exp2(s.astype(np.float64) - 127), 32, axis=1)
+        v = a.astype(np.float64) / scale
+        # nearest representable: error <= half a unit in the last place at |v| (subnormal
+        # floor at the minimum normal exponent), or the saturation distance beyond the max
+        e = np.floor(np.log2(np.maximum(np.abs(v), 1e-300)))
+        emin = 1 - (7 if fmt == oracle_mod.MX_FP8 else 1)
+        half_ulp = np.exp2(np.maximum(e, emin) - mbits - 1)
+        bound = np.maximum(half_ulp, np.abs(v) - maxv) + 1e-300
+        assert np.all(np.abs(d / scale - v) <= bound * (1 + 1e-12))
+        # scaling a row by 2^k moves its scales by k and keeps its codes
+        c2, s2 = oracle_mod.mx_quantize((a * 2.0 ** 5).astype(np.float32), fmt)
+        assert np.array_equal(c2, c) and np.array_equal(s2.astype(int), s.astype(int) + 5)
+
+
+def test_ffn_mx_exact_inputs_match_float64_matmul(oracle_mod):
+    """Inputs on the formats' grids with unit scales are quantized exactly, so the MX FFN is the
+    dense SwiGLU of those values: FC1 against a float64 library matmul (its quantized output
+    within the MXFP8 bound), FC2 on the oracle's own act against a float64 matmul rounded to
+    bf16 (the bf16 rounding is pinned above)."""
+    rng = np.random.default_rng(9)
+    H, I, E = 64, 64, 2
+    e4 = np.array([0, 0.5, 1.0, 1.5, 2.0, 3.0, 0.25, 0.375, 1.75, -1.0, -0.5, -2.5], np.float64)
+    e2 = np.array([0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, -0.5, -1.0, -1.5, -2.0, -3.0], np.float64)
+    x = rng.choice(e4, (6, H))
+    x[:, ::32] = 256.0  # a 256 in every block: shared exponent 0 for E4M3
+    w1 = rng.choice(e2, (E, 2 * I, H)) / 8
+    w1[..., ::32] = 4.0 / 8  # block max 0.5: shared exponent -3, values on the grid
+    w2 = rng.choice(e2, (E, H, I)) / 8
+    w2[..., ::32] = 4.0 / 8
+    xq, xs = oracle_mod.mx_quantize(x.astype(np.float32), oracle_mod.MX_FP8)
+    w1q, w1s = oracle_mod.mx_quantize(w1.reshape(-1, H).astype(np.float32), oracle_mod.MX_FP4)
+    w2q, w2s = oracle_mod.mx_quantize(w2.reshape(-1, I).astype(np.float32), oracle_mod.MX_FP4)
+    assert np.array_equal(oracle_mod.mx_dequantize(xq, xs, H, oracle_mod.MX_FP8), x)
+    assert np.array_equal(oracle_mod.mx_dequantize(w1q, w1s, H, oracle_mod.MX_FP4), w1.reshape(-1, H))
+    rows = np.arange(6, dtype=np.int32)
+    rexp = np.array([0, 1, 0, 1, 1, 0], np.int32)
+    actq, acts, yp = oracle_mod.ffn_mx_rows(xq, xs, w1q.reshape(E, 2 * I, H // 2),
+                                            w1s.reshape(E, 2 * I, H // 32),
+                                            w2q.reshape(E, H, I // 2), w2s.reshape(E, H, I // 32),
+                                            H, I, rows, rexp)
+    act = oracle_mod.mx_dequantize(actq, acts, I, oracle_mod.MX_FP8)
+    for j in range(6):
+        g = torch.from_numpy(x[j]).double() @ torch.from_numpy(w1[rexp[j], :I]).double().T
+        u = torch.from_numpy(x[j]).double() @ torch.from_numpy(w1[rexp[j], I:]).double().T
+        a = (g / (1 + torch.exp(-g)) * u).numpy()
+        ab = np.abs(a.reshape(-1, 32))
+        scale = np.exp2(np.floor(np.log2(np.maximum(ab.max(1, keepdims=True), 1e-300))) - 8)
+        # half an E4M3 ulp (relative 2^-4, subnormal floor 2^-10 x scale) or saturation at 448
+        bound = np.maximum(np.maximum(ab / 16, scale * 2.0 ** -10), ab - 448 * scale)
+        assert np.all(np.abs(act[j] - a).reshape(-1, 32) <= bound * (1 + 1e-12))
+        ref = (torch.from_numpy(act[j]).double() @ torch.from_numpy(w2[rexp[j]]).double().T).numpy()
+        got = inputs.from_bf16_bits(yp[j]).double().numpy()
+        assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-30)
