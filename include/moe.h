@@ -12,6 +12,7 @@
  *   moe_expert_ffn  SwiGLU expert FFN over the block table (grouped GEMMs on bf16 MFMA);
  *                   moe_expert_ffn_gather reads the token rows of x directly
  *   moe_combine     routing-weight combine of each token's expert outputs
+ *   moe_mx_quantize MXFP8 / MXFP4 quantization (the low-precision expert path's inputs)
  *
  * Sources (the pages these calls restate; cited by title and section):
  *   [MF]  "MegaFlux: Skew-Resilient MoE Megakernels via Pipelined Expert Replication",
@@ -57,6 +58,10 @@ typedef enum {
 } moe_status_t;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+/* MX element formats (OCP Microscaling Formats v1.0): FP8 E4M3 (one byte per element) and
+ * FP4 E2M1 (two per byte, the lower-indexed element in the low nibble); one E8M0 scale byte
+ * per 32 consecutive elements of a row. */
+typedef enum { MOE_MX_FP8 = 0, MOE_MX_FP4 = 1 } moe_mx_format_t;
 
 /* Human-readable name of a status code (static string). */
 const char* moe_status_string(moe_status_t s);
@@ -210,6 +215,20 @@ moe_status_t moe_plan_blocks(const int32_t* expert_counts, int E, int expert_beg
                              int32_t* q, int32_t* moves, int32_t* n_moves, int max_moves,
                              int32_t* blocks, int32_t* n_blocks, int max_blocks,
                              int32_t* err_word, hipStream_t stream);
+
+/* Quantize to an MX format ([MF §4.1]: MXFP4 weights, MXFP8 activations; [MEP] cost model:
+ * packed 4-bit values plus one scale per 32 values).  src [rows, cols] in dt (cols a multiple
+ * of 32), row-major; per block of 32 consecutive values of a row, shared exponent
+ * X = floor(log2 max|v|) - emax (emax 8 for FP8 E4M3, 2 for FP4 E2M1; -127 for an all-zero
+ * block; clamped to [-127, 127]), scales[r * cols/32 + b] = X + 127 (E8M0), and each element
+ * v / 2^X rounded to the nearest code, ties to the even code, saturating at 448 / 6 (a zero
+ * result has no sign).
+ *   codes   out: [rows, cols] bytes (FP8) or [rows, cols / 2] bytes (FP4).
+ *   scales  out: [rows, cols / 32] bytes.
+ * src and codes 16-byte aligned.  Used for activations and, ahead of time, for weights. */
+moe_status_t moe_mx_quantize(const void* src, moe_dtype_t dt, int64_t rows, int64_t cols,
+                             moe_mx_format_t fmt, uint8_t* codes, uint8_t* scales,
+                             hipStream_t stream);
 
 /* ------------------------------------------------------------------- expert FFN --- */
 

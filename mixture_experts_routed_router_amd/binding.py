@@ -51,6 +51,7 @@ _SIGNATURES = {
     "moe_expert_ffn_tile_schedule": (_i32, [_vp, _vp, _i32, _i32, _vp, _i64, _vp]),
     "moe_plan_blocks": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32,
                                _vp, _vp, _i32, _vp, _vp]),
+    "moe_mx_quantize": (_i32, [_vp, _i32, _i64, _i64, _i32, _vp, _vp, _vp]),
     "moe_route_ref": (_i32, [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
     "moe_router_topk": (_i32, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
                                _vp]),
@@ -310,6 +311,22 @@ def moe_expert_ffn_fc2(act, w2, blocks, n_blocks, yp, workspace, stream=None):
                                     _ptr(workspace, torch.int32, "workspace"), workspace.numel(),
                                     _stream(stream)),
            "moe_expert_ffn_fc2")
+
+
+MOE_MX_FP8, MOE_MX_FP4 = 0, 1
+
+
+def moe_mx_quantize(src, fmt, codes, scales, stream=None):
+    """src [rows, cols] float32/bf16 -> codes uint8 [rows, cols] (FP8) or [rows, cols/2] (FP4),
+    scales uint8 [rows, cols/32] (E8M0)."""
+    rows, cols = src.shape
+    want = cols if fmt == MOE_MX_FP8 else cols // 2
+    if codes.shape != (rows, want) or scales.shape != (rows, cols // 32):
+        raise MoeError("moe_mx_quantize: codes / scales shapes do not match src")
+    _check(lib().moe_mx_quantize(_ptr(src, None, "src"), _dt(src), rows, cols, fmt,
+                                 _ptr(codes, torch.uint8, "codes"),
+                                 _ptr(scales, torch.uint8, "scales"), _stream(stream)),
+           "moe_mx_quantize")
 
 
 def moe_combine(yp, topk_w, entry_pos, out, stream=None):

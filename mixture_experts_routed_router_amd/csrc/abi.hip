@@ -264,6 +264,18 @@ moe_status_t moe_expert_ffn_gather(const void* x, const int32_t* row_token, int 
                               max_rows, workspace, workspace_elems, stream);
 }
 
+moe_status_t moe_mx_quantize(const void* src, moe_dtype_t dt, int64_t rows, int64_t cols,
+                             moe_mx_format_t fmt, uint8_t* codes, uint8_t* scales,
+                             hipStream_t stream) {
+    if (!src || !codes || !scales) return MOE_ERR_INVALID;
+    if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID;
+    if (fmt != MOE_MX_FP8 && fmt != MOE_MX_FP4) return MOE_ERR_INVALID;
+    if (rows < 0 || cols < 32 || cols % 32 != 0) return MOE_ERR_INVALID;
+    if (!aligned16(src) || !aligned16(codes)) return MOE_ERR_INVALID;
+    if (rows > ((int64_t)1 << 40) / cols) return MOE_ERR_UNSUPPORTED;
+    return launched(moe_launch_mx_quantize(src, dt, rows, cols, fmt, codes, scales, stream));
+}
+
 moe_status_t moe_combine(const void* yp, moe_dtype_t dt, const float* topk_w,
                          const int32_t* entry_pos, int T, int H, int K, void* out,
                          hipStream_t stream) {

@@ -46,6 +46,8 @@ hipError_t moe_launch_ffn_fc2(const void* act, const void* w2, moe_dtype_t dt, i
                               int32_t* ws, void* yp, int64_t max_rows,
                               hipStream_t stream);
 
+hipError_t moe_launch_mx_quantize(const void* src, moe_dtype_t dt, int64_t rows, int64_t cols,
+                                  int fmt, uint8_t* codes, uint8_t* scales, hipStream_t stream);
 hipError_t moe_launch_combine(const void* yp, moe_dtype_t dt, const float* w,
                               const int32_t* entry_pos, int T, int H, int K, void* out,
                               hipStream_t stream);

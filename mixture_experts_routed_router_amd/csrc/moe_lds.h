@@ -64,17 +64,34 @@ __device__ __forceinline__ void one_copy(uint32_t m0, const void* base, uint32_t
         : "memory");
 }
 
+// One 4-byte copy: 4 B per lane from base + lane offset to LDS address M0 + 4 lane.
+__device__ __forceinline__ void one_copy_dword(uint32_t m0, const void* base, uint32_t off) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %1, %3\n\t"
+        "s_nop 0\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(off), "s"(m0), "s"(base)
+        : "memory");
+}
+
 // Wait until at most n of this wave's copies are outstanding, then meet the workgroup.
-// n = pending stages (0, 1 or 2) x copies per stage (8, 6 or 5).
+// n = pending stages (0, 1 or 2) x copies per stage (8, 7, 6 or 5).
 #define MOE_WAIT_CASE(n)                                                                      \
     case n:                                                                                   \
         asm volatile("s_waitcnt vmcnt(" #n ")\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); \
         break;
 __device__ __forceinline__ void wait_copies_and_barrier(int n) {
     switch (n) {
+        MOE_WAIT_CASE(14)
         MOE_WAIT_CASE(12)
         MOE_WAIT_CASE(10)
         MOE_WAIT_CASE(8)
+        MOE_WAIT_CASE(7)
         MOE_WAIT_CASE(6)
         MOE_WAIT_CASE(5)
         default:

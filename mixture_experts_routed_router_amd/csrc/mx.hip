@@ -1,0 +1,125 @@
+// mx.hip -- quantization into the MX formats (moe_mx_quantize).
+//
+// MegaFlux §4.1 (Platform and configurations): the forward pass uses MXFP4 weights and MXFP8
+// activations; MoonEP's cost model: packed 4-bit elements plus one scale per 32 elements.  The
+// encodings are the OCP Microscaling Formats (MX) v1.0 ones: per block of 32 consecutive values
+// one E8M0 scale 2^(code - 127) with shared exponent floor(log2 max|v|) - emax (emax 8 for FP8
+// E4M3, 2 for FP4 E2M1; -127 for an all-zero block), elements v / scale rounded to nearest,
+// ties to even, saturating at the largest value (448 / 6).  FP4 codes pack two per byte, the
+// lower-indexed element in the low nibble.
+//
+// Four lanes per block, eight values per lane: 16- or 32-byte loads, the block maximum from two
+// lane swaps, then each lane converts its values with integer rounding (the scaled value is
+// exact: a power-of-two multiple of the input) and stores 8 (FP8) or 4 (FP4) bytes.
+#include "moe_launch.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// |a| (finite, already divided by the block scale) -> E4M3 magnitude code, nearest, ties even,
+// saturating at 448 (0x7E).
+__device__ __forceinline__ uint32_t e4m3_code(float a) {
+    if (a >= 448.f) return 0x7E;
+    if (a < 0.015625f) return (uint32_t)rintf(a * 512.f);  // subnormal: units of 2^-9 (8 = 2^-6)
+    const int e = ilogbf(a);                                // 2^e <= a < 2^(e+1), e in [-6, 8]
+    int q = (int)rintf((ldexpf(a, -e) - 1.f) * 8.f);
+    int eb = e + 7;
+    if (q == 8) {
+        q = 0;
+        eb += 1;
+    }
+    const uint32_t c = ((uint32_t)eb << 3) | (uint32_t)q;
+    return c > 0x7E ? 0x7E : c;
+}
+
+// |a| -> E2M1 magnitude code (values 0, 0.5, 1, 1.5, 2, 3, 4, 6), nearest, ties even, saturating.
+__device__ __forceinline__ uint32_t e2m1_code(float a) {
+    if (a >= 6.f) return 0x7;
+    if (a < 1.f) return (uint32_t)rintf(a * 2.f);  // 0, 0.5 (1), 1.0 (2)
+    const int e = ilogbf(a);                          // 0, 1 or 2
+    int q = (int)rintf((ldexpf(a, -e) - 1.f) * 2.f);
+    int eb = e + 1;
+    if (q == 2) {
+        q = 0;
+        eb += 1;
+    }
+    const uint32_t c = ((uint32_t)eb << 1) | (uint32_t)q;
+    return c > 0x7 ? 0x7 : c;
+}
+
+template <bool kBF16, bool kFP4>
+__global__ void __launch_bounds__(kThreads)
+mx_quantize_kernel(const uint8_t* __restrict__ src, int64_t n8, uint8_t* __restrict__ codes,
+                   uint8_t* __restrict__ scales) {
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < n8; g += stride) {
+        float v[8];
+        if (kBF16) {
+            const uint4 u = reinterpret_cast<const uint4*>(src)[g];
+            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[2 * i] = moe_bf16_to_f32((uint16_t)(w[i] & 0xFFFFu));
+                v[2 * i + 1] = moe_bf16_to_f32((uint16_t)(w[i] >> 16));
+            }
+        } else {
+            const uint4 u0 = reinterpret_cast<const uint4*>(src)[2 * g];
+            const uint4 u1 = reinterpret_cast<const uint4*>(src)[2 * g + 1];
+            const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(w[i]);
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+        // the block is the aligned group of 4 lanes (g % 4 == lane % 4)
+        amax = fmaxf(amax, __shfl_xor(amax, 1, MOE_WAVE));
+        amax = fmaxf(amax, __shfl_xor(amax, 2, MOE_WAVE));
+        int se = -127;
+        if (amax > 0.f) se = max(-127, min(127, ilogbf(amax) - (kFP4 ? 2 : 8)));
+        if ((g & 3) == 0) scales[g >> 2] = (uint8_t)(se + 127);
+        uint32_t c[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float s = ldexpf(v[i], -se);
+            const uint32_t m = kFP4 ? e2m1_code(fabsf(s)) : e4m3_code(fabsf(s));
+            const uint32_t sign = (s < 0.f && m != 0) ? (kFP4 ? 0x8u : 0x80u) : 0u;
+            c[i] = m | sign;
+        }
+        if (kFP4) {
+            uint32_t packed = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) packed |= c[i] << (4 * i);
+            reinterpret_cast<uint32_t*>(codes)[g] = packed;
+        } else {
+            uint2 o;
+            o.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+            o.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+            reinterpret_cast<uint2*>(codes)[g] = o;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t moe_launch_mx_quantize(const void* src, moe_dtype_t dt, int64_t rows, int64_t cols,
+                                  int fmt, uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+    const int64_t n8 = rows * cols / 8;
+    int64_t grid = (n8 + kThreads - 1) / kThreads;
+    if (grid > 8192) grid = 8192;
+    if (grid < 1) return hipSuccess;
+    const uint8_t* s = static_cast<const uint8_t*>(src);
+    if (dt == MOE_BF16) {
+        if (fmt == MOE_MX_FP4)
+            mx_quantize_kernel<true, true><<<(int)grid, kThreads, 0, stream>>>(s, n8, codes, scales);
+        else
+            mx_quantize_kernel<true, false><<<(int)grid, kThreads, 0, stream>>>(s, n8, codes, scales);
+    } else {
+        if (fmt == MOE_MX_FP4)
+            mx_quantize_kernel<false, true><<<(int)grid, kThreads, 0, stream>>>(s, n8, codes, scales);
+        else
+            mx_quantize_kernel<false, false><<<(int)grid, kThreads, 0, stream>>>(s, n8, codes, scales);
+    }
+    return hipGetLastError();
+}

@@ -132,6 +132,16 @@ def test_plan_blocks_rejects(lib):
     assert plan(s=70000) == UNSUPPORTED
 
 
+def test_mx_quantize_rejects(lib):
+    q = lambda src=P[0], dt=1, rows=4, cols=64, fmt=0, codes=P[1], scales=P[2]: \
+        lib.moe_mx_quantize(src, dt, rows, cols, fmt, codes, scales, NULL)
+    assert q(src=NULL) == INVALID
+    assert q(cols=48) == INVALID          # not a multiple of 32
+    assert q(fmt=2) == INVALID
+    assert q(dt=5) == INVALID
+    assert q(codes=ctypes.c_void_p(0x1004)) == INVALID  # misaligned
+
+
 def test_ffn_and_combine_reject(lib):
     ffn = lambda dt, H, I, blocks=P[3], ws_elems=272: lib.moe_expert_ffn(
         P[0], P[1], P[2], dt, H, I, 8, blocks, P[4], 16, P[5], P[6], 1024, P[7], ws_elems, NULL)
