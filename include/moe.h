@@ -13,6 +13,8 @@
  *                   moe_expert_ffn_gather reads the token rows of x directly
  *   moe_combine     routing-weight combine of each token's expert outputs
  *   moe_mx_quantize MXFP8 / MXFP4 quantization (the low-precision expert path's inputs)
+ *   moe_expert_ffn_mx  the expert FFN with MXFP4 weights and MXFP8 activations (block-scaled
+ *                   MFMA)
  *
  * Sources (the pages these calls restate; cited by title and section):
  *   [MF]  "MegaFlux: Skew-Resilient MoE Megakernels via Pipelined Expert Replication",
@@ -220,12 +222,19 @@ moe_status_t moe_plan_blocks(const int32_t* expert_counts, int E, int expert_beg
  * packed 4-bit values plus one scale per 32 values).  src [rows, cols] in dt (cols a multiple
  * of 32), row-major; per block of 32 consecutive values of a row, shared exponent
  * X = floor(log2 max|v|) - emax (emax 8 for FP8 E4M3, 2 for FP4 E2M1; -127 for an all-zero
- * block; clamped to [-127, 127]), scales[r * cols/32 + b] = X + 127 (E8M0), and each element
+ * block; clamped to [-127, 127]), scales[r * pitch + b] = X + 127 (E8M0), and each element
  * v / 2^X rounded to the nearest code, ties to the even code, saturating at 448 / 6 (a zero
  * result has no sign).
  *   codes   out: [rows, cols] bytes (FP8) or [rows, cols / 2] bytes (FP4).
- *   scales  out: [rows, cols / 32] bytes.
+ *   scales  out: [rows, pitch] bytes, pitch = moe_mx_scale_pitch(cols); the (pitch - cols/32)
+ *           padding bytes of a row are not written, and no consumer uses them as scales.
  * src and codes 16-byte aligned.  Used for activations and, ahead of time, for weights. */
+/* Bytes per row of an MX scale array for rows of `cols` values: cols / 32 rounded up to a
+ * multiple of 4, so that every row's scales start on a 4-byte boundary (the MX expert GEMM
+ * reads the 4 scales of a 128-value slice as one word).  Equals cols / 32 when cols is a
+ * multiple of 128. */
+int64_t moe_mx_scale_pitch(int64_t cols);
+
 moe_status_t moe_mx_quantize(const void* src, moe_dtype_t dt, int64_t rows, int64_t cols,
                              moe_mx_format_t fmt, uint8_t* codes, uint8_t* scales,
                              hipStream_t stream);
@@ -297,6 +306,49 @@ moe_status_t moe_expert_ffn_fc1_gather(const void* x, const int32_t* row_token, 
                                        int max_blocks, void* act, int64_t max_rows,
                                        int32_t* workspace, int64_t workspace_elems,
                                        hipStream_t stream);
+
+/* SwiGLU expert FFN with MXFP4 weights and MXFP8 activations ([MF §4.1]: the forward pass
+ * uses MXFP4 weights and MXFP8 activations; [MF §2.1]: FC1, SwiGLU, FC2).  MX values are those
+ * of moe_mx_quantize (OCP MX v1.0: element code times the block's E8M0 scale).  For every block
+ * (r, l, first, rows) and row p in [first, first + rows), with x~ the MXFP8 values of the input
+ * row (row row_token[p] of xq/xs when row_token is given, else row p) and W~ the MXFP4 weight
+ * values:
+ *   a[p][i]  = SiLU(x~ . W1~[l][i]) * (x~ . W1~[l][I + i])        i < I   (float32 accumulation)
+ *   actq/acts[p] = a[p] in MXFP8 (the moe_mx_quantize rule, from the float32 values)
+ *   yp[p][h] = bf16(act~[p] . W2~[l][h])                           h < H   (float32 accumulation)
+ *   xq    [x_rows, H] FP8 E4M3 codes; xs [x_rows, moe_mx_scale_pitch(H)] E8M0 scales.
+ *   row_token  [max_rows] from moe_permute (gather-on-load), or NULL: xq holds the permuted
+ *         rows (x_rows >= max_rows).
+ *   w1q   [E_loc, 2I, H/2] FP4 E2M1 codes (rows 0..I-1 gate, I..2I-1 up; two per byte, low
+ *         nibble first); w1s [E_loc, 2I, moe_mx_scale_pitch(H)].
+ *   w2q   [E_loc, H, I/2]; w2s [E_loc, H, moe_mx_scale_pitch(I)].
+ *   actq  out [max_rows, I] FP8 codes; acts out [max_rows, moe_mx_scale_pitch(I)] (pad bytes
+ *         not written).  yp out [max_rows, H] bf16.  Rows outside the blocks are not written.
+ *   workspace  as for moe_expert_ffn (the same tile schedule); one workspace per stream.
+ * Codes and yp 16-byte aligned, scale arrays 4-byte aligned (MOE_ERR_INVALID otherwise).
+ * H and I multiples of 64 (MOE_ERR_UNSUPPORTED otherwise); x_rows * H, max_rows * I and I * H
+ * below 4 GiB (32-bit row offsets; MOE_ERR_UNSUPPORTED otherwise). */
+moe_status_t moe_expert_ffn_mx(const uint8_t* xq, const uint8_t* xs, const int32_t* row_token,
+                               int64_t x_rows, const uint8_t* w1q, const uint8_t* w1s,
+                               const uint8_t* w2q, const uint8_t* w2s, int H, int I, int E_loc,
+                               const int32_t* blocks, const int32_t* n_blocks, int max_blocks,
+                               uint8_t* actq, uint8_t* acts, void* yp, int64_t max_rows,
+                               int32_t* workspace, int64_t workspace_elems, hipStream_t stream);
+
+/* The two halves of moe_expert_ffn_mx (same arguments and semantics): fc1 writes the tile
+ * schedule into `workspace` and actq/acts; fc2 reads them, so it must follow an fc1 call with
+ * the same blocks and workspace on the same stream. */
+moe_status_t moe_expert_ffn_mx_fc1(const uint8_t* xq, const uint8_t* xs, const int32_t* row_token,
+                                   int64_t x_rows, const uint8_t* w1q, const uint8_t* w1s, int H,
+                                   int I, int E_loc, const int32_t* blocks,
+                                   const int32_t* n_blocks, int max_blocks, uint8_t* actq,
+                                   uint8_t* acts, int64_t max_rows, int32_t* workspace,
+                                   int64_t workspace_elems, hipStream_t stream);
+moe_status_t moe_expert_ffn_mx_fc2(const uint8_t* actq, const uint8_t* acts, const uint8_t* w2q,
+                                   const uint8_t* w2s, int H, int I, int E_loc,
+                                   const int32_t* blocks, const int32_t* n_blocks, int max_blocks,
+                                   void* yp, int64_t max_rows, int32_t* workspace,
+                                   int64_t workspace_elems, hipStream_t stream);
 
 /* ---------------------------------------------------------------------- combine --- */
 

@@ -52,6 +52,13 @@ _SIGNATURES = {
     "moe_plan_blocks": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32,
                                _vp, _vp, _i32, _vp, _vp]),
     "moe_mx_quantize": (_i32, [_vp, _i32, _i64, _i64, _i32, _vp, _vp, _vp]),
+    "moe_mx_scale_pitch": (_i64, [_i64]),
+    "moe_expert_ffn_mx": (_i32, [_vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp,
+                                 _vp, _i32, _vp, _vp, _vp, _i64, _vp, _i64, _vp]),
+    "moe_expert_ffn_mx_fc1": (_i32, [_vp, _vp, _vp, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _vp,
+                                     _i32, _vp, _vp, _i64, _vp, _i64, _vp]),
+    "moe_expert_ffn_mx_fc2": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _i32, _vp,
+                                     _i64, _vp, _i64, _vp]),
     "moe_route_ref": (_i32, [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
     "moe_router_topk": (_i32, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
                                _vp]),
@@ -316,17 +323,102 @@ def moe_expert_ffn_fc2(act, w2, blocks, n_blocks, yp, workspace, stream=None):
 MOE_MX_FP8, MOE_MX_FP4 = 0, 1
 
 
+def moe_mx_scale_pitch(cols: int) -> int:
+    """Bytes per row of an MX scale array for rows of `cols` values (cols/32 rounded up to 4)."""
+    return int(lib().moe_mx_scale_pitch(cols))
+
+
 def moe_mx_quantize(src, fmt, codes, scales, stream=None):
-    """src [rows, cols] float32/bf16 -> codes uint8 [rows, cols] (FP8) or [rows, cols/2] (FP4),
-    scales uint8 [rows, cols/32] (E8M0)."""
-    rows, cols = src.shape
+    """src [..., rows, cols] float32/bf16 -> codes uint8 [..., cols] (FP8) or [..., cols/2] (FP4),
+    scales uint8 [..., moe_mx_scale_pitch(cols)] (E8M0); leading dimensions are flattened."""
+    cols = src.shape[-1]
+    rows = src.numel() // cols if cols else 0
     want = cols if fmt == MOE_MX_FP8 else cols // 2
-    if codes.shape != (rows, want) or scales.shape != (rows, cols // 32):
+    pitch = moe_mx_scale_pitch(cols)
+    if (codes.shape[:-1] != src.shape[:-1] or codes.shape[-1] != want
+            or scales.shape[:-1] != src.shape[:-1] or scales.shape[-1] != pitch):
         raise MoeError("moe_mx_quantize: codes / scales shapes do not match src")
     _check(lib().moe_mx_quantize(_ptr(src, None, "src"), _dt(src), rows, cols, fmt,
                                  _ptr(codes, torch.uint8, "codes"),
                                  _ptr(scales, torch.uint8, "scales"), _stream(stream)),
            "moe_mx_quantize")
+
+
+def _mx_ffn_shapes(call, w1q, w2q, actq, yp):
+    E_loc, two_I, H2 = w1q.shape
+    I, H = two_I // 2, 2 * H2
+    if w2q.shape != (E_loc, H, I // 2):
+        raise MoeError(f"{call}: w2q must be [E_loc, H, I/2] = {(E_loc, H, I // 2)}")
+    if actq is not None and actq.shape[1] != I:
+        raise MoeError(f"{call}: actq must have I = {I} columns")
+    if yp is not None and (yp.shape[1] != H or yp.dtype != torch.bfloat16):
+        raise MoeError(f"{call}: yp must be bf16 with H = {H} columns")
+    return E_loc, H, I
+
+
+def _mx_scales(call, s, lead, cols, name):
+    want = tuple(lead) + (moe_mx_scale_pitch(cols),)
+    if tuple(s.shape) != want:
+        raise MoeError(f"{call}: {name} must be {want}, got {tuple(s.shape)}")
+    return _ptr(s, torch.uint8, name)
+
+
+def moe_expert_ffn_mx_fc1(xq, xs, row_token, w1q, w1s, blocks, n_blocks, actq, acts, workspace,
+                          stream=None):
+    """FC1 with MXFP8 input rows (xq/xs; gathered by row_token when given) and MXFP4 W1; the
+    activation leaves in MXFP8 (actq/acts)."""
+    call = "moe_expert_ffn_mx_fc1"
+    E_loc, two_I, H2 = w1q.shape
+    I, H = two_I // 2, 2 * H2
+    rows = actq.shape[0]
+    if xq.shape[1] != H or actq.shape[1] != I:
+        raise MoeError(f"{call}: inconsistent shapes")
+    if row_token is not None and row_token.shape[0] > rows:
+        raise MoeError(f"{call}: actq has fewer rows than row_token")
+    _check(lib().moe_expert_ffn_mx_fc1(
+        _ptr(xq, torch.uint8, "xq"), _mx_scales(call, xs, xq.shape[:1], H, "xs"),
+        _ptr(row_token, torch.int32, "row_token"), xq.shape[0], _ptr(w1q, torch.uint8, "w1q"),
+        _mx_scales(call, w1s, w1q.shape[:2], H, "w1s"), H, I, E_loc,
+        _ptr(blocks, torch.int32, "blocks"), _ptr(n_blocks, torch.int32, "n_blocks"),
+        blocks.shape[0], _ptr(actq, torch.uint8, "actq"),
+        _mx_scales(call, acts, actq.shape[:1], I, "acts"), rows,
+        _ptr(workspace, torch.int32, "workspace"), workspace.numel(), _stream(stream)), call)
+
+
+def moe_expert_ffn_mx_fc2(actq, acts, w2q, w2s, blocks, n_blocks, yp, workspace, stream=None):
+    call = "moe_expert_ffn_mx_fc2"
+    E_loc, H, I2 = w2q.shape
+    I = 2 * I2
+    rows = actq.shape[0]
+    if actq.shape[1] != I or yp.shape != (rows, H) or yp.dtype != torch.bfloat16:
+        raise MoeError(f"{call}: inconsistent shapes")
+    _check(lib().moe_expert_ffn_mx_fc2(
+        _ptr(actq, torch.uint8, "actq"), _mx_scales(call, acts, actq.shape[:1], I, "acts"),
+        _ptr(w2q, torch.uint8, "w2q"), _mx_scales(call, w2s, w2q.shape[:2], I, "w2s"), H, I,
+        E_loc, _ptr(blocks, torch.int32, "blocks"), _ptr(n_blocks, torch.int32, "n_blocks"),
+        blocks.shape[0], _ptr(yp, torch.bfloat16, "yp"), rows,
+        _ptr(workspace, torch.int32, "workspace"), workspace.numel(), _stream(stream)), call)
+
+
+def moe_expert_ffn_mx(xq, xs, row_token, w1q, w1s, w2q, w2s, blocks, n_blocks, actq, acts, yp,
+                      workspace, stream=None):
+    """The SwiGLU expert FFN with MXFP4 weights and MXFP8 activations (FC1 then FC2)."""
+    call = "moe_expert_ffn_mx"
+    E_loc, H, I = _mx_ffn_shapes(call, w1q, w2q, actq, yp)
+    rows = actq.shape[0]
+    if xq.shape[1] != H or yp.shape[0] != rows:
+        raise MoeError(f"{call}: inconsistent shapes")
+    if row_token is not None and row_token.shape[0] > rows:
+        raise MoeError(f"{call}: actq has fewer rows than row_token")
+    _check(lib().moe_expert_ffn_mx(
+        _ptr(xq, torch.uint8, "xq"), _mx_scales(call, xs, xq.shape[:1], H, "xs"),
+        _ptr(row_token, torch.int32, "row_token"), xq.shape[0], _ptr(w1q, torch.uint8, "w1q"),
+        _mx_scales(call, w1s, w1q.shape[:2], H, "w1s"), _ptr(w2q, torch.uint8, "w2q"),
+        _mx_scales(call, w2s, w2q.shape[:2], I, "w2s"), H, I, E_loc,
+        _ptr(blocks, torch.int32, "blocks"), _ptr(n_blocks, torch.int32, "n_blocks"),
+        blocks.shape[0], _ptr(actq, torch.uint8, "actq"),
+        _mx_scales(call, acts, actq.shape[:1], I, "acts"), _ptr(yp, torch.bfloat16, "yp"), rows,
+        _ptr(workspace, torch.int32, "workspace"), workspace.numel(), _stream(stream)), call)
 
 
 def moe_combine(yp, topk_w, entry_pos, out, stream=None):

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["abi.hip", "route.hip", "router.hip", "permute.hip", "plan.hip", "plan_blocks.hip", "ffn.hip", "combine.hip", "mx.hip"]
+SOURCES = ["abi.hip", "route.hip", "router.hip", "permute.hip", "plan.hip", "plan_blocks.hip", "ffn.hip", "combine.hip", "mx.hip", "ffn_mx.hip"]
 
 
 def hipcc() -> str:

@@ -264,6 +264,8 @@ moe_status_t moe_expert_ffn_gather(const void* x, const int32_t* row_token, int 
                               max_rows, workspace, workspace_elems, stream);
 }
 
+int64_t moe_mx_scale_pitch(int64_t cols) { return cols < 0 ? 0 : moe_mx_scale_pitch_impl(cols); }
+
 moe_status_t moe_mx_quantize(const void* src, moe_dtype_t dt, int64_t rows, int64_t cols,
                              moe_mx_format_t fmt, uint8_t* codes, uint8_t* scales,
                              hipStream_t stream) {
@@ -274,6 +276,78 @@ moe_status_t moe_mx_quantize(const void* src, moe_dtype_t dt, int64_t rows, int6
     if (!aligned16(src) || !aligned16(codes)) return MOE_ERR_INVALID;
     if (rows > ((int64_t)1 << 40) / cols) return MOE_ERR_UNSUPPORTED;
     return launched(moe_launch_mx_quantize(src, dt, rows, cols, fmt, codes, scales, stream));
+}
+
+namespace {
+
+bool aligned4(const void* p) { return ((uintptr_t)p & 3) == 0; }
+
+moe_status_t check_ffn_mx_shape(int H, int I, int E_loc, int max_blocks, int64_t max_rows,
+                                const int32_t* blocks, const int32_t* n_blocks,
+                                const int32_t* workspace, int64_t workspace_elems) {
+    if (!blocks || !n_blocks || !workspace) return MOE_ERR_INVALID;
+    if (H < 64 || I < 64 || E_loc < 1 || max_blocks < 1 || max_rows < 1) return MOE_ERR_INVALID;
+    if (H % 64 != 0 || I % 64 != 0) return MOE_ERR_UNSUPPORTED;
+    if (workspace_elems < moe_ffn_workspace_elems(max_blocks)) return MOE_ERR_INVALID;
+    if (E_loc > 256) return MOE_ERR_UNSUPPORTED;
+    // the GEMMs address rows with 32-bit byte offsets: token rows (x or act) and one expert's
+    // weight rows
+    const int64_t lim = 0xFFFFFFFFLL - 256;
+    if (max_rows * I > lim || (int64_t)I * H > lim) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+}  // namespace
+
+moe_status_t moe_expert_ffn_mx_fc1(const uint8_t* xq, const uint8_t* xs, const int32_t* row_token,
+                                   int64_t x_rows, const uint8_t* w1q, const uint8_t* w1s, int H,
+                                   int I, int E_loc, const int32_t* blocks,
+                                   const int32_t* n_blocks, int max_blocks, uint8_t* actq,
+                                   uint8_t* acts, int64_t max_rows, int32_t* workspace,
+                                   int64_t workspace_elems, hipStream_t stream) {
+    if (!xq || !xs || !w1q || !w1s || !actq || !acts) return MOE_ERR_INVALID;
+    if (!aligned16(xq) || !aligned16(w1q) || !aligned16(actq)) return MOE_ERR_INVALID;
+    if (!aligned4(xs) || !aligned4(w1s)) return MOE_ERR_INVALID;
+    moe_status_t st = check_ffn_mx_shape(H, I, E_loc, max_blocks, max_rows, blocks, n_blocks,
+                                         workspace, workspace_elems);
+    if (st != MOE_OK) return st;
+    if (x_rows < 1 || (!row_token && x_rows < max_rows)) return MOE_ERR_INVALID;
+    if (x_rows * H > 0xFFFFFFFFLL - 256) return MOE_ERR_UNSUPPORTED;
+    st = launched(moe_launch_ffn_schedule(blocks, n_blocks, max_blocks, E_loc, workspace, stream));
+    if (st != MOE_OK) return st;
+    return launched(moe_launch_ffn_mx_fc1(xq, xs, row_token, w1q, w1s, H, I, max_blocks, workspace,
+                                          actq, acts, stream));
+}
+
+moe_status_t moe_expert_ffn_mx_fc2(const uint8_t* actq, const uint8_t* acts, const uint8_t* w2q,
+                                   const uint8_t* w2s, int H, int I, int E_loc,
+                                   const int32_t* blocks, const int32_t* n_blocks, int max_blocks,
+                                   void* yp, int64_t max_rows, int32_t* workspace,
+                                   int64_t workspace_elems, hipStream_t stream) {
+    if (!actq || !acts || !w2q || !w2s || !yp) return MOE_ERR_INVALID;
+    if (!aligned16(actq) || !aligned16(w2q) || !aligned16(yp)) return MOE_ERR_INVALID;
+    if (!aligned4(acts) || !aligned4(w2s)) return MOE_ERR_INVALID;
+    moe_status_t st = check_ffn_mx_shape(H, I, E_loc, max_blocks, max_rows, blocks, n_blocks,
+                                         workspace, workspace_elems);
+    if (st != MOE_OK) return st;
+    return launched(moe_launch_ffn_mx_fc2(actq, acts, w2q, w2s, H, I, max_blocks, workspace,
+                                          static_cast<uint16_t*>(yp), stream));
+}
+
+moe_status_t moe_expert_ffn_mx(const uint8_t* xq, const uint8_t* xs, const int32_t* row_token,
+                               int64_t x_rows, const uint8_t* w1q, const uint8_t* w1s,
+                               const uint8_t* w2q, const uint8_t* w2s, int H, int I, int E_loc,
+                               const int32_t* blocks, const int32_t* n_blocks, int max_blocks,
+                               uint8_t* actq, uint8_t* acts, void* yp, int64_t max_rows,
+                               int32_t* workspace, int64_t workspace_elems, hipStream_t stream) {
+    if (!w2q || !w2s || !yp || !aligned16(w2q) || !aligned16(yp) || !aligned4(w2s))
+        return MOE_ERR_INVALID;
+    moe_status_t st = moe_expert_ffn_mx_fc1(xq, xs, row_token, x_rows, w1q, w1s, H, I, E_loc,
+                                            blocks, n_blocks, max_blocks, actq, acts, max_rows,
+                                            workspace, workspace_elems, stream);
+    if (st != MOE_OK) return st;
+    return moe_expert_ffn_mx_fc2(actq, acts, w2q, w2s, H, I, E_loc, blocks, n_blocks, max_blocks,
+                                 yp, max_rows, workspace, workspace_elems, stream);
 }
 
 moe_status_t moe_combine(const void* yp, moe_dtype_t dt, const float* topk_w,

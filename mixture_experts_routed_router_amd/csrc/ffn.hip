@@ -28,30 +28,15 @@
 // Block and tile counts are read on the device; there is no host round trip.
 #include "moe_launch.h"
 #include "moe_lds.h"
+#include "moe_ffn_ws.h"
 
 namespace {
 
-constexpr int HALF = 128;    // rows per tile half (= the plan's largest block at beta 128)
+using namespace moe_ffn_ws;
 constexpr int BN = 256;      // B rows per tile (FC1: 128 gate + 128 up; FC2: 256 columns of H)
 constexpr int BK = 64;       // K slice per LDS stage: 128-byte rows = whole cache lines
 constexpr int kWaves = 8;    // two waves per SIMD
 constexpr int kThreads = kWaves * MOE_WAVE;
-constexpr int kXcds = 8;
-// FFN workspace (int32): [0] tile count; [8 + x] FC1 item counter of XCD x, [16 + x] FC2's;
-// [24] FC1 / [25] FC2 finished-workgroup counters; from [32]: max_blocks block indices
-// sorted by expert, then the tiles, 7 ints each (expert, first row and row count of half 0,
-// first row and row count of half 1 (count 0 = no half 1), the expert's first tile and its
-// tile count).
-constexpr int WS_NTILES = 0, WS_CTR_FC1 = 8, WS_CTR_FC2 = 16, WS_DONE_FC1 = 24, WS_DONE_FC2 = 25;
-constexpr int WS_HEAD = 32;
-constexpr int TILE_INTS = 7;
-// Items of one expert are taken in groups of up to GROUP_TILES tiles, column tile by column
-// tile within a group: the items in flight on an XCD then share a few A tiles and a few B
-// column tiles, which stay in its L2 instead of being fetched again from HBM.
-#ifndef GROUP_TILES
-#define GROUP_TILES 4
-#endif
-constexpr int kGroupTiles = GROUP_TILES;
 constexpr int ROW_BYTES = BK * 2;           // 128
 constexpr int SEG_ROWS = 1024 / ROW_BYTES;  // 8 rows per 1 KB copy
 constexpr int B_REGION = BN * ROW_BYTES;    // 32 KB of B rows per stage

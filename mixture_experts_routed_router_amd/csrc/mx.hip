@@ -12,46 +12,16 @@
 // lane swaps, then each lane converts its values with integer rounding (the scaled value is
 // exact: a power-of-two multiple of the input) and stores 8 (FP8) or 4 (FP4) bytes.
 #include "moe_launch.h"
+#include "moe_mx.h"
 
 namespace {
 
 constexpr int kThreads = 256;
 
-// |a| (finite, already divided by the block scale) -> E4M3 magnitude code, nearest, ties even,
-// saturating at 448 (0x7E).
-__device__ __forceinline__ uint32_t e4m3_code(float a) {
-    if (a >= 448.f) return 0x7E;
-    if (a < 0.015625f) return (uint32_t)rintf(a * 512.f);  // subnormal: units of 2^-9 (8 = 2^-6)
-    const int e = ilogbf(a);                                // 2^e <= a < 2^(e+1), e in [-6, 8]
-    int q = (int)rintf((ldexpf(a, -e) - 1.f) * 8.f);
-    int eb = e + 7;
-    if (q == 8) {
-        q = 0;
-        eb += 1;
-    }
-    const uint32_t c = ((uint32_t)eb << 3) | (uint32_t)q;
-    return c > 0x7E ? 0x7E : c;
-}
-
-// |a| -> E2M1 magnitude code (values 0, 0.5, 1, 1.5, 2, 3, 4, 6), nearest, ties even, saturating.
-__device__ __forceinline__ uint32_t e2m1_code(float a) {
-    if (a >= 6.f) return 0x7;
-    if (a < 1.f) return (uint32_t)rintf(a * 2.f);  // 0, 0.5 (1), 1.0 (2)
-    const int e = ilogbf(a);                          // 0, 1 or 2
-    int q = (int)rintf((ldexpf(a, -e) - 1.f) * 2.f);
-    int eb = e + 1;
-    if (q == 2) {
-        q = 0;
-        eb += 1;
-    }
-    const uint32_t c = ((uint32_t)eb << 1) | (uint32_t)q;
-    return c > 0x7 ? 0x7 : c;
-}
-
 template <bool kBF16, bool kFP4>
 __global__ void __launch_bounds__(kThreads)
-mx_quantize_kernel(const uint8_t* __restrict__ src, int64_t n8, uint8_t* __restrict__ codes,
-                   uint8_t* __restrict__ scales) {
+mx_quantize_kernel(const uint8_t* __restrict__ src, int64_t n8, int64_t nb, int64_t pitch,
+                   uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
     const int64_t stride = (int64_t)gridDim.x * kThreads;
     for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < n8; g += stride) {
         float v[8];
@@ -76,9 +46,11 @@ mx_quantize_kernel(const uint8_t* __restrict__ src, int64_t n8, uint8_t* __restr
         // the block is the aligned group of 4 lanes (g % 4 == lane % 4)
         amax = fmaxf(amax, __shfl_xor(amax, 1, MOE_WAVE));
         amax = fmaxf(amax, __shfl_xor(amax, 2, MOE_WAVE));
-        int se = -127;
-        if (amax > 0.f) se = max(-127, min(127, ilogbf(amax) - (kFP4 ? 2 : 8)));
-        if ((g & 3) == 0) scales[g >> 2] = (uint8_t)(se + 127);
+        const int se = mx_shared_exp(amax, kFP4 ? 2 : 8);
+        if ((g & 3) == 0) {
+            const int64_t b = g >> 2, row = b / nb;  // block b = (row, b - row * nb)
+            scales[row * pitch + (b - row * nb)] = (uint8_t)(se + 127);
+        }
         uint32_t c[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -105,21 +77,21 @@ mx_quantize_kernel(const uint8_t* __restrict__ src, int64_t n8, uint8_t* __restr
 
 hipError_t moe_launch_mx_quantize(const void* src, moe_dtype_t dt, int64_t rows, int64_t cols,
                                   int fmt, uint8_t* codes, uint8_t* scales, hipStream_t stream) {
-    const int64_t n8 = rows * cols / 8;
+    const int64_t n8 = rows * cols / 8, nb = cols / 32, pitch = moe_mx_scale_pitch_impl(cols);
     int64_t grid = (n8 + kThreads - 1) / kThreads;
     if (grid > 8192) grid = 8192;
     if (grid < 1) return hipSuccess;
     const uint8_t* s = static_cast<const uint8_t*>(src);
     if (dt == MOE_BF16) {
         if (fmt == MOE_MX_FP4)
-            mx_quantize_kernel<true, true><<<(int)grid, kThreads, 0, stream>>>(s, n8, codes, scales);
+            mx_quantize_kernel<true, true><<<(int)grid, kThreads, 0, stream>>>(s, n8, nb, pitch, codes, scales);
         else
-            mx_quantize_kernel<true, false><<<(int)grid, kThreads, 0, stream>>>(s, n8, codes, scales);
+            mx_quantize_kernel<true, false><<<(int)grid, kThreads, 0, stream>>>(s, n8, nb, pitch, codes, scales);
     } else {
         if (fmt == MOE_MX_FP4)
-            mx_quantize_kernel<false, true><<<(int)grid, kThreads, 0, stream>>>(s, n8, codes, scales);
+            mx_quantize_kernel<false, true><<<(int)grid, kThreads, 0, stream>>>(s, n8, nb, pitch, codes, scales);
         else
-            mx_quantize_kernel<false, false><<<(int)grid, kThreads, 0, stream>>>(s, n8, codes, scales);
+            mx_quantize_kernel<false, false><<<(int)grid, kThreads, 0, stream>>>(s, n8, nb, pitch, codes, scales);
     }
     return hipGetLastError();
 }

@@ -142,6 +142,34 @@ def test_mx_quantize_rejects(lib):
     assert q(codes=ctypes.c_void_p(0x1004)) == INVALID  # misaligned
 
 
+def test_mx_scale_pitch(lib):
+    assert lib.moe_mx_scale_pitch(2048) == 64
+    assert lib.moe_mx_scale_pitch(2880) == 92   # 90 scales, padded to a multiple of 4
+    assert lib.moe_mx_scale_pitch(64) == 4
+    assert lib.moe_mx_scale_pitch(32) == 4
+
+
+def test_mx_ffn_rejects(lib):
+    def ffn(xq=P[0], xs=P[1], row_token=P[2], x_rows=64, H=128, I=256, blocks=P[3],
+            ws_elems=272, max_rows=1024, w1s=P[5]):
+        return lib.moe_expert_ffn_mx(xq, xs, row_token, x_rows, P[4], w1s, P[6], P[7], H, I, 8,
+                                     blocks, P[8], 16, P[9], P[10], P[11], max_rows, P[12],
+                                     ws_elems, NULL)
+    assert ffn(xq=NULL) == INVALID
+    assert ffn(blocks=NULL) == INVALID
+    assert ffn(xq=ctypes.c_void_p(0x1008)) == INVALID        # codes 16-byte aligned
+    assert ffn(w1s=ctypes.c_void_p(0x1002)) == INVALID       # scales 4-byte aligned
+    assert ffn(H=96) == UNSUPPORTED                          # multiples of 64
+    assert ffn(I=2880 + 32) == UNSUPPORTED
+    assert ffn(H=32) == INVALID
+    assert ffn(ws_elems=271) == INVALID
+    assert ffn(x_rows=0) == INVALID
+    assert ffn(row_token=NULL, x_rows=1000) == INVALID       # materialised rows < max_rows
+    assert ffn(x_rows=1 << 23, H=1024) == UNSUPPORTED        # 8 GiB of codes: 32-bit offsets
+    assert lib.moe_expert_ffn_mx_fc2(P[0], P[1], P[2], P[3], 128, 256, 8, P[4], P[5], 16,
+                                     ctypes.c_void_p(0x1008), 1024, P[6], 272, NULL) == INVALID
+
+
 def test_ffn_and_combine_reject(lib):
     ffn = lambda dt, H, I, blocks=P[3], ws_elems=272: lib.moe_expert_ffn(
         P[0], P[1], P[2], dt, H, I, 8, blocks, P[4], 16, P[5], P[6], 1024, P[7], ws_elems, NULL)

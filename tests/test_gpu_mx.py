@@ -16,10 +16,14 @@ def _gpu_quantize(t, fmt):
     rows, cols = t.shape
     codes = torch.full((rows, cols if fmt == binding.MOE_MX_FP8 else cols // 2), 0xAA,
                        dtype=torch.uint8, device="cuda")
-    scales = torch.full((rows, cols // 32), 0xAA, dtype=torch.uint8, device="cuda")
+    pitch = binding.moe_mx_scale_pitch(cols)
+    scales = torch.full((rows, pitch), 0xAA, dtype=torch.uint8, device="cuda")
     binding.moe_mx_quantize(t.cuda(), fmt, codes, scales)
     torch.cuda.synchronize()
-    return host(codes), host(scales)
+    s = host(scales)
+    # the padding of a scale row (pitch > cols / 32) is not written
+    assert (s[:, cols // 32:] == 0xAA).all()
+    return host(codes), s[:, : cols // 32]
 
 
 def _check(t, label):
@@ -48,6 +52,14 @@ def test_mx_quantize_ties_and_saturation():
     fp8 = [448.0] + [1 + k / 16 for k in range(16)] + [2.0 ** -10 * k for k in range(15)]
     _check(torch.tensor([fp4, fp8], dtype=torch.float32), "midpoints")
     _check(torch.tensor([fp4, fp8], dtype=torch.float32).to(torch.bfloat16), "midpoints bf16")
+
+
+def test_mx_quantize_padded_scale_rows():
+    """Rows of 2880 values (90 scales, padded to 92 per row) and of 64 values (2 -> 4)."""
+    rng = np.random.default_rng(23)
+    _check(torch.from_numpy(rng.standard_normal((33, 2880), dtype=np.float32)).to(torch.bfloat16),
+           "2880 cols")
+    _check(torch.from_numpy(rng.standard_normal((5, 64), dtype=np.float32)), "64 cols")
 
 
 def test_mx_quantize_expert_weights():
