@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "routed-expert layer tokens/s + grouped-GEMM TFLOP/s (% MFMA peak) vs skew"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA (the MX path's FP4 x FP8 products)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
@@ -50,6 +51,11 @@ def parse():
                          "about 12 s of CPU work)")
     ap.add_argument("--no-all-skews", action="store_true",
                     help="skip timing every skew of the workload (the by_skew field)")
+    ap.add_argument("--precision", choices=("bf16", "mx"), default="bf16",
+                    help="bf16 expert GEMMs (the default) or the MX path: MXFP4 weights, MXFP8 "
+                         "activations (x quantized inside the step)")
+    ap.add_argument("--no-mx-summary", action="store_true",
+                    help="skip the MX path's summary (mx_path) in a bf16 run")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a reference for "
                          "hardware byte counters)")
@@ -71,26 +77,24 @@ class Step:
     """The path's calls on one stream, with optional HIP events between them."""
 
     CALLS = ("route", "permute", "plan", "fc1", "fc2", "combine")
+    CALLS_MX = ("route", "permute", "quantize_x", "plan", "fc1", "fc2", "combine")
 
     def __init__(self, layer, logits, x, W1, W2):
         self.layer, self.logits, self.x, self.W1, self.W2 = layer, logits, x, W1, W2
+        self.calls = self.CALLS_MX if layer.precision == "mx" else self.CALLS
 
     def run(self, events=None):
         L = self.layer
-        rec = (lambda i: events[i].record()) if events is not None else (lambda i: None)
-        rec(0)
-        L.route(self.logits)
-        rec(1)
-        L.permute(self.x)
-        rec(2)
-        L.plan()
-        rec(3)
-        L.expert_ffn_fc1(self.W1)
-        rec(4)
-        L.expert_ffn_fc2(self.W2)
-        rec(5)
-        L.combine()
-        rec(6)
+        fns = {"route": lambda: L.route(self.logits), "permute": lambda: L.permute(self.x),
+               "quantize_x": lambda: L.quantize_x(self.x), "plan": L.plan,
+               "fc1": lambda: L.expert_ffn_fc1(self.W1), "fc2": lambda: L.expert_ffn_fc2(self.W2),
+               "combine": L.combine}
+        if events is not None:
+            events[0].record()
+        for i, c in enumerate(self.calls):
+            fns[c]()
+            if events is not None:
+                events[i + 1].record()
 
 
 def time_steps(step, steps, warmup, torch, graph=None):
@@ -106,12 +110,13 @@ def time_steps(step, steps, warmup, torch, graph=None):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
     # per-call durations: HIP events on the stream the kernels are launched on
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(step.calls) + 1)]
+          for _ in range(steps)]
     for i in range(steps):
         step.run(ev[i])
     torch.cuda.synchronize()
     per = {c: sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)) / steps * 1e3
-           for j, c in enumerate(Step.CALLS)}
+           for j, c in enumerate(step.calls)}
     # the FC1 call starts with the tile-schedule kernel: time it alone on the same table, so
     # that the FC1 GEMM kernel's own duration is fc1 - schedule
     if step.layer.dtype == torch.bfloat16:
@@ -125,12 +130,12 @@ def time_steps(step, steps, warmup, torch, graph=None):
     return wall, per
 
 
-def ffn_roofline(w, n_loc, eb):
+def ffn_roofline(w, n_loc, eb, peak=PEAK_BF16_TFLOPS):
     """Per-expert roofline of the two expert GEMMs: each touched expert costs the larger of
     its valid-row flops at the MFMA peak and one read of its weights (3 H I values) at the
     HBM peak.  Returns (t_roof seconds, touched experts, weight bytes of touched experts,
     bound of the sum: 'mfma' or 'hbm')."""
-    per_flop = 6.0 * w.H * w.I / (PEAK_BF16_TFLOPS * 1e12)
+    per_flop = 6.0 * w.H * w.I / (peak * 1e12)
     wbytes = 3.0 * w.H * w.I * eb
     per_byte = wbytes / (PEAK_HBM_GBS * 1e9)
     touched = [int(n) for n in n_loc if n > 0]
@@ -140,22 +145,25 @@ def ffn_roofline(w, n_loc, eb):
     return t_roof, len(touched), len(touched) * wbytes, bound
 
 
-def ffn_traffic(workload: str):
+def ffn_traffic(workload: str, precision: str = "bf16"):
     """HBM bytes per FC1 launch from committed rocprofv3 counter runs, if they were taken on
     the current FC1 kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"fc1_{workload}_traffic.json")
+    tag = "fc1_mx" if precision == "mx" else "fc1"
+    path = os.path.join(ROOT, "profiles", f"{tag}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("ffn_source_sha256") != ffn_source_sha256():
+    if rec.get("ffn_source_sha256") != ffn_source_sha256(precision):
         return None
     return rec.get("bytes_per_launch")
 
 
-def ffn_source_sha256() -> str:
-    """SHA-256 over the FC1 kernel's sources (ffn.hip, then the staging header it includes)."""
+def ffn_source_sha256(precision: str = "bf16") -> str:
+    """SHA-256 over the FC1 kernel's sources (the kernel file, then the headers it includes)."""
+    files = (("ffn_mx.hip", "moe_lds.h", "moe_ffn_ws.h", "moe_mx.h") if precision == "mx" else
+             ("ffn.hip", "moe_lds.h", "moe_ffn_ws.h"))
     h = hashlib.sha256()
-    for f in ("ffn.hip", "moe_lds.h"):
+    for f in files:
         h.update(open(os.path.join(ROOT, "mixture_experts_routed_router_amd", "csrc", f), "rb").read())
     return h.hexdigest()
 
@@ -192,10 +200,12 @@ def plan_comparison(layer, w, steps, torch):
     return res
 
 
-def cpu_baseline(w, skew, T_s, target_s=12.0):
+def cpu_baseline(w, skew, T_s, target_s=12.0, precision="bf16"):
     """The CPU oracle, as it stands, over the first tokens of the same batch (whole path).
     A first pass over T_s tokens sizes the measured sample to about target_s seconds of CPU
-    work (at most the whole batch, a multiple of P tokens)."""
+    work (at most the whole batch, a multiple of P tokens).  precision "mx": the oracle's MX
+    path (x quantized to MXFP8 inside the timed pass; the weights' MXFP4 codes prepared once,
+    outside it, as the GPU path's are)."""
     sys.path.insert(0, os.path.join(ROOT, "oracle"))
     import oracle
     from mixture_experts_routed_router_amd import inputs
@@ -204,6 +214,21 @@ def cpu_baseline(w, skew, T_s, target_s=12.0):
     x_all = inputs.as_oracle_array(inputs.make_x(w))
     W1, W2 = (inputs.as_oracle_array(t) for t in inputs.make_weights(w, threads=16))
     oracle.build()
+    if precision == "mx":
+        w1q, w1s = oracle.mx_quantize(W1.reshape(-1, w.H), oracle.MX_FP4)
+        w2q, w2s = oracle.mx_quantize(W2.reshape(-1, w.I), oracle.MX_FP4)
+        del W1, W2
+
+    def ffn_mx(xp, blocks):
+        rows = np.concatenate([np.arange(b0, b0 + m) for _, _, b0, m in blocks.tolist()]
+                              + [np.zeros(0, np.int64)]).astype(np.int32)
+        ex = np.concatenate([np.full(m, l) for _, l, _, m in blocks.tolist()]
+                            + [np.zeros(0, np.int64)]).astype(np.int32)
+        xq, xs = oracle.mx_quantize(xp, oracle.MX_FP8)
+        _, _, y = oracle.ffn_mx_rows(xq, xs, w1q, w1s, w2q, w2s, w.H, w.I, rows, ex)
+        yp = np.zeros((xp.shape[0], w.H), np.uint16)
+        yp[rows] = y
+        return yp
 
     def run(n):
         logits = np.ascontiguousarray(logits_all[:n])
@@ -214,7 +239,10 @@ def cpu_baseline(w, skew, T_s, target_s=12.0):
                                       w.n_local, w.beta, x)
         _, _, blocks = oracle.plan(counts, w.E, w.expert_begin, w.expert_stride, w.n_local, w.P,
                                    w.beta)
-        _, yp = oracle.ffn_blocks(xp, W1, W2, blocks)
+        if precision == "mx":
+            yp = ffn_mx(xp, blocks)
+        else:
+            _, yp = oracle.ffn_blocks(xp, W1, W2, blocks)
         oracle.combine(yp, wt, ep, n, w.K)
         return time.perf_counter() - t0
 
@@ -230,7 +258,8 @@ def cpu_baseline(w, skew, T_s, target_s=12.0):
             f"the whole batch of {w.T} tokens, {reps} times")
     return {"value": round(n * reps / dt, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"{what}, whole path (route, permute, plan, FFN, combine), float64 plain C "
+            "sample": f"{what}, whole path (route, permute, plan, "
+                      f"{'MX ' if precision == 'mx' else ''}FFN, combine), float64 plain C "
                       f"with OpenMP, {dt:.1f} s"}
 
 
@@ -252,13 +281,21 @@ def main():
     skew = pick_skew(w, args.skew)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
 
+    mx = args.precision == "mx"
+    if mx and (dt != torch.bfloat16 or args.materialize):
+        raise SystemExit("--precision mx takes a bf16 workload and gathers its input rows")
     W1, W2 = inputs.make_weights(w, threads=16)
     W1, W2 = W1.to(dev), W2.to(dev)
     x = inputs.make_x(w).to(dev)
+    wmx = None
+    if mx or (dt == torch.bfloat16 and not args.no_mx_summary):
+        wmx = binding.mx_quantize_weights(W1, W2)  # MXFP4 weights, prepared once
+    if mx:
+        W1, W2 = wmx
     layer = binding.RoutedExperts(w.T, w.H, w.E, w.K, w.I, w.P, dtype=dt, E_loc=w.n_local,
                                   expert_begin=w.expert_begin, expert_stride=w.expert_stride,
                                   block_m=w.beta, gather=not args.materialize,
-                                  planner=args.planner)
+                                  planner=args.planner, precision=args.precision)
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
@@ -268,15 +305,17 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def measure(sk, steps, warmup):
+    def measure(sk, steps, warmup, lay=None, w1=None, w2=None):
+        lay = lay or layer
+        w1, w2 = (w1, w2) if w1 is not None else (W1, W2)
         logits = torch.from_numpy(inputs.make_logits(w, sk)).to(dev)
-        step = Step(layer, logits, x, W1, W2)
-        graph = layer.capture(logits, x, W1, W2) if args.graph else None
+        step = Step(lay, logits, x, w1, w2)
+        graph = lay.capture(logits, x, w1, w2) if args.graph else None
         wall, per = time_steps(step, steps, warmup, torch, graph)
         eager_wall = time_steps(step, steps, 1, torch)[0] if graph is not None else wall
-        counts = layer.counts.cpu()
+        counts = lay.counts.cpu()
         N = int(counts[w.expert_begin::w.expert_stride][: w.n_local].sum())
-        nb = int(layer.n_blocks.item())
+        nb = int(lay.n_blocks.item())
         del graph
         return wall, per, N, nb, counts, eager_wall
 
@@ -292,12 +331,20 @@ def main():
     eb = 2 if dt == torch.bfloat16 else 4
     permute_bytes = (w.T + N) * w.H * eb + 4 * (w.T * w.K + rows_pad)
     combine_bytes = (N + w.T) * w.H * eb + 8 * w.T * w.K
-    traffic = ffn_traffic(w.name)
+    traffic = ffn_traffic(w.name, args.precision)
     t_roof, touched, wbytes, bound = ffn_roofline(w, loc.tolist(), eb)
     fc1_kernel = ("ffn_bf16_kernel<true, false>, the FC1 GEMM of moe_expert_ffn_fc1 (gate/up + SwiGLU)"
                   if args.materialize else
                   "ffn_bf16_kernel<true, true>, the FC1 GEMM of moe_expert_ffn_fc1_gather (gate/up + SwiGLU, "
                   "rows gathered from x)")
+    peak_mfma = PEAK_BF16_TFLOPS
+    if mx:
+        fc1_kernel = ("ffn_mx_kernel<true>, the FC1 GEMM of moe_expert_ffn_mx_fc1 (MXFP4 gate/up "
+                      "weights x MXFP8 rows gathered from x, SwiGLU, MXFP8 activation out)")
+        peak_mfma = PEAK_FP8_TFLOPS
+        # weights are 4.25 bits per value (codes + one E8M0 scale per 32): 17/32 byte
+        eb = 17.0 / 32.0
+        t_roof, touched, wbytes, bound = ffn_roofline(w, loc.tolist(), eb, PEAK_FP8_TFLOPS)
     if bound == "hbm":
         # weight-read bound (decode): FC1 streams the gate/up weights of every touched expert
         fc1_bytes = wbytes * 2.0 / 3.0
@@ -308,8 +355,8 @@ def main():
     else:
         roofline = {"kernel": fc1_kernel,
                     "bound": "mfma", "achieved": round(achieved, 1),
-                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
+                    "peak": peak_mfma, "unit": "TFLOP/s",
+                    "frac": round(achieved / peak_mfma, 4), "traffic": traffic}
 
     line = {
         "metric": METRIC,
@@ -323,19 +370,21 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if dt == torch.bfloat16 else "f32",
+        "dtype": ("mxfp4 weights x mxfp8 activations (f32 accumulation), bf16 in/out" if mx else
+                  "bf16" if dt == torch.bfloat16 else "f32"),
         "data": "synthetic (seeded Zipf-skewed router logits, N(0,1) activations, "
                 "N(0,0.02^2) expert weights)",
         "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "E_loc": w.n_local,
                    "K": w.K, "I": w.I, "P": w.P, "block_m": w.beta,
                    "skew": w.skew_label(skew), "local_entries": N, "blocks": nb,
                    "maxvio": round(maxvio, 3), "planner": args.planner,
+                   "precision": args.precision,
                    "parallelism": "single GPU",
                    "launch": "hip graph replay" if args.graph else "eager",
                    "dispatch": "materialised xp" if args.materialize else
                                "gather-on-load (FC1 reads x rows through row_token)"},
         "gemm_tflops": round(flops_ffn / ffn_s / 1e12, 1),
-        "gemm_frac_of_peak": round(flops_ffn / ffn_s / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "gemm_frac_of_peak": round(flops_ffn / ffn_s / 1e12 / peak_mfma, 4),
         "per_call_us": {k: round(v, 2) for k, v in per.items()},
         "permute_gbs": (round(permute_bytes / (per["permute"] * 1e-6) / 1e9, 1)
                         if args.materialize else None),
@@ -348,6 +397,25 @@ def main():
         "roofline": roofline,
         "roofline_kernel_us": round(fc1_s * 1e6, 2),
     }
+    if wmx is not None and not mx:
+        # the same step on the MX path (MXFP4 weights, MXFP8 activations), same batch
+        lay_mx = binding.RoutedExperts(w.T, w.H, w.E, w.K, w.I, w.P, dtype=dt, E_loc=w.n_local,
+                                       expert_begin=w.expert_begin,
+                                       expert_stride=w.expert_stride, block_m=w.beta,
+                                       planner=args.planner, precision="mx")
+        st = max(20, min(args.steps, 100))
+        wl_mx, pr_mx, n_mx, _, _, _ = measure(skew, st, st, lay_mx, wmx[0], wmx[1])
+        f1 = (pr_mx["fc1"] - pr_mx.get("fc1_schedule", 0.0)) * 1e-6
+        line["mx_path"] = {
+            "tokens_per_s": round(w.T / wl_mx, 1), "ms_per_step": round(wl_mx * 1e3, 4),
+            "fc1_kernel": "ffn_mx_kernel<true>",
+            "fc1_tflops": round(4.0 * w.H * w.I * n_mx / f1 / 1e12, 1),
+            "fc1_frac_of_fp8_peak": round(4.0 * w.H * w.I * n_mx / f1 / 1e12 / PEAK_FP8_TFLOPS, 4),
+            "gemm_tflops": round(6.0 * w.H * w.I * n_mx / ((pr_mx["fc1"] + pr_mx["fc2"]) * 1e-6) / 1e12, 1),
+            "per_call_us": {k: round(v, 2) for k, v in pr_mx.items()},
+            "steps": st}
+        del lay_mx
+        torch.cuda.empty_cache()
     if w.n_local // w.P <= 64 and w.n_local * w.P <= 4096:
         line["plan_comparison"] = plan_comparison(layer, w, max(20, args.steps // 4), torch)
     if not args.no_all_skews:
@@ -357,7 +425,7 @@ def main():
             f = 6.0 * w.H * w.I * n_
             ffn_t = (pr["fc1"] + pr["fc2"]) * 1e-6
             loc_ = cnt_[w.expert_begin::w.expert_stride][: w.n_local].tolist()
-            tr, tch, wb, _ = ffn_roofline(w, loc_, eb)
+            tr, tch, wb, _ = ffn_roofline(w, loc_, eb, peak_mfma)
             by.append({"skew": w.skew_label(sk), "tokens_per_s": round(w.T / wl, 1),
                        "ms_per_step": round(wl * 1e3, 4),
                        "gemm_tflops": round(f / ffn_t / 1e12, 1),
@@ -372,7 +440,7 @@ def main():
         T_s = max(w.P, T_s // w.P * w.P)
         del layer
         torch.cuda.empty_cache()
-        line["cpu_baseline"] = cpu_baseline(w, skew, T_s)
+        line["cpu_baseline"] = cpu_baseline(w, skew, T_s, precision=args.precision)
     print(json.dumps(line), flush=True)
 
 

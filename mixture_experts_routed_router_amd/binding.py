@@ -421,6 +421,20 @@ def moe_expert_ffn_mx(xq, xs, row_token, w1q, w1s, w2q, w2s, blocks, n_blocks, a
         _ptr(workspace, torch.int32, "workspace"), workspace.numel(), _stream(stream)), call)
 
 
+def mx_quantize_weights(W1, W2, stream=None):
+    """Expert weights W1 [E_loc, 2I, H] and W2 [E_loc, H, I] (bf16 or float32, on the GPU) in
+    MXFP4: ((w1q, w1s), (w2q, w2s)), the weight arguments of the MX path."""
+    out = []
+    for W in (W1, W2):
+        cols = W.shape[-1]
+        q = torch.empty(*W.shape[:-1], cols // 2, dtype=torch.uint8, device=W.device)
+        sc = torch.empty(*W.shape[:-1], moe_mx_scale_pitch(cols), dtype=torch.uint8,
+                         device=W.device)
+        moe_mx_quantize(W, MOE_MX_FP4, q, sc, stream)
+        out.append((q, sc))
+    return tuple(out)
+
+
 def moe_combine(yp, topk_w, entry_pos, out, stream=None):
     T, K = topk_w.shape
     H = yp.shape[1]
@@ -439,13 +453,23 @@ class RoutedExperts:
 
     Buffers are sized once from the library's static bounds (T, K, E_loc, P, block_m), so a
     forward pass allocates nothing.  Weights are device tensors W1 [E_loc, 2I, H],
-    W2 [E_loc, H, I] in the activation dtype.
+    W2 [E_loc, H, I] in the activation dtype; with precision="mx", the MXFP4 pairs that
+    mx_quantize_weights returns (x is then quantized to MXFP8 inside the step).
     """
 
     def __init__(self, T, H, E, K, I, P, dtype=torch.bfloat16, E_loc=None, expert_begin=0,
                  expert_stride=1, block_m=128, renormalize=True, device="cuda", gather=False,
-                 planner="moonep", replica_budget=None):
+                 planner="moonep", replica_budget=None, precision="bf16"):
         self.T, self.H, self.E, self.K, self.I, self.P = T, H, E, K, I, P
+        if precision not in ("bf16", "mx"):
+            raise MoeError(f"unknown precision {precision!r} (bf16 or mx)")
+        # mx: x is quantized to MXFP8 per token row, the expert GEMMs run on MXFP4 weights
+        # (mx_quantize_weights) and gather their input rows; act is MXFP8, yp / out bf16
+        self.precision = precision
+        if precision == "mx":
+            if dtype != torch.bfloat16:
+                raise MoeError("the MX path takes bf16 activations")
+            gather = True
         if planner not in ("moonep", "megaflux"):
             raise MoeError(f"unknown planner {planner!r} (moonep or megaflux)")
         # moonep: moe_plan (exact per-rank entry capacity); megaflux: moe_plan_blocks
@@ -479,7 +503,15 @@ class RoutedExperts:
         self.n_blocks = torch.empty((1,), **i32)
         self.err_word = torch.empty((1,), **i32)
         self.ffn_workspace = torch.empty((moe_ffn_workspace_elems(self.max_blocks),), **i32)
-        self.act = torch.empty((self.max_rows, I), dtype=dtype, device=device)
+        u8 = dict(dtype=torch.uint8, device=device)
+        if precision == "mx":
+            self.act = None
+            self.xq = torch.empty((T, H), **u8)
+            self.xs = torch.empty((T, moe_mx_scale_pitch(H)), **u8)
+            self.actq = torch.empty((self.max_rows, I), **u8)
+            self.acts = torch.empty((self.max_rows, moe_mx_scale_pitch(I)), **u8)
+        else:
+            self.act = torch.empty((self.max_rows, I), dtype=dtype, device=device)
         self.yp = torch.empty((self.max_rows, H), dtype=dtype, device=device)
         self.out = torch.empty((T, H), dtype=dtype, device=device)
 
@@ -502,7 +534,17 @@ class RoutedExperts:
                  self.q, self.moves, self.n_moves, self.blocks, self.n_blocks, self.err_word,
                  stream)
 
+    def quantize_x(self, x, stream=None):
+        """MX path: x [T, H] bf16 -> MXFP8 codes and scales (per token row)."""
+        moe_mx_quantize(x, MOE_MX_FP8, self.xq, self.xs, stream)
+
     def expert_ffn(self, w1, w2, stream=None):
+        if self.precision == "mx":
+            (w1q, w1s), (w2q, w2s) = w1, w2
+            moe_expert_ffn_mx(self.xq, self.xs, self.row_token, w1q, w1s, w2q, w2s, self.blocks,
+                              self.n_blocks, self.actq, self.acts, self.yp, self.ffn_workspace,
+                              stream)
+            return
         if self.gather:
             moe_expert_ffn_gather(self._x, self.row_token, w1, w2, self.blocks, self.n_blocks,
                                   self.act, self.yp, self.ffn_workspace, stream)
@@ -511,6 +553,10 @@ class RoutedExperts:
                            self.ffn_workspace, stream)
 
     def expert_ffn_fc1(self, w1, stream=None):
+        if self.precision == "mx":
+            moe_expert_ffn_mx_fc1(self.xq, self.xs, self.row_token, w1[0], w1[1], self.blocks,
+                                  self.n_blocks, self.actq, self.acts, self.ffn_workspace, stream)
+            return
         if self.gather:
             moe_expert_ffn_fc1_gather(self._x, self.row_token, w1, self.blocks, self.n_blocks,
                                       self.act, self.ffn_workspace, stream)
@@ -519,6 +565,10 @@ class RoutedExperts:
                                self.ffn_workspace, stream)
 
     def expert_ffn_fc2(self, w2, stream=None):
+        if self.precision == "mx":
+            moe_expert_ffn_mx_fc2(self.actq, self.acts, w2[0], w2[1], self.blocks, self.n_blocks,
+                                  self.yp, self.ffn_workspace, stream)
+            return
         moe_expert_ffn_fc2(self.act, w2, self.blocks, self.n_blocks, self.yp, self.ffn_workspace,
                            stream)
 
@@ -533,6 +583,8 @@ class RoutedExperts:
         """route -> permute -> plan -> expert FFN -> combine; returns the static `out`."""
         self.route(logits, stream)
         self.permute(x, stream)
+        if self.precision == "mx":
+            self.quantize_x(x, stream)
         self.plan(stream)
         self.expert_ffn(w1, w2, stream)
         self.combine(stream)

@@ -215,3 +215,72 @@ def test_mx_ffn_full_size_sampled(name, skew):
     del layer, mx
     gc.collect()
     torch.cuda.empty_cache()
+
+
+def _mx_layer(c):
+    dev = "cuda"
+    layer = binding.RoutedExperts(c.T, c.H, c.E, c.K, c.I, c.P, dtype=c.dtype, E_loc=c.n_local,
+                                  expert_begin=c.begin, expert_stride=c.stride,
+                                  block_m=c.block_m, renormalize=c.renormalize, device=dev,
+                                  precision="mx")
+    logits = torch.from_numpy(c.logits).to(dev)
+    x = c.x.to(dev)
+    w1, w2 = binding.mx_quantize_weights(c.W1.to(dev), c.W2.to(dev))
+    return layer, logits, x, w1, w2
+
+
+@pytest.mark.parametrize("name,kw", [SMALL[0], SMALL[3], SMALL[4]])
+def test_mx_layer_end_to_end(name, kw):
+    """RoutedExperts(precision="mx"): the whole step (route, permute, MXFP8 quantization of x,
+    plan, MX FFN, combine) against the oracle: index outputs bit-exact, yp per row, out per
+    token (oracle combine over the oracle's MX yp)."""
+    from parity_helpers import check_index_parity
+    _announce(f"mx layer {name}")
+    c = random_case(**kw)
+    layer, logits, x, w1, w2 = _mx_layer(c)
+    layer.forward(logits, x, w1, w2)
+    torch.cuda.synchronize()
+    ref = oracle_index(c)
+    check_index_parity(layer, ref)
+    assert np.array_equal(host(layer.xq), oracle.mx_quantize(inputs.as_oracle_array(c.x), FP8)[0])
+    rows = np.nonzero(ref.row_token >= 0)[0]
+    mx = MxRun.__new__(MxRun)  # the layer's own buffers, checked like an MxRun
+    mx.H, mx.I, mx.gather = c.H, c.I, True
+    (mx.w1q, mx.w1s), (mx.w2q, mx.w2s) = w1, w2
+    mx.xq, mx.xs, mx.actq, mx.acts, mx.yp = layer.xq, layer.xs, layer.actq, layer.acts, layer.yp
+    _check_rows(c, mx, ref, rows, f"layer {name}")
+    # out against the oracle's combine of the oracle's MX yp (all local rows)
+    x_o = inputs.as_oracle_array(c.x)
+    ex = row_experts(ref.blocks, rows)
+    xq_o, xs_o = oracle.mx_quantize(x_o[ref.row_token[rows]], FP8)
+    w1q_o, w1s_o = oracle.mx_quantize(inputs.as_oracle_array(c.W1).reshape(-1, c.H), FP4)
+    w2q_o, w2s_o = oracle.mx_quantize(inputs.as_oracle_array(c.W2).reshape(-1, c.I), FP4)
+    _, _, yp_o = oracle.ffn_mx_rows(xq_o, xs_o, w1q_o, w1s_o, w2q_o, w2s_o, c.H, c.I,
+                                    np.arange(len(rows), dtype=np.int32), ex.astype(np.int32))
+    yp_full = np.zeros((len(ref.row_token), c.H), np.uint16)
+    yp_full[rows] = yp_o
+    out_o = oracle.combine(yp_full, ref.w, ref.entry_pos, c.T, c.K)
+    e_out = rel_frob(oracle.bf16_to_f64(host(layer.out)), oracle.bf16_to_f64(out_o))
+    print(f"layer {name}: out={e_out:.2e}", flush=True)
+    assert e_out <= BF16_TOL, e_out
+
+
+def test_mx_layer_graph_replay():
+    """The MX step captured in a HIP graph: every replay (with eager work between) equals the
+    eager step bit for bit."""
+    _announce("mx layer graph replay")
+    c = random_case(seed=12, T=500, H=256, E=16, K=4, I=192, P=4, block_m=32)
+    layer, logits, x, w1, w2 = _mx_layer(c)
+    layer.forward(logits, x, w1, w2)
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (layer.out, layer.actq, layer.yp)]
+    graph = layer.capture(logits, x, w1, w2)
+    for _ in range(3):
+        layer.out.zero_()  # every row of out is rewritten by the step
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(layer.out, eager[0]), "out"
+        assert torch.equal(layer.actq, eager[1]), "actq"
+        assert torch.equal(layer.yp, eager[2]), "yp"
+    del graph
