@@ -308,23 +308,6 @@ __device__ __forceinline__ void mfma_step(v16f_t (&acc)[4][2], const Frags& f, c
                 (int)((sc.w[fb] >> (16 * m)) & 0xFFu), 0, (int)((sc.t[tb] >> (16 * m)) & 0xFFu));
 }
 
-// Four float32 values (already divided by the block scale) -> their E4M3 codes in one word,
-// value j in byte j: clamped to +-448 (saturation), then the hardware conversion (nearest,
-// ties to even); a zero result loses its sign.  Equal to the integer encoder for every finite
-// input (checked over all float32 mantissas at stride 2^9 in the E4M3 range and at every
-// code and midpoint).
-__device__ __forceinline__ uint32_t e4m3_word(float v0, float v1, float v2, float v3) {
-    v0 = __builtin_amdgcn_fmed3f(v0, -448.f, 448.f);
-    v1 = __builtin_amdgcn_fmed3f(v1, -448.f, 448.f);
-    v2 = __builtin_amdgcn_fmed3f(v2, -448.f, 448.f);
-    v3 = __builtin_amdgcn_fmed3f(v3, -448.f, 448.f);
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, w, true);
-    const uint32_t u = (uint32_t)w;
-    const uint32_t nz = ((u & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) & 0x80808080u;  // bit 7: magnitude != 0
-    return u & (0x7F7F7F7Fu | nz);
-}
-
 // FC1 epilogue: act = SiLU(gate) * up for this wave's 64 activation columns x 64 token rows,
 // quantized per 32-column block to MXFP8 (the moe_mx_quantize rule) and stored.
 __device__ __forceinline__ void epilogue_fc1(const MxArgs& g, const MxItem& it,

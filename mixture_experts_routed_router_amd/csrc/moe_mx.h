@@ -1,23 +1,8 @@
 // moe_mx.h -- element encoders of the OCP MX formats (shared by the quantizer and the MX
-// expert GEMM's activation epilogue).
+// expert GEMM's activation epilogue): E2M1 by integer rounding, E4M3 by the hardware
+// conversion, and the E8M0 shared exponent.
 #pragma once
 #include "moe_device.h"
-
-// |a| (finite, already divided by the block scale) -> E4M3 magnitude code, nearest, ties even,
-// saturating at 448 (0x7E).
-__device__ __forceinline__ uint32_t e4m3_code(float a) {
-    if (a >= 448.f) return 0x7E;
-    if (a < 0.015625f) return (uint32_t)rintf(a * 512.f);  // subnormal: units of 2^-9 (8 = 2^-6)
-    const int e = ilogbf(a);                                // 2^e <= a < 2^(e+1), e in [-6, 8]
-    int q = (int)rintf((ldexpf(a, -e) - 1.f) * 8.f);
-    int eb = e + 7;
-    if (q == 8) {
-        q = 0;
-        eb += 1;
-    }
-    const uint32_t c = ((uint32_t)eb << 3) | (uint32_t)q;
-    return c > 0x7E ? 0x7E : c;
-}
 
 // |a| -> E2M1 magnitude code (values 0, 0.5, 1, 1.5, 2, 3, 4, 6), nearest, ties even, saturating.
 __device__ __forceinline__ uint32_t e2m1_code(float a) {
@@ -40,4 +25,21 @@ __device__ __forceinline__ int mx_shared_exp(float amax, int emax) {
     if (!(amax > 0.f)) return -127;
     const int e = ilogbf(amax) - emax;
     return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// Four float32 values (already divided by the block scale) -> their E4M3 codes in one word,
+// value j in byte j: clamped to +-448 (saturation), then the hardware conversion (nearest,
+// ties to even); a zero result loses its sign.  Equal to an integer nearest-even encoder of the
+// same rule for every finite input (checked on the GPU over all float32 mantissas at stride 2^9
+// across the E4M3 range, and at every code and midpoint, both signs).
+__device__ __forceinline__ uint32_t e4m3_word(float v0, float v1, float v2, float v3) {
+    v0 = __builtin_amdgcn_fmed3f(v0, -448.f, 448.f);
+    v1 = __builtin_amdgcn_fmed3f(v1, -448.f, 448.f);
+    v2 = __builtin_amdgcn_fmed3f(v2, -448.f, 448.f);
+    v3 = __builtin_amdgcn_fmed3f(v3, -448.f, 448.f);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, w, true);
+    const uint32_t u = (uint32_t)w;
+    const uint32_t nz = ((u & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) & 0x80808080u;  // bit 7: magnitude != 0
+    return u & (0x7F7F7F7Fu | nz);
 }

@@ -9,8 +9,9 @@
 // lower-indexed element in the low nibble.
 //
 // Four lanes per block, eight values per lane: 16- or 32-byte loads, the block maximum from two
-// lane swaps, then each lane converts its values with integer rounding (the scaled value is
-// exact: a power-of-two multiple of the input) and stores 8 (FP8) or 4 (FP4) bytes.
+// lane swaps, then each lane scales its values (exactly: a power-of-two multiple) and converts
+// them -- FP8 with the hardware conversion after a +-448 clamp (moe_mx.h: equal to the integer
+// encoder), FP4 with integer rounding -- and stores 8 (FP8) or 4 (FP4) bytes.
 #include "moe_launch.h"
 #include "moe_mx.h"
 
@@ -20,10 +21,15 @@ constexpr int kThreads = 256;
 
 template <bool kBF16, bool kFP4>
 __global__ void __launch_bounds__(kThreads)
-mx_quantize_kernel(const uint8_t* __restrict__ src, int64_t n8, int64_t nb, int64_t pitch,
+mx_quantize_kernel(const uint8_t* __restrict__ src, int64_t n8, int64_t gpr, int64_t pitch,
                    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+    // group g = 8 consecutive values = (row, column group col); tracked incrementally over the
+    // grid-stride loop (one 64-bit division at the start)
     const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < n8; g += stride) {
+    const int64_t s_row = stride / gpr, s_col = stride - s_row * gpr;
+    int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    int64_t row = g / gpr, col = g - row * gpr;
+    for (; g < n8; g += stride) {
         float v[8];
         if (kBF16) {
             const uint4 u = reinterpret_cast<const uint4*>(src)[g];
@@ -47,28 +53,30 @@ mx_quantize_kernel(const uint8_t* __restrict__ src, int64_t n8, int64_t nb, int6
         amax = fmaxf(amax, __shfl_xor(amax, 1, MOE_WAVE));
         amax = fmaxf(amax, __shfl_xor(amax, 2, MOE_WAVE));
         const int se = mx_shared_exp(amax, kFP4 ? 2 : 8);
-        if ((g & 3) == 0) {
-            const int64_t b = g >> 2, row = b / nb;  // block b = (row, b - row * nb)
-            scales[row * pitch + (b - row * nb)] = (uint8_t)(se + 127);
-        }
-        uint32_t c[8];
+        if ((g & 3) == 0) scales[row * pitch + (col >> 2)] = (uint8_t)(se + 127);
+        float sv[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float s = ldexpf(v[i], -se);
-            const uint32_t m = kFP4 ? e2m1_code(fabsf(s)) : e4m3_code(fabsf(s));
-            const uint32_t sign = (s < 0.f && m != 0) ? (kFP4 ? 0x8u : 0x80u) : 0u;
-            c[i] = m | sign;
-        }
+        for (int i = 0; i < 8; ++i) sv[i] = ldexpf(v[i], -se);  // exact: a power-of-two scaling
         if (kFP4) {
             uint32_t packed = 0;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) packed |= c[i] << (4 * i);
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t m = e2m1_code(fabsf(sv[i]));
+                const uint32_t c = m | ((sv[i] < 0.f && m != 0) ? 0x8u : 0u);
+                packed |= c << (4 * i);
+            }
             reinterpret_cast<uint32_t*>(codes)[g] = packed;
         } else {
             uint2 o;
-            o.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-            o.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+            o.x = e4m3_word(sv[0], sv[1], sv[2], sv[3]);
+            o.y = e4m3_word(sv[4], sv[5], sv[6], sv[7]);
             reinterpret_cast<uint2*>(codes)[g] = o;
+        }
+        col += s_col;
+        row += s_row;
+        if (col >= gpr) {
+            col -= gpr;
+            row += 1;
         }
     }
 }
@@ -77,21 +85,21 @@ mx_quantize_kernel(const uint8_t* __restrict__ src, int64_t n8, int64_t nb, int6
 
 hipError_t moe_launch_mx_quantize(const void* src, moe_dtype_t dt, int64_t rows, int64_t cols,
                                   int fmt, uint8_t* codes, uint8_t* scales, hipStream_t stream) {
-    const int64_t n8 = rows * cols / 8, nb = cols / 32, pitch = moe_mx_scale_pitch_impl(cols);
+    const int64_t n8 = rows * cols / 8, gpr = cols / 8, pitch = moe_mx_scale_pitch_impl(cols);
     int64_t grid = (n8 + kThreads - 1) / kThreads;
     if (grid > 8192) grid = 8192;
     if (grid < 1) return hipSuccess;
     const uint8_t* s = static_cast<const uint8_t*>(src);
     if (dt == MOE_BF16) {
         if (fmt == MOE_MX_FP4)
-            mx_quantize_kernel<true, true><<<(int)grid, kThreads, 0, stream>>>(s, n8, nb, pitch, codes, scales);
+            mx_quantize_kernel<true, true><<<(int)grid, kThreads, 0, stream>>>(s, n8, gpr, pitch, codes, scales);
         else
-            mx_quantize_kernel<true, false><<<(int)grid, kThreads, 0, stream>>>(s, n8, nb, pitch, codes, scales);
+            mx_quantize_kernel<true, false><<<(int)grid, kThreads, 0, stream>>>(s, n8, gpr, pitch, codes, scales);
     } else {
         if (fmt == MOE_MX_FP4)
-            mx_quantize_kernel<false, true><<<(int)grid, kThreads, 0, stream>>>(s, n8, nb, pitch, codes, scales);
+            mx_quantize_kernel<false, true><<<(int)grid, kThreads, 0, stream>>>(s, n8, gpr, pitch, codes, scales);
         else
-            mx_quantize_kernel<false, false><<<(int)grid, kThreads, 0, stream>>>(s, n8, nb, pitch, codes, scales);
+            mx_quantize_kernel<false, false><<<(int)grid, kThreads, 0, stream>>>(s, n8, gpr, pitch, codes, scales);
     }
     return hipGetLastError();
 }
