@@ -230,23 +230,34 @@ def cpu_baseline(w, skew, T_s, target_s=12.0, precision="bf16"):
         yp[rows] = y
         return yp
 
+    steps_s = {"route": 0.0, "permute": 0.0, "plan": 0.0, "ffn": 0.0, "combine": 0.0}
+
     def run(n):
         logits = np.ascontiguousarray(logits_all[:n])
         x = np.ascontiguousarray(x_all[:n])
-        t0 = time.perf_counter()
+        t = [time.perf_counter()]
         ids, wt, counts = oracle.route(logits, w.K)
+        t.append(time.perf_counter())
         _, ep, _, xp = oracle.permute(ids, counts, w.E, w.expert_begin, w.expert_stride,
                                       w.n_local, w.beta, x)
+        t.append(time.perf_counter())
         _, _, blocks = oracle.plan(counts, w.E, w.expert_begin, w.expert_stride, w.n_local, w.P,
                                    w.beta)
+        t.append(time.perf_counter())
         if precision == "mx":
             yp = ffn_mx(xp, blocks)
         else:
             _, yp = oracle.ffn_blocks(xp, W1, W2, blocks)
+        t.append(time.perf_counter())
         oracle.combine(yp, wt, ep, n, w.K)
-        return time.perf_counter() - t0
+        t.append(time.perf_counter())
+        for k, name in enumerate(steps_s):
+            steps_s[name] += t[k + 1] - t[k]
+        return t[-1] - t[0]
 
     t_probe = run(T_s)
+    for name in steps_s:
+        steps_s[name] = 0.0
     want = int(T_s * target_s / max(t_probe, 1e-6))
     n = max(w.P, min(w.T, want) // w.P * w.P)
     # a whole batch that takes less than the target is run again until the target is reached
@@ -256,8 +267,17 @@ def cpu_baseline(w, skew, T_s, target_s=12.0, precision="bf16"):
         reps += 1
     what = (f"first {n} of {w.T} tokens of the same batch" if reps == 1 else
             f"the whole batch of {w.T} tokens, {reps} times")
+    cpu_model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": round(n * reps / dt, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model,
+            "per_step_s": {k: round(v, 3) for k, v in steps_s.items()},
             "sample": f"{what}, whole path (route, permute, plan, "
                       f"{'MX ' if precision == 'mx' else ''}FFN, combine), float64 plain C "
                       f"with OpenMP, {dt:.1f} s"}
