@@ -247,11 +247,13 @@ __device__ __forceinline__ void issue_slice(const MxArgs& g, const MxCtx& c, con
 }
 
 // The first slices of an item (the ring must be free).
-__device__ __forceinline__ void issue_prologue(const MxArgs& g, const MxCtx& c, const MxItem& item) {
+// Slices [s0, s1) of the first stages of an item (the ring must be free).
+__device__ __forceinline__ void issue_prologue(const MxArgs& g, const MxCtx& c, const MxItem& item,
+                                               int s0 = 0, int s1 = kStages) {
     const MxItem it = uniform_item(item);
     if (it.it < 0) return;
-    const int pre = c.nk < kStages ? c.nk : kStages;
-    for (int s = 0; s < pre; ++s) issue_slice(g, c, it, s);
+    const int pre = c.nk < s1 ? c.nk : s1;
+    for (int s = s0; s < pre; ++s) issue_slice(g, c, it, s);
 }
 
 __device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -475,12 +477,16 @@ __device__ __forceinline__ void mx_item(const MxArgs& g, const MxCtx& c, const M
         if (step == 3) wait_copies_n_and_barrier<0>();  // staged row_token entries
         decode_step<kFC1>(step, nxt, g, c);
     }
-    issue_prologue(g, c, nxt);
+    // the next item's slice 0 goes out before this item's stores, its other first slices after
+    // them: the next item's first wait (for all but the last (stages - 1) slices' copies) then
+    // covers slice 0 and the stores, not the slices behind them
+    issue_prologue(g, c, nxt, 0, 1);
 
     if (kFC1)
         epilogue_fc1(g, cur, acc, fh, tq, c.lane);
     else
         epilogue_fc2(g, cur, acc, fh, tq, c.lane);
+    issue_prologue(g, c, nxt, 1, kStages);
 }
 
 // Persistent grouped GEMM, one workgroup per CU (150 KB of LDS).
