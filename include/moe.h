@@ -357,7 +357,8 @@ moe_status_t moe_expert_ffn_mx_fc2(const uint8_t* actq, const uint8_t* acts, con
  *   out[t][h] = sum over k with entry_pos[t*K + k] >= 0 of topk_w[t][k] * yp[pos][h],
  * accumulated in float32 in ascending k, rounded to dt on store; 0 for a token with no
  * local entry.  yp [*, H], topk_w [T, K], entry_pos [T*K], out [T, H].
- * Row bytes (H * element size) must be a multiple of 16. */
+ * Row bytes (H * element size) must be a multiple of 16; K above 16 (the largest top-k of
+ * moe_route) returns MOE_ERR_UNSUPPORTED. */
 moe_status_t moe_combine(const void* yp, moe_dtype_t dt, const float* topk_w,
                          const int32_t* entry_pos, int T, int H, int K, void* out,
                          hipStream_t stream);

@@ -356,6 +356,7 @@ moe_status_t moe_combine(const void* yp, moe_dtype_t dt, const float* topk_w,
     if (!yp || !topk_w || !entry_pos || !out) return MOE_ERR_INVALID;
     if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID;
     if (T < 1 || H < 1 || K < 1) return MOE_ERR_INVALID;
+    if (K > MOE_MAX_K) return MOE_ERR_UNSUPPORTED;
     const int64_t row_bytes = (int64_t)H * (dt == MOE_BF16 ? 2 : 4);
     if (row_bytes % 16 != 0 || !aligned16(yp) || !aligned16(out)) return MOE_ERR_INVALID;
     return launched(moe_launch_combine(yp, dt, topk_w, entry_pos, T, H, K, out, stream));

@@ -9,10 +9,10 @@
 // One wavefront per token (grid-stride): lane k < K loads entry k's row and weight once; the
 // wave reads them back uniformly (readlane, scalar registers), skips non-local entries, and
 // walks the output row in 16-byte chunks (8 bf16 or 4 float32 per lane, stored non-temporally).
-// With four or more local entries it issues the loads of all entries of a chunk before its FMAs;
-// with fewer it takes 4 chunks per lane at once, entry by entry, so either way a wave has several
-// KB of loads in flight.  Rows of yp and out are read / written in coalesced 1 KB runs per wave
-// instruction; the sum runs over k in ascending order in both paths.
+// With four or more local entries it issues the loads of all entries for 2 chunks per lane before
+// their FMAs; with fewer it takes 4 chunks per lane at once, entry by entry, so either way a wave
+// has several KB of loads in flight.  Rows of yp and out are read / written in coalesced 1 KB
+// runs per wave instruction; the sum runs over k in ascending order in both paths.
 #include "moe_launch.h"
 
 namespace {
@@ -66,8 +66,13 @@ __device__ __forceinline__ uint4 pack_chunk(const float (&acc)[8]) {
 // mostly one), so that a wave keeps 4 KB of loads in flight instead of 1 KB (8 chunks
 // measured faster still on the one-entry shape but cost the dense path occupancy).
 constexpr int kSparseChunks = 4;
+// Chunks per lane with four or more local entries: two keep 2 KB per entry in flight per wave
+// (3-22% faster than one chunk after the down GEMM on the workloads' shapes; four chunks were
+// no faster on the large-H shapes and slower on the DeepSeek-V3 share).
+constexpr int kDenseChunks = 2;
 
-template <bool kBF16>
+// KM: the top-k bound the kernel is unrolled for (4, 8 or 16 >= K).
+template <bool kBF16, int KM>
 __global__ void __launch_bounds__(kThreads)
 combine_kernel(const uint8_t* __restrict__ yp, const float* __restrict__ w,
                const int32_t* __restrict__ entry_pos, int T, int H, int K,
@@ -86,27 +91,35 @@ combine_kernel(const uint8_t* __restrict__ yp, const float* __restrict__ w,
         uint4* orow = reinterpret_cast<uint4*>(out + (int64_t)t * row_bytes);
         const int n_local = __popcll(__ballot(my_p >= 0));
         if (n_local >= 4) {
-            // many entries: one chunk per lane, the loads of all entries before the FMAs
-            for (int c = lane; c < n16; c += MOE_WAVE) {
+            // many entries: kDenseChunks chunks per lane, the loads of all entries before the FMAs
+            for (int c0 = lane; c0 < n16; c0 += MOE_WAVE * kDenseChunks) {
                 // wave-uniform entry rows/weights (readlane: loop-invariant scalars)
-                uint4 v[MOE_MAX_K];
+                uint4 v[KM][kDenseChunks];
 #pragma unroll
-                for (int k = 0; k < MOE_MAX_K; ++k) {
+                for (int k = 0; k < KM; ++k) {
                     if (k < K) {
                         const int p = __builtin_amdgcn_readlane(my_p, k);
-                        if (p >= 0) v[k] = reinterpret_cast<const uint4*>(yp + (int64_t)p * row_bytes)[c];
-                    }
-                }
-                float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                        if (p >= 0) {
+                            const uint4* row = reinterpret_cast<const uint4*>(yp + (int64_t)p * row_bytes);
 #pragma unroll
-                for (int k = 0; k < MOE_MAX_K; ++k) {
-                    if (k < K && __builtin_amdgcn_readlane(my_p, k) >= 0) {
-                        const float wk = __builtin_bit_cast(
-                            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_w), k));
-                        fma_chunk<kBF16>(acc, v[k], wk);
+                            for (int u = 0; u < kDenseChunks; ++u)
+                                if (c0 + u * MOE_WAVE < n16) v[k][u] = row[c0 + u * MOE_WAVE];
+                        }
                     }
                 }
-                store_nt16(pack_chunk<kBF16>(acc), orow + c);
+#pragma unroll
+                for (int u = 0; u < kDenseChunks; ++u) {
+                    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int k = 0; k < KM; ++k) {
+                        if (k < K && __builtin_amdgcn_readlane(my_p, k) >= 0) {
+                            const float wk = __builtin_bit_cast(
+                                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_w), k));
+                            fma_chunk<kBF16>(acc, v[k][u], wk);
+                        }
+                    }
+                    if (c0 + u * MOE_WAVE < n16) store_nt16(pack_chunk<kBF16>(acc), orow + c0 + u * MOE_WAVE);
+                }
             }
         } else {
             // few entries (or none: zeros): kSparseChunks chunks per lane, entry by entry
@@ -142,6 +155,17 @@ combine_kernel(const uint8_t* __restrict__ yp, const float* __restrict__ w,
     }
 }
 
+template <bool kBF16>
+void launch_km(int grid, hipStream_t stream, const uint8_t* yp, const float* w,
+               const int32_t* entry_pos, int T, int H, int K, uint8_t* out) {
+    if (K <= 4)
+        combine_kernel<kBF16, 4><<<grid, kThreads, 0, stream>>>(yp, w, entry_pos, T, H, K, out);
+    else if (K <= 8)
+        combine_kernel<kBF16, 8><<<grid, kThreads, 0, stream>>>(yp, w, entry_pos, T, H, K, out);
+    else
+        combine_kernel<kBF16, 16><<<grid, kThreads, 0, stream>>>(yp, w, entry_pos, T, H, K, out);
+}
+
 }  // namespace
 
 hipError_t moe_launch_combine(const void* yp, moe_dtype_t dt, const float* w,
@@ -150,11 +174,11 @@ hipError_t moe_launch_combine(const void* yp, moe_dtype_t dt, const float* w,
     const int waves_per_block = kThreads / MOE_WAVE;
     int64_t grid = ((int64_t)T + waves_per_block - 1) / waves_per_block;
     if (grid > 4096) grid = 4096;  // grid-stride beyond 16K waves
+    const uint8_t* y = static_cast<const uint8_t*>(yp);
+    uint8_t* o = static_cast<uint8_t*>(out);
     if (dt == MOE_BF16)
-        combine_kernel<true><<<(int)grid, kThreads, 0, stream>>>(
-            static_cast<const uint8_t*>(yp), w, entry_pos, T, H, K, static_cast<uint8_t*>(out));
+        launch_km<true>((int)grid, stream, y, w, entry_pos, T, H, K, o);
     else
-        combine_kernel<false><<<(int)grid, kThreads, 0, stream>>>(
-            static_cast<const uint8_t*>(yp), w, entry_pos, T, H, K, static_cast<uint8_t*>(out));
+        launch_km<false>((int)grid, stream, y, w, entry_pos, T, H, K, o);
     return hipGetLastError();
 }

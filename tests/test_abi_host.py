@@ -191,6 +191,7 @@ def test_ffn_and_combine_reject(lib):
     assert lib.moe_combine(P[0], 1, P[1], P[2], 4, 100, 2, P[3], NULL) == INVALID  # 200-B rows
     assert lib.moe_combine(P[0], 1, P[1], NULL, 4, 128, 2, P[3], NULL) == INVALID
     assert lib.moe_combine(P[0], 1, P[1], P[2], 0, 128, 2, P[3], NULL) == INVALID
+    assert lib.moe_combine(P[0], 1, P[1], P[2], 4, 128, 17, P[3], NULL) == UNSUPPORTED  # K > 16
 
 
 def test_binding_fails_loudly_without_a_gpu_tensor(lib):
