@@ -122,6 +122,7 @@ moe_status_t moe_plan(const int32_t* expert_counts, int E, int expert_begin, int
                       int max_blocks, int32_t* err_word, hipStream_t stream) {
     if (!expert_counts || !q || !moves || !n_moves || !blocks || !n_blocks)
         return MOE_ERR_INVALID;
+    if (!aligned16(moves) || !aligned16(blocks)) return MOE_ERR_INVALID;  // 16-byte records
     if (!valid_local_set(E, expert_begin, expert_stride, E_loc) || P < 1 || E_loc % P != 0 ||
         !valid_block_m(block_m) || max_moves < 0 || max_blocks < 1)
         return MOE_ERR_INVALID;

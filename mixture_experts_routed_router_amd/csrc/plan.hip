@@ -8,12 +8,13 @@
 // expert's rows are cut into blocks of at most beta rows in the expert's stable order.
 //
 // One workgroup.  The greedy is sequential by nature (at most P-1 rank moves, each a few
-// slices) and runs in wave 0: lane r holds rank r's surplus in a register, the experts'
-// remaining counts sit in LDS.  Arg-min / arg-max run only over the lanes that compete (the
-// P ranks, or the donor's G = E_loc / P experts, one per lane) under total orders (value,
-// then lowest id), so ties resolve exactly as stated in moe.h; groups of up to 16 lanes
-// reduce with DPP lane swaps inside a row, larger ones add cross-row shuffles.  The block
-// table is then emitted by all threads from a scan of per-(rank, expert) block counts.
+// slices) and runs in wave 0: lane r holds rank r's surplus in a register, and lane i the
+// remaining entries of experts i, i+64, ... (E_loc <= 256).  Every arg-min / arg-max is one
+// branch-free reduction of 64-bit (value, index) keys over the wave, under total orders
+// (value, then lowest id), so ties resolve exactly as stated in moe.h; lanes that do not
+// compete hold the losing key.  The slice counts sit in LDS in table order (rank-major), so
+// the block table is emitted by all threads from a scan of per-slice block counts with
+// consecutive threads reading consecutive slices; each block is then written by its own thread.
 #include "moe_launch.h"
 #include "moe_wave.h"
 
@@ -28,23 +29,22 @@ plan_kernel(const int32_t* __restrict__ counts, int begin, int stride, int E_loc
             int32_t* __restrict__ n_moves, int max_moves, int32_t* __restrict__ blocks,
             int32_t* __restrict__ n_blocks, int max_blocks, int32_t* __restrict__ err_word) {
     __shared__ int n_s[256];
-    __shared__ int rem_s[256];
     __shared__ int off_s[257];
-    __shared__ int q_s[kMaxSlices];      // [l * P + r]
-    __shared__ int start_s[kMaxSlices];  // first row of slice (l, r), then its first block
+    // slice (l, r) = the rows of local expert l that rank r computes, kept in table order
+    // s = r * E_loc + l: q_s = its row count, start_s = its first row
+    __shared__ int q_s[kMaxSlices];
+    __shared__ int start_s[kMaxSlices];
+    __shared__ int boff_s[kMaxSlices];  // first block of each slice
     __shared__ int part[kThreads / MOE_WAVE];
     __shared__ int err_s;
 
     const int tid = threadIdx.x;
     const int lane = moe_lane_id();
     const int G = E_loc / P;
+    const int S = E_loc * P;
 
-    for (int l = tid; l < E_loc; l += kThreads) {
-        const int n = counts[begin + l * stride];
-        n_s[l] = n;
-        rem_s[l] = n;
-    }
-    for (int i = tid; i < E_loc * P; i += kThreads) q_s[i] = 0;
+    for (int l = tid; l < E_loc; l += kThreads) n_s[l] = counts[begin + l * stride];
+    for (int i = tid; i < S; i += kThreads) q_s[i] = 0;
     if (tid == 0) err_s = 0;
     __syncthreads();
 
@@ -82,54 +82,56 @@ plan_kernel(const int32_t* __restrict__ counts, int begin, int stride, int E_loc
             for (int l = lane * G; l < (lane + 1) * G; ++l) load += n_s[l];
             d = load - (N / P + (lane < N % P ? 1 : 0));
         }
-        const int rank_levels = ceil_log2(P);
-        const int gsize = G < MOE_WAVE ? G : MOE_WAVE;
-        const int expert_levels = ceil_log2(gsize);
+        // remaining (not yet moved) entries of local expert lane + 64 j, in registers
+        int rem[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rem[j] = lane + 64 * j < E_loc ? n_s[lane + 64 * j] : 0;
+
+        // The greedy runs in uniform control flow: every search is a branch-free reduction of
+        // 64-bit (value, index) keys over the whole wave (ranks >= P and experts outside the
+        // donor hold the losing key), so the rank min / max searches of one step overlap.
         int nm = 0, err = 0;
         for (int iter = 0; iter <= P; ++iter) {
-            int mn = lane < P ? d : 0x7FFFFFFF, mn_i = lane;
-            int mx = lane < P ? d : (int)0x80000000, mx_i = lane;
-            group_best<false>(mn, mn_i, rank_levels);
-            group_best<true>(mx, mx_i, rank_levels);
-            mn = __builtin_amdgcn_readfirstlane(mn);
-            mn_i = __builtin_amdgcn_readfirstlane(mn_i);
-            mx_i = __builtin_amdgcn_readfirstlane(mx_i);
+            const int64_t kmin = wave_best_key<false>(lane < P ? moe_wave::min_key(d, lane) : INT64_MAX);
+            const int64_t kmax = wave_best_key<true>(lane < P ? moe_wave::max_key(d, lane) : INT64_MIN);
+            const int mn = moe_wave::key_value(kmin);
             if (mn >= 0) break;
             if (iter == P) {  // cannot happen: each move settles one rank for good
                 err |= 4;
                 break;
             }
-            const int recv = mn_i, donor = mx_i;
+            const int recv = moe_wave::min_key_index(kmin), donor = moe_wave::max_key_index(kmax);
             int need = -mn;
             if (lane == donor) d -= need;
             if (lane == recv) d = 0;
-            for (int s = 0; need > 0; ++s) {
-                // donor's own expert with the most remaining entries (lowest id on ties):
-                // lane i looks at experts donor*G + i, + 64, ...
-                int bv = 0, bl = 0x7FFFFFFF;
-                for (int l = donor * G + lane; l < (donor + 1) * G; l += MOE_WAVE) {
-                    const int r = rem_s[l];
-                    if (r > 0 && (r > bv || (r == bv && l < bl))) {
-                        bv = r;
-                        bl = l;
+            const int e0 = donor * G, e1 = e0 + G;
+            for (int sl = 0; need > 0; ++sl) {
+                // donor's own expert with the most remaining entries (lowest id on ties)
+                int64_t kb = INT64_MIN;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int l = lane + 64 * j;
+                    if (l >= e0 && l < e1 && rem[j] > 0) {
+                        const int64_t c = moe_wave::max_key(rem[j], l);
+                        kb = c > kb ? c : kb;
                     }
                 }
-                group_best<true>(bv, bl, expert_levels);
-                bv = __builtin_amdgcn_readfirstlane(bv);
-                bl = __builtin_amdgcn_readfirstlane(bl);
-                if (bv <= 0 || s > G) {  // cannot happen: a donor always covers its move
+                kb = wave_best_key<true>(kb);
+                const int bv = moe_wave::key_value(kb);
+                const int bl = moe_wave::max_key_index(kb);
+                if (kb == INT64_MIN || bv <= 0 || sl > G) {  // cannot happen: a donor covers its move
                     err |= 4;
                     break;
                 }
                 const int take = bv < need ? bv : need;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (bl == lane + 64 * j) rem[j] -= take;
                 if (lane == 0) {
-                    rem_s[bl] = bv - take;
-                    q_s[bl * P + recv] += take;
+                    atomicAdd(&q_s[recv * E_loc + bl], take);  // no return value: no wait
                     if (nm < max_moves) {
-                        moves[4 * nm + 0] = donor;
-                        moves[4 * nm + 1] = recv;
-                        moves[4 * nm + 2] = bl;
-                        moves[4 * nm + 3] = take;
+                        const int4 mv = make_int4(donor, recv, bl, take);
+                        *reinterpret_cast<int4*>(moves + 4 * nm) = mv;
                     }
                 }
                 ++nm;
@@ -139,7 +141,11 @@ plan_kernel(const int32_t* __restrict__ counts, int begin, int stride, int E_loc
         }
         if (nm > max_moves) err |= 2;
         // leftovers stay with the owner
-        for (int l = lane; l < E_loc; l += MOE_WAVE) q_s[l * P + l / G] += rem_s[l];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int l = lane + 64 * j;
+            if (l < E_loc) atomicAdd(&q_s[(l / G) * E_loc + l], rem[j]);
+        }
         if (lane == 0) {
             *n_moves = nm < max_moves ? nm : max_moves;
             err_s = err;
@@ -147,27 +153,27 @@ plan_kernel(const int32_t* __restrict__ counts, int begin, int stride, int E_loc
     }
     __syncthreads();
 
-    for (int i = tid; i < E_loc * P; i += kThreads) q_out[i] = q_s[i];
-    // first row of slice (l, r): segment start + rows of expert l taken by lower ranks
+    // q output [E_loc, P]; first row of slice (l, r): segment start + rows of expert l taken
+    // by lower ranks
+    for (int i = tid; i < S; i += kThreads) {
+        const int r = i / E_loc, l = i - r * E_loc;
+        q_out[l * P + r] = q_s[i];
+    }
     for (int l = tid; l < E_loc; l += kThreads) {
         int acc = off_s[l];
         for (int r = 0; r < P; ++r) {
-            start_s[l * P + r] = acc;
-            acc += q_s[l * P + r];
+            start_s[r * E_loc + l] = acc;
+            acc += q_s[r * E_loc + l];
         }
     }
     __syncthreads();
 
-    // blocks per slice, slices in table order s = r * E_loc + l; thread owns a run of slices
-    const int S = E_loc * P;
+    // blocks per slice in table order; thread owns a run of slices
     const int per = (S + kThreads - 1) / kThreads;
     const int s_begin = min(S, tid * per);
     const int s_end = min(S, s_begin + per);
     int cnt = 0;
-    for (int s = s_begin; s < s_end; ++s) {
-        int r = s / E_loc, l = s - r * E_loc;
-        cnt += (q_s[l * P + r] + beta - 1) / beta;
-    }
+    for (int s = s_begin; s < s_end; ++s) cnt += (q_s[s] + beta - 1) / beta;
     // exclusive scan of the per-thread block counts: within each wave by shuffles, across
     // the four waves through LDS
     int incl = cnt;
@@ -185,19 +191,25 @@ plan_kernel(const int32_t* __restrict__ counts, int begin, int stride, int E_loc
         b += w < wave ? part[w] : 0;
         total += part[w];
     }
+    // each slice's first block; then one thread per block finds its slice by a binary search
+    // (a slice may hold many blocks: walking them per slice serialised a wave on its largest)
     for (int s = s_begin; s < s_end; ++s) {
-        int r = s / E_loc, l = s - r * E_loc;
-        int take = q_s[l * P + r];
-        int first = start_s[l * P + r];
-        for (int j = 0; j * beta < take; ++j, ++b) {
-            if (b < max_blocks) {
-                int rows = take - j * beta < beta ? take - j * beta : beta;
-                blocks[4 * b + 0] = r;
-                blocks[4 * b + 1] = l;
-                blocks[4 * b + 2] = first + j * beta;
-                blocks[4 * b + 3] = rows;
-            }
-        }
+        boff_s[s] = b;
+        b += (q_s[s] + beta - 1) / beta;
+    }
+    __syncthreads();
+    const int n_emit = total < max_blocks ? total : max_blocks;
+    int top = 1;
+    while (top * 2 <= S) top *= 2;
+    for (int bb = tid; bb < n_emit; bb += kThreads) {
+        int s = 0;  // last slice whose first block is <= bb: the slice holding block bb
+        for (int step = top; step > 0; step >>= 1)
+            if (s + step < S && boff_s[s + step] <= bb) s += step;
+        const int r = s / E_loc, l = s - r * E_loc;
+        const int j = bb - boff_s[s];
+        const int take = q_s[s];
+        const int rows = take - j * beta < beta ? take - j * beta : beta;
+        *reinterpret_cast<int4*>(blocks + 4 * bb) = make_int4(r, l, start_s[s] + j * beta, rows);
     }
     if (tid == 0) {
         int err = err_s;
