@@ -15,6 +15,8 @@
 // block counts q[l][r] sit in LDS and lane r only touches column r of them (the donor's
 // expert-scan snapshot excepted).  A donor's fan-out works on one expert row in registers
 // (lane r = q[l][r]), so every single-block move is two wave reductions and a lane update.
+// Every arg-min / arg-max is one branch-free reduction of 64-bit (value, index) keys over the
+// whole wave (moe_wave.h), with the losing value in the lanes that do not compete.
 // Selection, pruning (a bitonic sort of the replica keys by all threads, then wave 0) and
 // the single-block pass follow; the table is emitted by all threads from per-(expert, rank)
 // prefix sums, in the same layout as moe_plan's.
@@ -35,7 +37,6 @@ typedef volatile int vint;
 // One greedy search; runs in one wave.  Returns through q (LDS) and the lane registers.
 __device__ void search(vint* q, const int* b_s, int E_loc, int P, int G, int tau, int s,
                        bool by_overload, bool many, int lane, int& L, int& repl) {
-    const int lp = ceil_log2(P), lg = ceil_log2(G);
     const bool rank_lane = lane < P;
     for (int i = lane; i < E_loc * P; i += MOE_WAVE) q[i] = 0;
     for (int l = lane; l < E_loc; l += MOE_WAVE) q[l * P + l / G] = b_s[l];
@@ -58,22 +59,22 @@ __device__ void search(vint* q, const int* b_s, int E_loc, int P, int G, int tau
         bool visited = false;
         for (;;) {
             int v = (!visited && key >= 0) ? key : -1, d = lane;
-            wave_best<true>(v, d, 6);
+            wave_best_all<true>(v, d);
             if (v < 0) break;
             if (lane == d) visited = true;
-            int Ld = __shfl(L, d, MOE_WAVE);
+            int Ld = __builtin_amdgcn_readlane(L, d);
             if (Ld <= tau) continue;
             // the donor's home experts with blocks at home, most blocks first (fixed at visit start)
             const int snap = lane < G ? (int)q[(d * G + lane) * P + d] : 0;
             bool scanned = false;
             while (Ld > tau) {
                 int v2 = (lane < G && !scanned && snap > 0) ? snap : -1, j = lane;
-                wave_best<true>(v2, j, lg);
+                wave_best_all<true>(v2, j);
                 if (v2 < 0) break;
                 if (lane == j) scanned = true;
                 const int l = d * G + j;
                 int qc = rank_lane ? (int)q[l * P + lane] : 0;  // this lane's column of row l
-                int qd = __shfl(qc, d, MOE_WAVE);               // blocks of l still at home
+                int qd = __builtin_amdgcn_readlane(qc, d);       // blocks of l still at home
                 bool opened = false;                            // a new copy of l this round
                 // Single-block moves, k at a time: the receiver stays the least-loaded eligible
                 // copy (lower rank on ties) until it passes the runner-up, reaches tau, the
@@ -84,19 +85,19 @@ __device__ void search(vint* q, const int* b_s, int E_loc, int P, int G, int tau
                     if (qd == 0 || Ld <= tau) break;
                     const bool existing = rank_lane && lane != d && qc > 0 && L < tau;
                     int v3 = existing ? L : kBig, rcv = lane;
-                    wave_best<false>(v3, rcv, lp);
+                    wave_best_all<false>(v3, rcv);
                     bool open_new = false;
                     int k = min(qd, Ld - tau);
                     if (v3 != kBig) {
                         int v5 = (existing && lane != rcv) ? L : kBig, r2 = lane;
-                        wave_best<false>(v5, r2, lp);
+                        wave_best_all<false>(v5, r2);
                         k = min(k, tau - v3);
                         if (v5 != kBig) k = min(k, rcv < r2 ? v5 - v3 + 1 : v5 - v3);
                     } else {
                         if (!many && opened) break;
                         int v4 = (rank_lane && lane != d && qc == 0 && repl < s && L < tau) ? L : kBig;
                         rcv = lane;
-                        wave_best<false>(v4, rcv, lp);
+                        wave_best_all<false>(v4, rcv);
                         if (v4 == kBig) break;
                         open_new = true;
                         k = min(k, tau - v4);
@@ -262,7 +263,6 @@ plan_blocks_kernel(const int32_t* __restrict__ counts, int begin, int stride, in
     }
 
     if (wave == 0) {
-        const int lp = ceil_log2(P);
         const bool rank_lane = lane < P;
         int L = 0;
         if (rank_lane)
@@ -273,15 +273,15 @@ plan_blocks_kernel(const int32_t* __restrict__ counts, int begin, int stride, in
             const unsigned long long k = keys[i];
             const int l = (int)((k >> 16) & 0xFFFF), r = (int)(k & 0xFFFF), h = l / G;
             int qc = rank_lane ? (int)q[l * P + lane] : 0;
-            const int a = __shfl(qc, r, MOE_WAVE);
+            const int a = __builtin_amdgcn_readlane(qc, r);
             if (a == 0) continue;
             int tgt = -1;
-            if (__shfl(L, h, MOE_WAVE) + a <= Lmax) {
+            if (__builtin_amdgcn_readlane(L, h) + a <= Lmax) {
                 tgt = h;
             } else {
                 int v = (rank_lane && lane != r && lane != h && qc > 0 && L + a <= Lmax) ? L : kBig;
                 int t = lane;
-                wave_best<false>(v, t, lp);
+                wave_best_all<false>(v, t);
                 if (v != kBig) tgt = t;
             }
             if (tgt < 0) continue;
@@ -298,9 +298,9 @@ plan_blocks_kernel(const int32_t* __restrict__ counts, int begin, int stride, in
         // refinement 2: single blocks from the most- to the least-loaded rank
         for (int it = 0; it < sum_b; ++it) {
             int vmax = rank_lane ? L : -1, rmax = lane;
-            wave_best<true>(vmax, rmax, lp);
+            wave_best_all<true>(vmax, rmax);
             int vmin = rank_lane ? L : kBig, rmin = lane;
-            wave_best<false>(vmin, rmin, lp);
+            wave_best_all<false>(vmin, rmin);
             if (vmax - vmin <= 1) break;
             int lm = -1;
             for (int l0 = 0; l0 < E_loc && lm < 0; l0 += MOE_WAVE) {
