@@ -106,10 +106,13 @@ def test_permute_rejects(lib):
 
 def test_plan_rejects(lib):
     def plan(E=8, begin=0, stride=1, E_loc=8, Pn=4, bm=128, max_moves=12, max_blocks=16,
-             counts=P[0]):
-        return lib.moe_plan(counts, E, begin, stride, E_loc, Pn, bm, P[1], P[2], P[3], max_moves,
-                            P[4], P[5], max_blocks, NULL, NULL)
+             counts=P[0], moves=P[2], blocks=P[4]):
+        return lib.moe_plan(counts, E, begin, stride, E_loc, Pn, bm, P[1], moves, P[3], max_moves,
+                            blocks, P[5], max_blocks, NULL, NULL)
     assert plan(counts=NULL) == INVALID
+    # moves and blocks are written as 16-byte records
+    assert plan(moves=ctypes.c_void_p(P[2].value + 4)) == INVALID
+    assert plan(blocks=ctypes.c_void_p(P[4].value + 8)) == INVALID
     assert plan(Pn=3) == INVALID            # P must divide E_loc
     assert plan(bm=48) == INVALID
     assert plan(max_blocks=0) == INVALID
