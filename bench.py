@@ -120,14 +120,30 @@ def time_steps(step, steps, warmup, torch, graph=None):
     # the FC1 call starts with the tile-schedule kernel: time it alone on the same table, so
     # that the FC1 GEMM kernel's own duration is fc1 - schedule
     if step.layer.dtype == torch.bfloat16:
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(steps):
-            step.layer.tile_schedule()
-        e1.record()
-        torch.cuda.synchronize()
-        per["fc1_schedule"] = e0.elapsed_time(e1) / steps * 1e3
+        per["fc1_schedule"] = schedule_us(step.layer, torch)
     return wall, per
+
+
+def schedule_us(layer, torch, n=50, reps=8):
+    """GPU time of one tile-schedule launch: a HIP graph of n back-to-back launches, replayed
+    reps times between two events, so that the host's per-call overhead (longer than this
+    small kernel) is not counted as the kernel's time."""
+    layer.tile_schedule()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(n):
+            layer.tile_schedule()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del graph
+    return e0.elapsed_time(e1) / (n * reps) * 1e3
 
 
 def ffn_roofline(w, n_loc, eb, peak=PEAK_BF16_TFLOPS):
