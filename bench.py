@@ -4,10 +4,10 @@
 
 One step = route -> permute -> plan -> expert FFN (FC1, FC2) -> combine over one batch of
 seeded synthetic input already resident in HBM, timed as eager calls on one stream (--graph:
-as HIP-graph replays of the whole path; the eager figure is then reported beside it).  Prints ONE JSON line: whole-path tokens/s,
-the grouped GEMM's TFLOP/s, the dominant kernel (FC1, the gate/up GEMM with fused SwiGLU)
-against the bf16 MFMA peak, per-call times, and the CPU oracle timed on a bounded sample of
-the same workload on the host cores.
+as HIP-graph replays of the whole path; the eager figure is then reported beside it).
+Prints ONE JSON line: whole-path tokens/s, the grouped GEMM's TFLOP/s, the dominant kernel
+(FC1, the gate/up GEMM with fused SwiGLU) against the bf16 MFMA peak, per-call times, and the
+CPU oracle timed on a bounded sample of the same workload on the host cores.
 """
 from __future__ import annotations
 
