@@ -81,7 +81,8 @@ def test_plan_blocks_random_shapes():
     for trial in range(40):
         E_loc, P, beta = shapes[trial % len(shapes)]
         scale = int(rng.integers(1, 4000))
-        counts = (rng.zipf(1.3 + rng.random(), size=E_loc) * scale // 7).astype(np.int64)
+        z = np.minimum(rng.zipf(1.3 + rng.random(), size=E_loc), 1 << 20).astype(np.int64)
+        counts = z * scale // 7  # no int64 overflow; anything this large is capped below
         counts[rng.random(E_loc) < 0.2] = 0
         counts = np.minimum(counts, 20000).astype(np.int32)
         s = int(rng.integers(0, 9))
