@@ -81,6 +81,11 @@ def test_tiny_f32_full():
     ("one_rank", dict(seed=14, T=100, H=64, E=16, K=2, I=64, P=1)),
     # more than 3072 blocks: the FFN tile schedule walks the block table in global memory
     ("many_blocks", dict(seed=15, T=8192, H=64, E=64, K=8, I=64, P=8, block_m=16)),
+    # the permutation's two index passes at their limit (64 blocks of 256 tokens x 256 local
+    # experts = 16384 count values; the last block sums 63 x 256 of them), and one block past
+    # it (the three-pass form)
+    ("two_pass_limit", dict(seed=16, T=16384, H=64, E=256, K=4, I=64, P=8, block_m=16)),
+    ("three_pass", dict(seed=17, T=16385, H=64, E=256, K=4, I=64, P=8, block_m=16)),
 ])
 def test_small_layers_full(name, kw):
     c = random_case(**kw)
