@@ -86,6 +86,8 @@ def test_tiny_f32_full():
     # it (the three-pass form)
     ("two_pass_limit", dict(seed=16, T=16384, H=64, E=256, K=4, I=64, P=8, block_m=16)),
     ("three_pass", dict(seed=17, T=16385, H=64, E=256, K=4, I=64, P=8, block_m=16)),
+    # the two-pass form with the largest top-k (16 entries per token in one place pass)
+    ("two_pass_k16", dict(seed=18, T=16384, H=64, E=64, K=16, I=64, P=8, block_m=16)),
 ])
 def test_small_layers_full(name, kw):
     c = random_case(**kw)
