@@ -1,10 +1,11 @@
 // plan.hip -- skew-balancing plan over logical rank partitions + block table (moe_plan).
 //
 // MoonEP routing flow ("Same data, summed per rank" and "The greedy balance, step by step"):
-// a rank's surplus is its experts' entries minus its capacity S*K; each move refills the
-// currently hungriest rank in one shot from the currently biggest donor, the donor may
-// overshoot below capacity and be refilled later, and a move is realised by slicing the
-// donor's biggest experts.  MegaFlux §3.1 / App. A.2: the plan keeps every selection; each
+// a rank's surplus is its experts' entries minus its capacity S*K.  A single move brings the
+// rank furthest below capacity back to exactly zero, taking everything it lacks from the rank
+// furthest above; that donor may fall below capacity itself and is then topped up by a later
+// move.  The donor pays with its own experts, largest remaining first, split where the need
+// runs out.  MegaFlux §3.1 / App. A.2: the plan keeps every selection; each
 // expert's rows are cut into blocks of at most beta rows in the expert's stable order.
 //
 // One workgroup.  The greedy is sequential by nature (at most P-1 rank moves, each a few

@@ -303,8 +303,11 @@ int oracle_permute(const int32_t* ids, const int32_t* counts, int T, int K, int 
  * expert l take consecutive ranges of its segment in ascending rank order; the table lists
  * blocks rank by rank, then expert by expert: (rank, expert, first row, rows).
  * Pinned by: exact capacity and conservation invariants, move-count bound, hand-worked
- * golden plans, and an exhaustive sweep of small count vectors against brute-force
- * properties. */
+ * golden plans (among them tied receivers and one donor serving two receivers, where the
+ * second slice depends on the remaining counts), an exhaustive sweep of small count vectors
+ * against brute-force properties, and move-for-move equality with a second, independent
+ * statement of the greedy in Python (tests/plan_reference.py) on that sweep and on random
+ * skewed counts. */
 int oracle_plan(const int32_t* counts, int E, int begin, int stride, int E_loc, int P, int beta,
                 int32_t* q, int32_t* moves, int32_t* n_moves, int max_moves,
                 int32_t* blocks, int32_t* n_blocks, int max_blocks) {
@@ -425,10 +428,12 @@ done:
  * consecutive runs of its blocks in ascending rank order, so only the expert's last block is
  * partial); moves = one entry (owner, rank, expert, rows) per replica, expert then rank
  * ascending; blocks = (rank, expert, first row, rows), rank by rank, then expert by expert,
- * in block order.  Pinned by hand-worked plans (tests/golden/megaflux_plan_cases.json),
- * closed forms (no budget or a balanced start keep the no-replica assignment; an ample
- * budget reaches tau) and invariants (conservation, budget, one partial block per expert,
- * the refinement never raising the maximum). */
+ * in block order.  Pinned by hand-worked plans (tests/golden/megaflux_plan_cases.json, one
+ * of them with all four candidates tied on maximum load and replica count), closed forms (no
+ * budget or a balanced start keep the no-replica assignment; an ample budget reaches tau),
+ * invariants (conservation, budget, one partial block per expert, the refinement never
+ * raising the maximum), and equality with a second, independent statement in Python
+ * (tests/plan_reference.py) on random skewed counts. */
 static void bp_search(const int64_t* b, int E_loc, int P, int G, int64_t tau, int s,
                       int by_overload, int many, int64_t* q, int64_t* L, int* repl,
                       unsigned char* opened, unsigned char* visited, int64_t* key, int* order) {

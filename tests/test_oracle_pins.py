@@ -314,6 +314,54 @@ def test_plan_exhaustive_small(oracle_mod, P, G, cmax):
         _check_plan(c, E, 0, 1, E, P, 2, q, moves, blocks)
 
 
+
+def _random_counts(rng, E, hot):
+    """Zipf-like counts with occasional hot experts and zeros (small enough for Python)."""
+    c = rng.zipf(1.5, size=E).astype(np.int64) * int(rng.integers(1, 6))
+    if hot:
+        c[rng.integers(0, E)] += int(rng.integers(20, 200))
+    c[rng.random(E) < 0.2] = 0
+    return np.minimum(c, 3000).astype(np.int32)
+
+
+@pytest.mark.parametrize("P,G,cmax", [(2, 2, 4), (3, 2, 3), (4, 2, 3), (3, 1, 6), (4, 1, 5)])
+def test_plan_equals_independent_greedy_exhaustive(oracle_mod, P, G, cmax):
+    """Every count vector of the small sweep: the oracle's plan equals the independent Python
+    statement of the greedy (tests/plan_reference.py) move for move, q and blocks included."""
+    import itertools
+    from plan_reference import moonep_plan
+    E = P * G
+    for cnt in itertools.product(range(cmax + 1), repeat=E):
+        c = np.array(cnt, np.int32)
+        q, moves, blocks = oracle_mod.plan(c, E, 0, 1, E, P, 2)
+        rq, rm, rb = moonep_plan(list(cnt), P, 2)
+        assert q.tolist() == rq, cnt
+        assert moves.tolist() == rm, cnt
+        assert blocks.tolist() == rb, cnt
+
+
+def test_plan_equals_independent_greedy_random(oracle_mod):
+    """Random skewed count vectors up to 32 ranks and 8 experts per rank (totals not always
+    divisible by P), and every workload's counts: identical to the independent greedy."""
+    from plan_reference import moonep_plan
+    rng = np.random.default_rng(7)
+    for trial in range(400):
+        P = int(rng.choice([2, 3, 4, 5, 8, 16, 32]))
+        G = int(rng.integers(1, 9))
+        beta = int(rng.choice([1, 2, 16, 128]))
+        c = _random_counts(rng, P * G, trial % 2 == 0)
+        q, moves, blocks = oracle_mod.plan(c, P * G, 0, 1, P * G, P, beta)
+        rq, rm, rb = moonep_plan(c.tolist(), P, beta)
+        assert (q.tolist(), moves.tolist(), blocks.tolist()) == (rq, rm, rb), (trial, c.tolist(), P)
+    for w in inputs.WORKLOADS.values():
+        for skew in w.skews:
+            _, _, counts = oracle_mod.route(inputs.make_logits(w, skew), w.K)
+            n = [int(counts[w.expert_begin + l * w.expert_stride]) for l in range(w.n_local)]
+            q, moves, blocks = oracle_mod.plan(counts, w.E, w.expert_begin, w.expert_stride,
+                                               w.n_local, w.P, w.beta)
+            rq, rm, rb = moonep_plan(n, w.P, w.beta)
+            assert (q.tolist(), moves.tolist(), blocks.tolist()) == (rq, rm, rb), (w.name, skew)
+
 # --------------------------------------------------------------------------- ffn ---
 
 def _swiglu_f64(x, w1, w2, I):
@@ -539,6 +587,35 @@ def test_plan_blocks_invariants_all_workloads(oracle_mod, name):
             if s == 0:
                 assert np.array_equal(load, home)
 
+
+
+def test_plan_blocks_equals_independent_statement(oracle_mod):
+    """Random small and skewed count vectors at budgets 0, 1, 2, E/(4P) and E: the oracle's
+    block-granular plan equals the independent Python statement (tests/plan_reference.py),
+    replicas and table included.  Small P and beta make ties between ranks, experts and the
+    four candidates common."""
+    from plan_reference import megaflux_plan
+    rng = np.random.default_rng(5)
+    for trial in range(1500):
+        P = int(rng.choice([2, 3, 4, 5, 8]))
+        G = int(rng.integers(1, 5))
+        E = P * G
+        beta = int(rng.choice([1, 1, 2, 4, 16]))
+        c = _random_counts(rng, E, trial % 3 == 0) // (1 if beta > 1 else 4)
+        c = c.astype(np.int32)
+        s = int(rng.choice([0, 1, 2, max(E // (4 * P), 1), E]))
+        q, moves, blocks = oracle_mod.plan_blocks(c, E, 0, 1, E, P, beta, s)
+        rq, rm, rb = megaflux_plan(c.tolist(), P, beta, s)
+        assert (q.tolist(), moves.tolist(), blocks.tolist()) == (rq, rm, rb), (trial, c.tolist(), P, beta, s)
+    for w in inputs.WORKLOADS.values():
+        for skew in w.skews:
+            _, _, counts = oracle_mod.route(inputs.make_logits(w, skew), w.K)
+            n = [int(counts[w.expert_begin + l * w.expert_stride]) for l in range(w.n_local)]
+            s = w.n_local // (4 * w.P)
+            q, moves, blocks = oracle_mod.plan_blocks(counts, w.E, w.expert_begin,
+                                                      w.expert_stride, w.n_local, w.P, w.beta, s)
+            rq, rm, rb = megaflux_plan(n, w.P, w.beta, s)
+            assert (q.tolist(), moves.tolist(), blocks.tolist()) == (rq, rm, rb), (w.name, skew)
 
 # -------------------------------------------------------------------- MX formats ---
 # Expected codes and values below are worked by hand from the OCP Microscaling Formats (MX)
