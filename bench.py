@@ -4,10 +4,15 @@
 
 One step = route -> permute -> plan -> expert FFN (FC1, FC2) -> combine over one batch of
 seeded synthetic input already resident in HBM, timed as eager calls on one stream (--graph:
-as HIP-graph replays of the whole path; the eager figure is then reported beside it).
+as HIP-graph replays of the whole path; the eager figure is then reported beside it).  The
+default layer is the largest one that fits one GPU: one GPU's 32-expert share of a
+DeepSeek-V3-sized layer (T=32768, H=7168, I=2048, top-8 of 256) at Zipf skew 1.0.
+Protocol: a settle phase of whole steps (--settle-s seconds), W warm-up steps, then exactly
+K timed steps, each bracketed by HIP events; ms_per_step is the median step.
 Prints ONE JSON line: whole-path tokens/s, the grouped GEMM's TFLOP/s, the dominant kernel
 (FC1, the gate/up GEMM with fused SwiGLU) against the bf16 MFMA peak, per-call times, and the
-CPU oracle timed on a bounded sample of the same workload on the host cores.
+CPU oracle timed on a bounded sample of the same workload on the host cores (all threads,
+and one thread).
 """
 from __future__ import annotations
 
@@ -35,7 +40,12 @@ def parse():
     # a few hundred warm-up steps: the GPU's clocks take on the order of 100 ms to settle
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="olmoe_shaped")
+    ap.add_argument("--workload", default="deepseek_v3_share",
+                    help="layer shape (default: the largest one-GPU layer, one GPU's 32-expert share "
+                         "of a DeepSeek-V3-sized layer, T=32768, H=7168, I=2048)")
+    ap.add_argument("--settle-s", type=float, default=2.0,
+                    help="seconds of whole steps run before the warm-up steps, outside the timed "
+                         "region, so that the GPU clock has settled under this load")
     ap.add_argument("--skew", default=None, help="Zipf exponent or 'hot4' (default: middle skew)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--planner", choices=("moonep", "megaflux"), default="moonep",
@@ -97,31 +107,64 @@ class Step:
                 events[i + 1].record()
 
 
-def time_steps(step, steps, warmup, torch, graph=None):
-    """Wall time per step (HIP-graph replays of the whole path if `graph`, else eager calls)
-    and per-call durations from event-bracketed eager steps."""
-    run = graph.replay if graph is not None else step.run
-    for _ in range(warmup):
-        run()
+def settle(run, seconds, torch):
+    """Whole steps for about `seconds` of wall time (outside the timed region): the GPU's
+    clock takes on the order of a second to settle under a sustained load.  Returns (steps,
+    seconds)."""
+    if seconds <= 0:
+        return 0, 0.0
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
+    n = 0
+    while True:
+        for _ in range(4):
+            run()
+        n += 4
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            return n, el
+
+
+def time_steps(step, steps, warmup, torch, graph=None, settle_s=0.0):
+    """Times exactly `steps` steps (HIP-graph replays of the whole path if `graph`, else eager
+    calls) after a settle phase and `warmup` untimed steps.  Every timed step is bracketed by
+    HIP events on the stream the kernels run on (eager steps: also between its calls), so the
+    per-step and per-call figures are medians over the timed steps themselves; the wall clock
+    around the timed region (synchronised on both sides) is reported beside them."""
+    run = graph.replay if graph is not None else step.run
+    n_settle, t_settle = settle(run, settle_s, torch)
+    for _ in range(warmup):
         run()
+    ncall = len(step.calls)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(ncall + 1 if graph is None else 2)]
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if graph is None:
+            step.run(ev[i])
+        else:
+            ev[i][0].record()
+            graph.replay()
+            ev[i][1].record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
-    # per-call durations: HIP events on the stream the kernels are launched on
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(step.calls) + 1)]
-          for _ in range(steps)]
-    for i in range(steps):
-        step.run(ev[i])
-    torch.cuda.synchronize()
-    per = {c: sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)) / steps * 1e3
+    step_ms = [e[0].elapsed_time(e[-1]) for e in ev]
+    if graph is not None:
+        # per-call durations from event-bracketed eager steps after the timed region
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(ncall + 1)] for _ in range(steps)]
+        for i in range(steps):
+            step.run(ev[i])
+        torch.cuda.synchronize()
+    per = {c: float(np.median([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)])) * 1e3
            for j, c in enumerate(step.calls)}
     # the FC1 call starts with the tile-schedule kernel: time it alone on the same table, so
     # that the FC1 GEMM kernel's own duration is fc1 - schedule
     if step.layer.dtype == torch.bfloat16:
         per["fc1_schedule"] = schedule_us(step.layer, torch)
-    return wall, per
+    return {"median_s": float(np.median(step_ms)) * 1e-3, "mean_s": float(np.mean(step_ms)) * 1e-3,
+            "wall_s": wall, "per": per, "settle_steps": n_settle, "settle_s": t_settle}
 
 
 def schedule_us(layer, torch, n=50, reps=8):
@@ -271,18 +314,32 @@ def cpu_baseline(w, skew, T_s, target_s=12.0, precision="bf16"):
             steps_s[name] += t[k + 1] - t[k]
         return t[-1] - t[0]
 
-    t_probe = run(T_s)
-    for name in steps_s:
-        steps_s[name] = 0.0
-    want = int(T_s * target_s / max(t_probe, 1e-6))
-    n = max(w.P, min(w.T, want) // w.P * w.P)
-    # a whole batch that takes less than the target is run again until the target is reached
-    reps, dt = 0, 0.0
-    while reps == 0 or (n == w.T and dt < target_s):
-        dt += run(n)
-        reps += 1
-    what = (f"first {n} of {w.T} tokens of the same batch" if reps == 1 else
-            f"the whole batch of {w.T} tokens, {reps} times")
+    def sized(t_probe_tokens, target):
+        """Sizes a sample from a probe run to about `target` seconds and runs it; returns
+        (tokens, repetitions, seconds, description, per-step seconds)."""
+        t_probe = run(t_probe_tokens)
+        for name in steps_s:
+            steps_s[name] = 0.0
+        want = int(t_probe_tokens * target / max(t_probe, 1e-6))
+        n = max(w.P, min(w.T, want) // w.P * w.P)
+        # a whole batch that takes less than the target is run again until the target is reached
+        reps, dt = 0, 0.0
+        while reps == 0 or (n == w.T and dt < target):
+            dt += run(n)
+            reps += 1
+        what = (f"first {n} of {w.T} tokens of the same batch" if reps == 1 else
+                f"the whole batch of {w.T} tokens, {reps} times")
+        per_step = {k: round(v, 3) for k, v in steps_s.items()}
+        return n, reps, dt, what, per_step
+
+    cores = oracle.num_threads()
+    n, reps, dt, what, per_step = sized(T_s, target_s)
+    # the same oracle on one thread, over a shorter sample
+    oracle.set_num_threads(1)
+    try:
+        n1, reps1, dt1, what1, per_step1 = sized(w.P, target_s / 2)
+    finally:
+        oracle.set_num_threads(cores)
     cpu_model = None
     try:
         for line in open("/proc/cpuinfo"):
@@ -291,12 +348,14 @@ def cpu_baseline(w, skew, T_s, target_s=12.0, precision="bf16"):
                 break
     except OSError:
         pass
-    return {"value": round(n * reps / dt, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "cpu_model": cpu_model,
-            "per_step_s": {k: round(v, 3) for k, v in steps_s.items()},
-            "sample": f"{what}, whole path (route, permute, plan, "
-                      f"{'MX ' if precision == 'mx' else ''}FFN, combine), float64 plain C "
-                      f"with OpenMP, {dt:.1f} s"}
+    kind = f"{'MX ' if precision == 'mx' else ''}FFN"
+    return {"value": round(n * reps / dt, 3), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle", "cpu_model": cpu_model, "per_step_s": per_step,
+            "sample": f"{what}, whole path (route, permute, plan, {kind}, combine), float64 plain C "
+                      f"with OpenMP on {cores} threads, {dt:.1f} s",
+            "one_thread": {"value": round(n1 * reps1 / dt1, 3), "unit": "tokens/s", "cores": 1,
+                           "per_step_s": per_step1,
+                           "sample": f"{what1}, the same path on one thread, {dt1:.1f} s"}}
 
 
 def main():
@@ -341,21 +400,23 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def measure(sk, steps, warmup, lay=None, w1=None, w2=None):
+    def measure(sk, steps, warmup, lay=None, w1=None, w2=None, settle_s=0.0):
         lay = lay or layer
         w1, w2 = (w1, w2) if w1 is not None else (W1, W2)
         logits = torch.from_numpy(inputs.make_logits(w, sk)).to(dev)
         step = Step(lay, logits, x, w1, w2)
         graph = lay.capture(logits, x, w1, w2) if args.graph else None
-        wall, per = time_steps(step, steps, warmup, torch, graph)
-        eager_wall = time_steps(step, steps, 1, torch)[0] if graph is not None else wall
+        tm = time_steps(step, steps, warmup, torch, graph, settle_s)
+        tm["eager_median_s"] = (time_steps(step, steps, 1, torch)["median_s"] if graph is not None
+                                else tm["median_s"])
         counts = lay.counts.cpu()
         N = int(counts[w.expert_begin::w.expert_stride][: w.n_local].sum())
         nb = int(lay.n_blocks.item())
         del graph
-        return wall, per, N, nb, counts, eager_wall
+        return tm, N, nb, counts
 
-    wall, per, N, nb, counts, eager_wall = measure(skew, args.steps, args.warmup)
+    tm, N, nb, counts = measure(skew, args.steps, args.warmup, settle_s=args.settle_s)
+    wall, per = tm["median_s"], tm["per"]
     flops_fc1 = 4.0 * w.H * w.I * N
     flops_ffn = 6.0 * w.H * w.I * N
     fc1_s = (per["fc1"] - per.get("fc1_schedule", 0.0)) * 1e-6  # the FC1 GEMM kernel alone
@@ -402,7 +463,12 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(wall * 1e3, 4),
-        "eager_ms_per_step": round(eager_wall * 1e3, 4),
+        "timing": {"ms_per_step": "median of the timed steps' HIP-event durations",
+                   "mean_ms_per_step": round(tm["mean_s"] * 1e3, 4),
+                   "wall_ms_per_step": round(tm["wall_s"] * 1e3, 4),
+                   "eager_median_ms_per_step": round(tm["eager_median_s"] * 1e3, 4),
+                   "per_call_us": "medians over the timed steps",
+                   "settle_s": round(tm["settle_s"], 3), "settle_steps": tm["settle_steps"]},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -440,7 +506,8 @@ def main():
                                        expert_stride=w.expert_stride, block_m=w.beta,
                                        planner=args.planner, precision="mx")
         st = max(20, min(args.steps, 100))
-        wl_mx, pr_mx, n_mx, _, _, _ = measure(skew, st, st, lay_mx, wmx[0], wmx[1])
+        tm_mx, n_mx, _, _ = measure(skew, st, st, lay_mx, wmx[0], wmx[1], settle_s=0.5)
+        wl_mx, pr_mx = tm_mx["median_s"], tm_mx["per"]
         f1 = (pr_mx["fc1"] - pr_mx.get("fc1_schedule", 0.0)) * 1e-6
         line["mx_path"] = {
             "tokens_per_s": round(w.T / wl_mx, 1), "ms_per_step": round(wl_mx * 1e3, 4),
@@ -457,7 +524,9 @@ def main():
     if not args.no_all_skews:
         by = []
         for sk in w.skews:
-            wl, pr, n_, nb_, cnt_, _ = measure(sk, max(10, args.steps // 4), max(10, args.warmup // 4))
+            tm_, n_, nb_, cnt_ = measure(sk, max(10, args.steps // 4), max(10, args.warmup // 4),
+                                         settle_s=0.5)
+            wl, pr = tm_["median_s"], tm_["per"]
             f = 6.0 * w.H * w.I * n_
             ffn_t = (pr["fc1"] + pr["fc2"]) * 1e-6
             loc_ = cnt_[w.expert_begin::w.expert_stride][: w.n_local].tolist()

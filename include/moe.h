@@ -277,13 +277,31 @@ moe_status_t moe_expert_ffn_fc2(const void* act, const void* w2, moe_dtype_t dt,
                                 int32_t* workspace, int64_t workspace_elems,
                                 hipStream_t stream);
 
-/* The bf16 FC1 calls start with this: the GEMM tile schedule of the block table, written to
+/* Every FC1 call starts with this: the GEMM tile schedule of the block table, written to
  * `workspace` (each expert's row-contiguous blocks cut into 128-row pieces, paired into
- * 256-row tiles; the GEMMs' work counters cleared).  Exposed so that it can be timed apart
- * from the GEMM; calling it is never required.  Arguments as for moe_expert_ffn. */
+ * 256-row tiles; the GEMMs' work counters cleared), and the table's error word (below).
+ * Exposed so that it can be timed apart from the GEMM; calling it is never required.
+ * Arguments as for moe_expert_ffn. */
 moe_status_t moe_expert_ffn_tile_schedule(const int32_t* blocks, const int32_t* n_blocks,
-                                          int max_blocks, int E_loc, int32_t* workspace,
-                                          int64_t workspace_elems, hipStream_t stream);
+                                          int max_blocks, int E_loc, int64_t max_rows,
+                                          int32_t* workspace, int64_t workspace_elems,
+                                          hipStream_t stream);
+
+/* The table is data on the device and is checked there: a block (r, l, first, rows) is
+ * skipped unless 0 <= l < E_loc, 0 <= rows <= MOE_FFN_MAX_BLOCK_ROWS and
+ * 0 <= first <= first + rows <= max_rows; n_blocks is clamped to [0, max_blocks].  Each FC1
+ * call (the schedule) sets workspace[MOE_FFN_WS_ERR] to the OR of the MOE_FFN_ERR_* bits of
+ * what it skipped or clamped (0 for a table from moe_plan / moe_plan_blocks); blocks of 0
+ * rows are skipped silently.  Whatever the table holds, the FFN then reads and writes only
+ * inside its buffers (gathered rows outside [0, T) read as row 0 and are never stored).
+ * Blocks that overlap one another are a caller error: no access leaves the buffers, but
+ * rows no block covers may then be written. */
+#define MOE_FFN_WS_ERR 1
+#define MOE_FFN_MAX_BLOCK_ROWS 256
+#define MOE_FFN_ERR_EXPERT 1 /* expert index outside [0, E_loc) */
+#define MOE_FFN_ERR_ROWS 2   /* rows outside [0, MOE_FFN_MAX_BLOCK_ROWS] */
+#define MOE_FFN_ERR_RANGE 4  /* row range outside [0, max_rows) */
+#define MOE_FFN_ERR_COUNT 8  /* n_blocks outside [0, max_blocks] */
 
 /* moe_expert_ffn with the dispatch gather folded into FC1's loads: row p of the GEMM input is
  * x[row_token[p]] instead of xp[p] ([MF §2.1]: dispatch, FC1, FC2 and combine form one

@@ -48,7 +48,7 @@ _SIGNATURES = {
                                      _vp, _i32, _vp, _vp, _i64, _vp, _i64, _vp]),
     "moe_expert_ffn_fc1_gather": (_i32, [_vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp, _vp,
                                          _i32, _vp, _i64, _vp, _i64, _vp]),
-    "moe_expert_ffn_tile_schedule": (_i32, [_vp, _vp, _i32, _i32, _vp, _i64, _vp]),
+    "moe_expert_ffn_tile_schedule": (_i32, [_vp, _vp, _i32, _i32, _i64, _vp, _i64, _vp]),
     "moe_plan_blocks": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32,
                                _vp, _vp, _i32, _vp, _vp]),
     "moe_mx_quantize": (_i32, [_vp, _i32, _i64, _i64, _i32, _vp, _vp, _vp]),
@@ -243,14 +243,20 @@ def moe_expert_ffn(xp, w1, w2, blocks, n_blocks, act, yp, workspace, stream=None
            "moe_expert_ffn")
 
 
-def moe_expert_ffn_tile_schedule(blocks, n_blocks, E_loc, workspace, stream=None):
-    """The GEMM tile schedule that the bf16 FC1 calls compute first (for timing it alone)."""
+def moe_expert_ffn_tile_schedule(blocks, n_blocks, E_loc, max_rows, workspace, stream=None):
+    """The GEMM tile schedule (and the table check) that the FC1 calls compute first (for
+    timing it alone)."""
     _check(lib().moe_expert_ffn_tile_schedule(_ptr(blocks, torch.int32, "blocks"),
                                               _ptr(n_blocks, torch.int32, "n_blocks"),
-                                              blocks.shape[0], E_loc,
+                                              blocks.shape[0], E_loc, int(max_rows),
                                               _ptr(workspace, torch.int32, "workspace"),
                                               workspace.numel(), _stream(stream)),
            "moe_expert_ffn_tile_schedule")
+
+
+# workspace word holding the FFN's table error bits (MOE_FFN_WS_ERR and MOE_FFN_ERR_* in moe.h)
+FFN_WS_ERR = 1
+FFN_ERR_EXPERT, FFN_ERR_ROWS, FFN_ERR_RANGE, FFN_ERR_COUNT = 1, 2, 4, 8
 
 
 def moe_expert_ffn_gather(x, row_token, w1, w2, blocks, n_blocks, act, yp, workspace,
@@ -573,8 +579,13 @@ class RoutedExperts:
                            stream)
 
     def tile_schedule(self, stream=None):
-        moe_expert_ffn_tile_schedule(self.blocks, self.n_blocks, self.E_loc, self.ffn_workspace,
-                                     stream)
+        moe_expert_ffn_tile_schedule(self.blocks, self.n_blocks, self.E_loc, self.max_rows,
+                                     self.ffn_workspace, stream)
+
+    def ffn_error(self) -> int:
+        """The last FC1 call's table error bits (FFN_ERR_*; 0 for a plan's own table).
+        Synchronises the current stream."""
+        return int(self.ffn_workspace[FFN_WS_ERR].item())
 
     def combine(self, stream=None):
         moe_combine(self.yp, self.topk_w, self.entry_pos, self.out, stream)

@@ -168,14 +168,16 @@ moe_status_t moe_plan_blocks(const int32_t* expert_counts, int E, int expert_beg
 }
 
 moe_status_t moe_expert_ffn_tile_schedule(const int32_t* blocks, const int32_t* n_blocks,
-                                          int max_blocks, int E_loc, int32_t* workspace,
-                                          int64_t workspace_elems, hipStream_t stream) {
-    if (!blocks || !n_blocks || !workspace || max_blocks < 1 || E_loc < 1)
+                                          int max_blocks, int E_loc, int64_t max_rows,
+                                          int32_t* workspace, int64_t workspace_elems,
+                                          hipStream_t stream) {
+    if (!blocks || !n_blocks || !workspace || max_blocks < 1 || E_loc < 1 || max_rows < 1)
         return MOE_ERR_INVALID;
+    if (!aligned16(blocks)) return MOE_ERR_INVALID;  // 16-byte records
     if (workspace_elems < moe_ffn_workspace_elems(max_blocks)) return MOE_ERR_INVALID;
-    if (E_loc > 256) return MOE_ERR_UNSUPPORTED;
-    return launched(moe_launch_ffn_schedule(blocks, n_blocks, max_blocks, E_loc, workspace,
-                                            stream));
+    if (E_loc > 256 || max_rows > 0x7FFFFFFFLL) return MOE_ERR_UNSUPPORTED;
+    return launched(moe_launch_ffn_schedule(blocks, n_blocks, max_blocks, E_loc, max_rows,
+                                            workspace, stream));
 }
 
 moe_status_t moe_expert_ffn_fc1(const void* xp, const void* w1, moe_dtype_t dt, int H, int I,
@@ -184,18 +186,18 @@ moe_status_t moe_expert_ffn_fc1(const void* xp, const void* w1, moe_dtype_t dt, 
                                 int32_t* workspace, int64_t workspace_elems,
                                 hipStream_t stream) {
     if (!xp || !w1 || !blocks || !n_blocks || !act || !workspace) return MOE_ERR_INVALID;
-    if (!aligned16(xp) || !aligned16(w1) || !aligned16(act)) return MOE_ERR_INVALID;
+    if (!aligned16(xp) || !aligned16(w1) || !aligned16(act) || !aligned16(blocks))
+        return MOE_ERR_INVALID;
     moe_status_t st = check_ffn_shape(dt, H, I, E_loc, max_blocks, max_rows);
     if (st != MOE_OK) return st;
     if (workspace_elems < moe_ffn_workspace_elems(max_blocks)) return MOE_ERR_INVALID;
     if (E_loc > 256) return MOE_ERR_UNSUPPORTED;
-    if (dt == MOE_BF16) {
-        st = launched(moe_launch_ffn_schedule(blocks, n_blocks, max_blocks, E_loc, workspace,
-                                              stream));
-        if (st != MOE_OK) return st;
-    }
-    return launched(moe_launch_ffn_fc1(xp, w1, dt, H, I, blocks, n_blocks, max_blocks,
-                                       workspace, act, max_rows, nullptr, stream));
+    // the schedule checks every block (and writes the error word) for both dtypes
+    st = launched(moe_launch_ffn_schedule(blocks, n_blocks, max_blocks, E_loc, max_rows,
+                                          workspace, stream));
+    if (st != MOE_OK) return st;
+    return launched(moe_launch_ffn_fc1(xp, w1, dt, H, I, E_loc, blocks, n_blocks, max_blocks,
+                                       workspace, act, max_rows, max_rows, nullptr, stream));
 }
 
 moe_status_t moe_expert_ffn_fc1_gather(const void* x, const int32_t* row_token, int T,
@@ -206,20 +208,19 @@ moe_status_t moe_expert_ffn_fc1_gather(const void* x, const int32_t* row_token, 
                                        hipStream_t stream) {
     if (!x || !row_token || !w1 || !blocks || !n_blocks || !act || !workspace)
         return MOE_ERR_INVALID;
-    if (!aligned16(x) || !aligned16(w1) || !aligned16(act) || T < 1) return MOE_ERR_INVALID;
+    if (!aligned16(x) || !aligned16(w1) || !aligned16(act) || !aligned16(blocks) || T < 1)
+        return MOE_ERR_INVALID;
     moe_status_t st = check_ffn_shape(dt, H, I, E_loc, max_blocks, max_rows);
     if (st != MOE_OK) return st;
     if (workspace_elems < moe_ffn_workspace_elems(max_blocks)) return MOE_ERR_INVALID;
     if (E_loc > 256) return MOE_ERR_UNSUPPORTED;
     // the bf16 GEMM addresses x rows with 32-bit byte offsets
     if (dt == MOE_BF16 && (int64_t)T * H * 2 > 0xFFFFFFFFLL - 16) return MOE_ERR_UNSUPPORTED;
-    if (dt == MOE_BF16) {
-        st = launched(moe_launch_ffn_schedule(blocks, n_blocks, max_blocks, E_loc, workspace,
-                                              stream));
-        if (st != MOE_OK) return st;
-    }
-    return launched(moe_launch_ffn_fc1(x, w1, dt, H, I, blocks, n_blocks, max_blocks, workspace,
-                                       act, T, row_token, stream));
+    st = launched(moe_launch_ffn_schedule(blocks, n_blocks, max_blocks, E_loc, max_rows,
+                                          workspace, stream));
+    if (st != MOE_OK) return st;
+    return launched(moe_launch_ffn_fc1(x, w1, dt, H, I, E_loc, blocks, n_blocks, max_blocks,
+                                       workspace, act, max_rows, T, row_token, stream));
 }
 
 moe_status_t moe_expert_ffn_fc2(const void* act, const void* w2, moe_dtype_t dt, int H, int I,
@@ -233,7 +234,7 @@ moe_status_t moe_expert_ffn_fc2(const void* act, const void* w2, moe_dtype_t dt,
     if (st != MOE_OK) return st;
     if (workspace_elems < moe_ffn_workspace_elems(max_blocks)) return MOE_ERR_INVALID;
     if (E_loc > 256) return MOE_ERR_UNSUPPORTED;
-    return launched(moe_launch_ffn_fc2(act, w2, dt, H, I, blocks, n_blocks, max_blocks,
+    return launched(moe_launch_ffn_fc2(act, w2, dt, H, I, E_loc, blocks, n_blocks, max_blocks,
                                        workspace, yp, max_rows, stream));
 }
 
@@ -314,10 +315,11 @@ moe_status_t moe_expert_ffn_mx_fc1(const uint8_t* xq, const uint8_t* xs, const i
     if (st != MOE_OK) return st;
     if (x_rows < 1 || (!row_token && x_rows < max_rows)) return MOE_ERR_INVALID;
     if (x_rows * H > 0xFFFFFFFFLL - 256) return MOE_ERR_UNSUPPORTED;
-    st = launched(moe_launch_ffn_schedule(blocks, n_blocks, max_blocks, E_loc, workspace, stream));
+    st = launched(moe_launch_ffn_schedule(blocks, n_blocks, max_blocks, E_loc, max_rows, workspace,
+                                          stream));
     if (st != MOE_OK) return st;
-    return launched(moe_launch_ffn_mx_fc1(xq, xs, row_token, w1q, w1s, H, I, max_blocks, workspace,
-                                          actq, acts, stream));
+    return launched(moe_launch_ffn_mx_fc1(xq, xs, row_token, x_rows, w1q, w1s, H, I, max_blocks,
+                                          workspace, actq, acts, stream));
 }
 
 moe_status_t moe_expert_ffn_mx_fc2(const uint8_t* actq, const uint8_t* acts, const uint8_t* w2q,
@@ -332,7 +334,7 @@ moe_status_t moe_expert_ffn_mx_fc2(const uint8_t* actq, const uint8_t* acts, con
                                          workspace, workspace_elems);
     if (st != MOE_OK) return st;
     return launched(moe_launch_ffn_mx_fc2(actq, acts, w2q, w2s, H, I, max_blocks, workspace,
-                                          static_cast<uint16_t*>(yp), stream));
+                                          static_cast<uint16_t*>(yp), max_rows, stream));
 }
 
 moe_status_t moe_expert_ffn_mx(const uint8_t* xq, const uint8_t* xs, const int32_t* row_token,

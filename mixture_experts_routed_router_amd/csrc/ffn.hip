@@ -33,6 +33,10 @@
 namespace {
 
 using namespace moe_ffn_ws;
+static_assert(MOE_FFN_WS_ERR == WS_ERR && MOE_FFN_MAX_BLOCK_ROWS == kMaxBlockRows &&
+                  MOE_FFN_ERR_EXPERT == FFN_ERR_EXPERT && MOE_FFN_ERR_ROWS == FFN_ERR_ROWS &&
+                  MOE_FFN_ERR_RANGE == FFN_ERR_RANGE && MOE_FFN_ERR_COUNT == FFN_ERR_COUNT,
+              "the error word's layout in moe.h");
 constexpr int BN = 256;      // B rows per tile (FC1: 128 gate + 128 up; FC2: 256 columns of H)
 constexpr int BK = 64;       // K slice per LDS stage: 128-byte rows = whole cache lines
 constexpr int kWaves = 8;    // two waves per SIMD
@@ -95,6 +99,19 @@ __device__ __forceinline__ bf16x8_t lds_frag(const uint8_t* stage, int row, bool
 // thread per expert) touch LDS only; larger tables are walked in global memory.
 constexpr int kSchedLds = 3072;
 
+// FFN_ERR_* bits of table entry (expert l, first row, rows) for E_loc experts and max_rows
+// rows.  The schedule takes a block only when this is 0 and rows > 0, which keeps every tile
+// inside [0, max_rows) and every expert index inside the weights, whatever the table holds;
+// blocks of at most kMaxBlockRows rows also keep the tiles within their 2 * max_blocks
+// records (an expert's 128-row pieces number at most twice its blocks).
+__device__ __forceinline__ int block_error(int l, int first, int rows, int E_loc, int64_t max_rows) {
+    int e = 0;
+    if (l < 0 || l >= E_loc) e |= FFN_ERR_EXPERT;
+    if (rows < 0 || rows > kMaxBlockRows) e |= FFN_ERR_ROWS;
+    if (first < 0 || (int64_t)first + (rows > 0 ? rows : 0) > max_rows) e |= FFN_ERR_RANGE;
+    return e;
+}
+
 // Exclusive prefix sum of v over the 256 threads of the workgroup (thread order); *total gets
 // the sum.  part holds one int per wave.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* part, int* total) {
@@ -131,19 +148,26 @@ struct SchedShared {
     unsigned long long mask[4][256];
     int s_l[kSchedLds], s_first[kSchedLds], s_rows[kSchedLds], s_sorted[kSchedLds];
     int scan_part[4];
+    int err;
 };
 
 // kLds: the table (nb <= kSchedLds blocks) has been staged in sh.s_*; otherwise it is read
 // from global memory.  Two instantiations, so that neither path carries the other's loads.
 template <bool kLds>
 __device__ __forceinline__ void schedule_body(const int32_t* __restrict__ blocks, int nb,
-                                              int max_blocks, int E_loc,
+                                              int max_blocks, int E_loc, int64_t max_rows,
                                               int32_t* __restrict__ ws, SchedShared& sh) {
     const int tid = threadIdx.x, lane = moe_lane_id(), wave = tid / MOE_WAVE;
     int32_t* sorted_g = ws + WS_HEAD;
     int32_t* tiles = ws + WS_HEAD + max_blocks;
+    // the block's expert, or -1 for a block the schedule skips
     auto blk_l = [&](int b) {
-        if constexpr (kLds) return sh.s_l[b]; else return blocks[4 * b + 1];
+        if constexpr (kLds) {
+            return sh.s_l[b];
+        } else {
+            const int4 v = reinterpret_cast<const int4*>(blocks)[b];
+            return block_error(v.y, v.z, v.w, E_loc, max_rows) == 0 && v.w > 0 ? v.y : -1;
+        }
     };
     auto blk_first = [&](int b) {
         if constexpr (kLds) return sh.s_first[b]; else return blocks[4 * b + 2];
@@ -155,7 +179,10 @@ __device__ __forceinline__ void schedule_body(const int32_t* __restrict__ blocks
         if constexpr (kLds) return sh.s_sorted[i]; else return sorted_g[i];
     };
 
-    for (int b = tid; b < nb; b += 256) atomicAdd(&sh.cnt[blk_l(b)], 1);
+    for (int b = tid; b < nb; b += 256) {
+        const int l = blk_l(b);
+        if (l >= 0) atomicAdd(&sh.cnt[l], 1);
+    }
     __syncthreads();
     {
         int total;
@@ -256,17 +283,25 @@ __device__ __forceinline__ void schedule_body(const int32_t* __restrict__ blocks
 // Common case: every expert's blocks cover one contiguous row range (a moe_plan table: an
 // expert's shares are consecutive ranges of its segment).  Then its pieces are 128-row cuts
 // of that range and each tile follows from the expert's first row and row count alone.
+// Every block is checked here first (block_error); the error word of the call is written.
 __device__ __forceinline__ bool schedule_contiguous(const int32_t* __restrict__ blocks, int nb,
-                                                    int max_blocks, int E_loc,
+                                                    int max_blocks, int E_loc, int64_t max_rows,
                                                     int32_t* __restrict__ ws, SchedShared& sh) {
     const int tid = threadIdx.x;
     for (int b = tid; b < nb; b += 256) {
         const int4 v = reinterpret_cast<const int4*>(blocks)[b];
+        const int e = block_error(v.y, v.z, v.w, E_loc, max_rows);
+        if (e != 0) {
+            atomicOr(&sh.err, e);
+            continue;
+        }
+        if (v.w == 0) continue;
         atomicAdd(&sh.sum_rows[v.y], v.w);
         atomicMin(&sh.min_first[v.y], v.z);
         atomicMax(&sh.max_end[v.y], v.z + v.w);
     }
     __syncthreads();
+    if (tid == 0) ws[WS_ERR] = sh.err;
     // blocks never overlap, so the union is one range exactly when its span equals the sum
     const bool ok = tid >= E_loc || sh.sum_rows[tid] == 0 ||
                     sh.sum_rows[tid] == sh.max_end[tid] - sh.min_first[tid];
@@ -304,12 +339,13 @@ __device__ __forceinline__ bool schedule_contiguous(const int32_t* __restrict__ 
 
 __global__ void __launch_bounds__(256)
 ffn_schedule_kernel(const int32_t* __restrict__ blocks, const int32_t* __restrict__ n_blocks_ptr,
-                    int max_blocks, int E_loc, int32_t* __restrict__ ws) {
+                    int max_blocks, int E_loc, int64_t max_rows, int32_t* __restrict__ ws) {
     __shared__ SchedShared sh;
     const int tid = threadIdx.x;
-    int nb = *n_blocks_ptr;
-    nb = nb < max_blocks ? nb : max_blocks;
+    const int nb_in = *n_blocks_ptr;
+    const int nb = nb_in < 0 ? 0 : (nb_in < max_blocks ? nb_in : max_blocks);
     if (tid >= WS_CTR_FC1 && tid < WS_HEAD) ws[tid] = 0;  // item and finished counters
+    if (tid == 0) sh.err = nb_in < 0 || nb_in > max_blocks ? FFN_ERR_COUNT : 0;
     for (int l = tid; l < E_loc; l += 256) {
         sh.cnt[l] = 0;
         sh.running[l] = 0;
@@ -318,19 +354,20 @@ ffn_schedule_kernel(const int32_t* __restrict__ blocks, const int32_t* __restric
         sh.max_end[l] = 0;
     }
     __syncthreads();
-    if (schedule_contiguous(blocks, nb, max_blocks, E_loc, ws, sh)) return;
+    if (schedule_contiguous(blocks, nb, max_blocks, E_loc, max_rows, ws, sh)) return;
     if (nb <= kSchedLds) {
         for (int b = tid; b < nb; b += 256) {
             const int4 v = reinterpret_cast<const int4*>(blocks)[b];
-            sh.s_l[b] = v.y;
+            const bool ok = block_error(v.y, v.z, v.w, E_loc, max_rows) == 0 && v.w > 0;
+            sh.s_l[b] = ok ? v.y : -1;  // skipped
             sh.s_first[b] = v.z;
             sh.s_rows[b] = v.w;
         }
         __syncthreads();
-        schedule_body<true>(blocks, nb, max_blocks, E_loc, ws, sh);
+        schedule_body<true>(blocks, nb, max_blocks, E_loc, max_rows, ws, sh);
     } else {
         __syncthreads();
-        schedule_body<false>(blocks, nb, max_blocks, E_loc, ws, sh);
+        schedule_body<false>(blocks, nb, max_blocks, E_loc, max_rows, ws, sh);
     }
 }
 
@@ -493,7 +530,9 @@ __device__ __forceinline__ void decode_step(int s, Item& n, const GemmArgs& g, Q
                 const int copies = n.rows_a / 64;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int tok = q < copies && (int)n.offa[q] >= 0 ? (int)n.offa[q] : 0;
+                    // row_token -1 (padding) or out of range: read row 0, never stored
+                    const int t = (int)n.offa[q];
+                    const int tok = q < copies && t >= 0 && t < g.a_rows ? t : 0;
                     n.offa[q] = (uint32_t)tok * (uint32_t)g.Kdim * 2u + seg_lchunk * 16u;
                 }
             }
@@ -824,7 +863,9 @@ ffn_bf16_kernel(const uint16_t* __restrict__ A, int64_t a_rows, int Kdim,
 }
 
 // float32 path (small layers): C[p][c] = A[p] . B[l][c] over the block table (FC1: SiLU of
-// the gate product times the up product, B rows c and I + c).  One workgroup per (block, 64
+// the gate product times the up product, B rows c and I + c).  Blocks that fail block_error
+// are skipped (the schedule pass of the same call reports them); gathered rows outside
+// [0, a_rows) read as zeros.  One workgroup per (block, 64
 // output columns), grid-stride over those items; K is staged 64 at a time through LDS: the
 // block's A rows (64 rows per pass, gathered through `gather` when given) and the 64
 // columns' B rows.  Thread (rg, c) accumulates rows rg, rg+4, ..., rg+60 of column c with
@@ -832,10 +873,11 @@ ffn_bf16_kernel(const uint16_t* __restrict__ A, int64_t a_rows, int Kdim,
 // row c); A reads are wave-uniform broadcasts.
 template <bool kSwiGLU>
 __global__ void __launch_bounds__(256)
-ffn_f32_kernel(const float* __restrict__ A, const int32_t* __restrict__ gather, int Kdim,
-               const float* __restrict__ B, int64_t b_expert_stride, int I,
+ffn_f32_kernel(const float* __restrict__ A, const int32_t* __restrict__ gather, int64_t a_rows,
+               int Kdim, const float* __restrict__ B, int64_t b_expert_stride, int I,
                float* __restrict__ C, int ldc, int n_cols, const int32_t* __restrict__ blocks,
-               const int32_t* __restrict__ n_blocks_ptr, int max_blocks) {
+               const int32_t* __restrict__ n_blocks_ptr, int max_blocks, int E_loc,
+               int64_t max_rows) {
     constexpr int TC = 64, TK = 64, TR = 64, RPT = TR / 4;
     __shared__ float a_s[TR][TK + 1];
     __shared__ float g_s[TC][TK + 1];
@@ -847,6 +889,7 @@ ffn_f32_kernel(const float* __restrict__ A, const int32_t* __restrict__ gather, 
     for (int item = blockIdx.x; item < nb * nct; item += gridDim.x) {
         const int b = item / nct, ct = item - b * nct;
         const int l = blocks[4 * b + 1], row0 = blocks[4 * b + 2], m = blocks[4 * b + 3];
+        if (block_error(l, row0, m, E_loc, max_rows) != 0) continue;  // uniform: whole workgroup
         const float* Bl = B + (int64_t)l * b_expert_stride;
         const int col = ct * TC + c;
         for (int r0 = 0; r0 < m; r0 += TR) {
@@ -860,7 +903,7 @@ ffn_f32_kernel(const float* __restrict__ A, const int32_t* __restrict__ gather, 
                     float v = 0.f;
                     if (r < m && k0 + kk < Kdim) {
                         const int64_t arow = gather ? gather[row0 + r] : row0 + r;
-                        v = A[arow * Kdim + k0 + kk];
+                        if (arow >= 0 && arow < a_rows) v = A[arow * Kdim + k0 + kk];
                     }
                     a_s[rr][kk] = v;
                 }
@@ -914,21 +957,22 @@ int64_t moe_ffn_workspace_elems_impl(int max_blocks) {
 }
 
 hipError_t moe_launch_ffn_schedule(const int32_t* blocks, const int32_t* n_blocks, int max_blocks,
-                                   int E_loc, int32_t* ws, hipStream_t stream) {
-    ffn_schedule_kernel<<<1, 256, 0, stream>>>(blocks, n_blocks, max_blocks, E_loc, ws);
+                                   int E_loc, int64_t max_rows, int32_t* ws, hipStream_t stream) {
+    ffn_schedule_kernel<<<1, 256, 0, stream>>>(blocks, n_blocks, max_blocks, E_loc, max_rows, ws);
     return hipGetLastError();
 }
 
 hipError_t moe_launch_ffn_fc1(const void* a, const void* w1, moe_dtype_t dt, int H, int I,
-                              const int32_t* blocks, const int32_t* n_blocks, int max_blocks,
-                              int32_t* ws, void* act, int64_t a_rows, const int32_t* gather,
-                              hipStream_t stream) {
+                              int E_loc, const int32_t* blocks, const int32_t* n_blocks,
+                              int max_blocks, int32_t* ws, void* act, int64_t max_rows,
+                              int64_t a_rows, const int32_t* gather, hipStream_t stream) {
     if (dt == MOE_F32) {
         const int64_t items = (int64_t)max_blocks * ((I + 63) / 64);
         const int grid = items < 2048 ? (int)items : 2048;
         ffn_f32_kernel<true><<<grid, 256, 0, stream>>>(
-            static_cast<const float*>(a), gather, H, static_cast<const float*>(w1),
-            (int64_t)2 * I * H, I, static_cast<float*>(act), I, I, blocks, n_blocks, max_blocks);
+            static_cast<const float*>(a), gather, a_rows, H, static_cast<const float*>(w1),
+            (int64_t)2 * I * H, I, static_cast<float*>(act), I, I, blocks, n_blocks, max_blocks,
+            E_loc, max_rows);
         return hipGetLastError();
     }
     if (gather)
@@ -945,15 +989,16 @@ hipError_t moe_launch_ffn_fc1(const void* a, const void* w1, moe_dtype_t dt, int
 }
 
 hipError_t moe_launch_ffn_fc2(const void* act, const void* w2, moe_dtype_t dt, int H, int I,
-                              const int32_t* blocks, const int32_t* n_blocks, int max_blocks,
-                              int32_t* ws, void* yp, int64_t max_rows,
+                              int E_loc, const int32_t* blocks, const int32_t* n_blocks,
+                              int max_blocks, int32_t* ws, void* yp, int64_t max_rows,
                               hipStream_t stream) {
     if (dt == MOE_F32) {
         const int64_t items = (int64_t)max_blocks * ((H + 63) / 64);
         const int grid = items < 2048 ? (int)items : 2048;
         ffn_f32_kernel<false><<<grid, 256, 0, stream>>>(
-            static_cast<const float*>(act), nullptr, I, static_cast<const float*>(w2),
-            (int64_t)H * I, I, static_cast<float*>(yp), H, H, blocks, n_blocks, max_blocks);
+            static_cast<const float*>(act), nullptr, max_rows, I, static_cast<const float*>(w2),
+            (int64_t)H * I, I, static_cast<float*>(yp), H, H, blocks, n_blocks, max_blocks,
+            E_loc, max_rows);
         return hipGetLastError();
     }
     ffn_bf16_kernel<false, false><<<persistent_grid(), kThreads, 0, stream>>>(

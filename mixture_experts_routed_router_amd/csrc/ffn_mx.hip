@@ -57,6 +57,7 @@ struct MxArgs {
     const uint8_t* aq;      // token codes [a_rows, K] (FP8); the rows of x with `gather`
     const uint8_t* as;      // token scales [a_rows, sp]
     const int32_t* gather;  // row_token (row p's input is row gather[p]) or nullptr
+    int64_t a_rows;         // rows of aq / as (gathered token rows outside [0, a_rows) read row 0)
     int K, sp;              // values per row, scale bytes per row
     const uint8_t* wq;      // weight codes [E_loc][wrows, K / 2] (FP4)
     const uint8_t* wsc;     // weight scales [E_loc][wrows, sp]
@@ -188,7 +189,7 @@ __device__ __forceinline__ void decode_step(int step, MxItem& n, const MxArgs& g
                 for (int j = 0; j < 4; ++j) {
                     const int r = 8 * (c.wave + 8 * j) + (c.lane >> 3);
                     int t = g.gather ? mx_gidx[r] : tile_pos(n, r);
-                    t = t >= 0 ? t : 0;  // row_token -1 (no entry): read, unused
+                    t = t >= 0 && t < g.a_rows ? t : 0;  // row_token -1 (no entry): read, unused
                     n.tok[j] = (uint32_t)t * (uint32_t)g.K + 16u * c.tok_lc;
                 }
 #pragma unroll
@@ -198,7 +199,7 @@ __device__ __forceinline__ void decode_step(int step, MxItem& n, const MxArgs& g
                 if (c.wave < 4) {
                     const int r = 64 * c.wave + c.lane;
                     int t = g.gather ? mx_gidx[r] : tile_pos(n, r);
-                    t = t >= 0 ? t : 0;
+                    t = t >= 0 && t < g.a_rows ? t : 0;
                     n.sc = (uint32_t)t * (uint32_t)g.sp;
                 } else {
                     n.sc = w_row<kFC1>(g, n.nt, 64 * (c.wave - 4) + c.lane) * (uint32_t)g.sp;
@@ -540,13 +541,15 @@ int mx_grid() {
 }  // namespace
 
 hipError_t moe_launch_ffn_mx_fc1(const uint8_t* xq, const uint8_t* xs, const int32_t* gather,
-                                 const uint8_t* w1q, const uint8_t* w1s, int H, int I,
+                                 int64_t x_rows, const uint8_t* w1q, const uint8_t* w1s, int H,
+                                 int I,
                                  int max_blocks, int32_t* ws, uint8_t* actq, uint8_t* acts,
                                  hipStream_t stream) {
     MxArgs g{};
     g.aq = xq;
     g.as = xs;
     g.gather = gather;
+    g.a_rows = x_rows;
     g.K = H;
     g.sp = (int)moe_mx_scale_pitch_impl(H);
     g.wq = w1q;
@@ -567,11 +570,12 @@ hipError_t moe_launch_ffn_mx_fc1(const uint8_t* xq, const uint8_t* xs, const int
 
 hipError_t moe_launch_ffn_mx_fc2(const uint8_t* actq, const uint8_t* acts, const uint8_t* w2q,
                                  const uint8_t* w2s, int H, int I, int max_blocks, int32_t* ws,
-                                 uint16_t* yp, hipStream_t stream) {
+                                 uint16_t* yp, int64_t max_rows, hipStream_t stream) {
     MxArgs g{};
     g.aq = actq;
     g.as = acts;
     g.gather = nullptr;
+    g.a_rows = max_rows;
     g.K = I;
     g.sp = (int)moe_mx_scale_pitch_impl(I);
     g.wq = w2q;

@@ -34,25 +34,26 @@ hipError_t moe_launch_plan_blocks(const int32_t* counts, int begin, int stride, 
                                   int max_moves, int32_t* blocks, int32_t* n_blocks,
                                   int max_blocks, int32_t* err_word, hipStream_t stream);
 hipError_t moe_launch_ffn_schedule(const int32_t* blocks, const int32_t* n_blocks, int max_blocks,
-                                   int E_loc, int32_t* ws, hipStream_t stream);
+                                   int E_loc, int64_t max_rows, int32_t* ws, hipStream_t stream);
 
 hipError_t moe_launch_ffn_fc1(const void* a, const void* w1, moe_dtype_t dt, int H, int I,
-                              const int32_t* blocks, const int32_t* n_blocks, int max_blocks,
-                              int32_t* ws, void* act, int64_t a_rows, const int32_t* gather,
-                              hipStream_t stream);
+                              int E_loc, const int32_t* blocks, const int32_t* n_blocks,
+                              int max_blocks, int32_t* ws, void* act, int64_t max_rows,
+                              int64_t a_rows, const int32_t* gather, hipStream_t stream);
 
 hipError_t moe_launch_ffn_fc2(const void* act, const void* w2, moe_dtype_t dt, int H, int I,
-                              const int32_t* blocks, const int32_t* n_blocks, int max_blocks,
-                              int32_t* ws, void* yp, int64_t max_rows,
+                              int E_loc, const int32_t* blocks, const int32_t* n_blocks,
+                              int max_blocks, int32_t* ws, void* yp, int64_t max_rows,
                               hipStream_t stream);
 
 hipError_t moe_launch_ffn_mx_fc1(const uint8_t* xq, const uint8_t* xs, const int32_t* gather,
-                                 const uint8_t* w1q, const uint8_t* w1s, int H, int I,
+                                 int64_t x_rows, const uint8_t* w1q, const uint8_t* w1s, int H,
+                                 int I,
                                  int max_blocks, int32_t* ws, uint8_t* actq, uint8_t* acts,
                                  hipStream_t stream);
 hipError_t moe_launch_ffn_mx_fc2(const uint8_t* actq, const uint8_t* acts, const uint8_t* w2q,
                                  const uint8_t* w2s, int H, int I, int max_blocks, int32_t* ws,
-                                 uint16_t* yp, hipStream_t stream);
+                                 uint16_t* yp, int64_t max_rows, hipStream_t stream);
 inline int64_t moe_mx_scale_pitch_impl(int64_t cols) { return (cols / 32 + 3) / 4 * 4; }
 hipError_t moe_launch_mx_quantize(const void* src, moe_dtype_t dt, int64_t rows, int64_t cols,
                                   int fmt, uint8_t* codes, uint8_t* scales, hipStream_t stream);

@@ -90,6 +90,16 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Threads of the oracle's parallel loops from now on (n >= 1); returns the new count. */
+int oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+    return oracle_num_threads();
+}
+
 /* ------------------------------------------------------------------------ route --- */
 
 /* Router top-k and routing weights.  [MF §1]: each token is sent to k experts and their

@@ -50,6 +50,8 @@ def _load():
         lib.oracle_double_to_bf16.restype = ctypes.c_uint16
         lib.oracle_double_to_bf16.argtypes = [ctypes.c_double]
         lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_set_num_threads.restype = ctypes.c_int
+        lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
         for name in ("oracle_route", "oracle_route_ref", "oracle_router_logits", "oracle_permute",
                      "oracle_plan", "oracle_plan_blocks", "oracle_ffn_rows", "oracle_ffn_blocks",
                      "oracle_combine", "oracle_mx_quantize", "oracle_mx_dequantize",
@@ -71,6 +73,11 @@ def _check(rc: int, what: str):
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> int:
+    """Threads of the oracle's OpenMP loops from now on; returns the count in effect."""
+    return int(_load().oracle_set_num_threads(int(n)))
 
 
 def double_to_bf16(v: float) -> int:

@@ -22,6 +22,37 @@ def rel_frob(got: np.ndarray, ref: np.ndarray) -> float:
     return float(np.linalg.norm(got - ref) / (n if n > 0 else 1.0))
 
 
+def check_rows(got: np.ndarray, ref: np.ndarray, what: str, row_tol: float = 1e-2,
+               ulp_rel: float = 2.0 ** -7, rms_frac: float = 2e-3, extra=None) -> dict:
+    """Element-resolving comparison of bf16 output rows (float64 views) with the oracle's, next
+    to the layer-wide relative Frobenius bar:
+      * every row's own relative Frobenius error is at most row_tol, and
+      * every element satisfies |got - ref| <= ulp_rel |ref| + rms_frac rms(ref row) + extra.
+    Both sides round to bf16 once from float32 (HIP) or float64 (oracle) accumulation, so a
+    correct element differs by at most one bf16 ulp (<= 2^-7 |ref|) plus the accumulation
+    difference, which is orders of magnitude below rms_frac of the row.  `extra` carries what
+    the step's own inputs already differ by, propagated exactly (the sum over the reduction of
+    |input difference| x |weight|): an input that rounded to the neighbouring bf16 value moves
+    the output by that much and no more.  A wrong element, a wrong column block or a wrong row
+    moves by about the row's rms.  Returns the worst figures."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    rms = np.sqrt(np.mean(ref * ref, axis=1, keepdims=True))
+    diff = np.abs(got - ref)
+    bound = ulp_rel * np.abs(ref) + rms_frac * rms + 1e-30
+    if extra is not None:
+        bound = bound + 1.01 * np.asarray(extra, np.float64)
+    viol = diff > bound
+    assert not viol.any(), (what, "elements out of bound", int(viol.sum()),
+                            [tuple(int(v) for v in i) for i in np.argwhere(viol)[:8]])
+    rnorm = np.linalg.norm(ref, axis=1)
+    row_err = np.linalg.norm(got - ref, axis=1) / np.where(rnorm > 0, rnorm, 1.0)
+    assert row_err.max(initial=0.0) <= row_tol, (what, "row", int(row_err.argmax()), float(row_err.max()))
+    return {"max_row_err": float(row_err.max(initial=0.0)),
+            "max_elem_ratio": float((diff / bound).max(initial=0.0))}
+
+
 def to_f64(a: np.ndarray) -> np.ndarray:
     return oracle.bf16_to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)
 
@@ -160,6 +191,22 @@ def row_experts(blocks: np.ndarray, rows: np.ndarray) -> np.ndarray:
     for _, l, b0, m in blocks.tolist():
         ex[b0:b0 + m] = l
     return ex[rows]
+
+
+def tile_rows(ref: OracleIndex, seed: int = 0, piece: int = 128, sub: int = 32) -> np.ndarray:
+    """One random row from every `sub`-row block of every `piece`-row cut of each expert's
+    rows.  The FFN's tile schedule cuts each expert's row range into 128-row pieces (two per
+    256-row GEMM tile) and each wave computes 32-row blocks of a piece, so this reaches every
+    tile, both halves, and every 32-row block of the GEMMs, over all their column tiles."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for l in range(len(ref.offsets) - 1):
+        first = int(ref.offsets[l])
+        n = int(np.count_nonzero(ref.row_token[first:int(ref.offsets[l + 1])] >= 0))
+        for p0 in range(0, n, piece):
+            for s0 in range(p0, min(p0 + piece, n), sub):
+                out.append(first + int(rng.integers(s0, min(s0 + sub, n))))
+    return np.array(sorted(set(out)), np.int64)
 
 
 def sample_rows(ref: OracleIndex, n: int, seed: int = 0) -> np.ndarray:

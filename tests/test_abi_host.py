@@ -184,9 +184,13 @@ def test_ffn_and_combine_reject(lib):
     gather = lambda row_token=P[8], T=64, H=128, ws_elems=272: lib.moe_expert_ffn_gather(
         P[0], row_token, T, P[1], P[2], 1, H, 256, 8, P[3], P[4], 16, P[5], P[6], 1024, P[7],
         ws_elems, NULL)
-    assert lib.moe_expert_ffn_tile_schedule(P[3], P[4], 16, 8, P[7], 271, NULL) == INVALID
-    assert lib.moe_expert_ffn_tile_schedule(NULL, P[4], 16, 8, P[7], 272, NULL) == INVALID
-    assert lib.moe_expert_ffn_tile_schedule(P[3], P[4], 16, 300, P[7], 272, NULL) == UNSUPPORTED
+    sched = lib.moe_expert_ffn_tile_schedule
+    assert sched(P[3], P[4], 16, 8, 1024, P[7], 271, NULL) == INVALID
+    assert sched(NULL, P[4], 16, 8, 1024, P[7], 272, NULL) == INVALID
+    assert sched(P[3], P[4], 16, 300, 1024, P[7], 272, NULL) == UNSUPPORTED
+    assert sched(P[3], P[4], 16, 8, 0, P[7], 272, NULL) == INVALID              # no rows
+    assert sched(ctypes.c_void_p(0x1008), P[4], 16, 8, 1024, P[7], 272, NULL) == INVALID  # 16-B records
+    assert ffn(1, 128, 256, blocks=ctypes.c_void_p(0x1008)) == INVALID
     assert gather(row_token=NULL) == INVALID
     assert gather(T=0) == INVALID
     assert gather(ws_elems=271) == INVALID

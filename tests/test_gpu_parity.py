@@ -10,8 +10,9 @@ import torch
 
 import oracle
 from mixture_experts_routed_router_amd import binding, inputs
-from parity_helpers import (check_index_parity, check_xp, host, oracle_index, random_case,
-                            rel_frob, row_experts, run_gpu, sample_rows, to_f64, workload_case)
+from parity_helpers import (check_index_parity, check_rows, check_xp, host, oracle_index,
+                            random_case, rel_frob, row_experts, run_gpu, sample_rows, tile_rows,
+                            to_f64, workload_case)
 
 pytestmark = pytest.mark.gpu
 
@@ -204,6 +205,72 @@ def test_ffn_arbitrary_block_table(name, kw, drop):
     assert not to_f64(g_act[~covered]).any() and not to_f64(g_yp[~covered]).any(), "untouched"
 
 
+@pytest.mark.parametrize("name,kw", [
+    ("lds_walk", dict(seed=1, T=600, H=128, E=12, K=3, I=192, P=4, block_m=32)),
+    ("global_walk", dict(seed=15, T=8192, H=64, E=64, K=8, I=64, P=8, block_m=16)),
+    ("float32", dict(seed=3, T=200, H=64, E=8, K=2, I=128, P=4, block_m=32,
+                     dtype=torch.float32)),
+])
+def test_ffn_checks_the_block_table(name, kw):
+    """A table with bad entries (expert outside [0, E_loc), rows outside [0, 256], a row range
+    outside [0, max_rows), n_blocks past max_blocks): the FFN skips exactly those entries and
+    reports their bits in the workspace's error word; every intact block is computed as the
+    oracle computes it and no other row is written.  A negative n_blocks computes nothing."""
+    _announce(f"ffn on a table with bad entries: {name}")
+    c = random_case(**kw)
+    layer = run_gpu(c)
+    assert layer.ffn_error() == 0
+    ref = oracle_index(c)
+    nb = int(layer.n_blocks.item())
+    tab = host(layer.blocks[:nb]).copy()
+    max_rows, E_loc = layer.max_rows, c.n_local
+    bad = {1: (1, E_loc + 3), 3: (1, -1), 5: (3, 300), 7: (3, -4), 9: (2, max_rows - 3),
+           11: (2, -64)}
+    assert nb > max(bad) + 2
+    for i, (field, v) in bad.items():
+        tab[i, field] = v
+    keep = np.array([i not in bad for i in range(nb)])
+    dev = layer.blocks.device
+    buf = torch.zeros_like(layer.blocks)  # entries past nb: (0, 0, 0, 0), 0 rows: skipped
+    buf[:nb] = torch.from_numpy(tab).to(dev)
+    n_over = torch.tensor([layer.max_blocks + 5], dtype=torch.int32, device=dev)
+    act = torch.zeros_like(layer.act)
+    yp = torch.zeros_like(layer.yp)
+    _, _, W1, W2 = layer._inputs
+    binding.moe_expert_ffn(layer.xp, W1, W2, buf, n_over, act, yp, layer.ffn_workspace)
+    torch.cuda.synchronize()
+    err = int(layer.ffn_workspace[binding.FFN_WS_ERR].item())
+    assert err == (binding.FFN_ERR_EXPERT | binding.FFN_ERR_ROWS | binding.FFN_ERR_RANGE |
+                   binding.FFN_ERR_COUNT), err
+    sub = np.ascontiguousarray(host(layer.blocks[:nb])[keep])
+    x = inputs.as_oracle_array(c.x)
+    _, _, _, xp = oracle.permute(ref.ids, ref.counts, c.E, c.begin, c.stride, c.n_local,
+                                 c.block_m, x)
+    act_o, yp_o = oracle.ffn_blocks(xp, inputs.as_oracle_array(c.W1),
+                                    inputs.as_oracle_array(c.W2), sub)
+    covered = np.zeros(xp.shape[0], bool)
+    for _, _, first, rows in sub:
+        covered[first:first + rows] = True
+    g_act, g_yp = host(act), host(yp)
+    n = len(covered)
+    e_act = rel_frob(to_f64(g_act[:n][covered]), to_f64(act_o[covered]))
+    e_yp = rel_frob(to_f64(g_yp[:n][covered]), to_f64(yp_o[covered]))
+    assert e_act <= c.tol and e_yp <= c.tol, (e_act, e_yp)
+    assert not to_f64(g_act[:n][~covered]).any() and not to_f64(g_yp[:n][~covered]).any()
+    assert not to_f64(g_act[n:]).any() and not to_f64(g_yp[n:]).any(), "rows past the segments"
+    # a negative block count: nothing computed, the count bit set
+    act.zero_()
+    n_neg = torch.tensor([-3], dtype=torch.int32, device=dev)
+    binding.moe_expert_ffn(layer.xp, W1, W2, layer.blocks, n_neg, act, yp, layer.ffn_workspace)
+    torch.cuda.synchronize()
+    assert int(layer.ffn_workspace[binding.FFN_WS_ERR].item()) == binding.FFN_ERR_COUNT
+    assert torch.count_nonzero(act) == 0
+    # and the plan's own table again: error word back to 0
+    binding.moe_expert_ffn(layer.xp, W1, W2, layer.blocks, layer.n_blocks, act, yp,
+                           layer.ffn_workspace)
+    assert layer.ffn_error() == 0
+
+
 # ------------------------------------------------- gather-on-load expert FFN ---
 
 GATHER_CASES = [
@@ -252,14 +319,6 @@ def test_gather_small_layers(name, kw):
     assert e_act <= c.tol and e_out <= c.tol, (e_act, e_out)
 
 
-def test_gather_full_size_olmoe():
-    """Full OLMoE-shaped layer: gather path bit-identical to the materialising path."""
-    _announce("gather full olmoe_shaped s=1.2")
-    c = workload_case("olmoe_shaped", 1.2, weights=_weights("olmoe_shaped"))
-    _gather_vs_materialised(c)
-    torch.cuda.empty_cache()
-
-
 # ------------------------------------------------------ full-size layers: sampled ---
 
 FULL = [(n, s) for n in ("olmoe_shaped", "qwen3_30b_a3b_shaped", "gpt_oss_120b_shaped",
@@ -281,14 +340,28 @@ def _weights(name):
 
 @pytest.mark.parametrize("name,skew", FULL)
 def test_full_size_sampled(name, skew):
-    """At the full layer size: index outputs bit-exact on every entry; act / yp on sampled
-    rows and out on sampled tokens against the oracle, which computes those one by one."""
+    """At the full layer size, on both FFN input paths: index outputs bit-exact on every
+    entry; the benchmarked gather-on-load path bit-identical to the materialising path on
+    every valid row of act and yp and on every token of out; and the gather path's act / yp on
+    sampled rows (one per 32-row block of every 128-row piece of every expert, block edges,
+    random rows, and every row behind the sampled tokens) and out on sampled tokens against
+    the oracle, which computes those one by one, with per-row and per-element bounds beside
+    the layer-wide relative Frobenius bar."""
     _announce(f"full {name} skew={skew}")
     c = workload_case(name, skew, weights=_weights(name))
-    layer = run_gpu(c)
+    mat = run_gpu(c)
     ref = oracle_index(c)
+    check_index_parity(mat, ref)
+    check_xp(mat, c, ref)
+    layer = run_gpu(c, gather=True)
     check_index_parity(layer, ref)
-    check_xp(layer, c, ref)
+    rows_pad = int(ref.offsets[-1])
+    valid = torch.nonzero(mat.row_token[:rows_pad] >= 0).squeeze(1)
+    for nm in ("act", "yp"):
+        assert torch.equal(getattr(layer, nm)[valid], getattr(mat, nm)[valid]), ("gather vs xp", nm)
+    assert torch.equal(layer.out, mat.out), ("gather vs xp", "out")
+    del mat
+    torch.cuda.empty_cache()
 
     # sampled tokens (with at least one local entry) + sampled rows
     rng = np.random.default_rng(1)
@@ -296,25 +369,48 @@ def test_full_size_sampled(name, skew):
     has_local = np.nonzero((ep >= 0).any(1))[0]
     toks = np.sort(rng.choice(has_local, size=min(16, len(has_local)), replace=False))
     tok_rows = ep[toks][ep[toks] >= 0]
-    rows = np.unique(np.concatenate([sample_rows(ref, 48), tok_rows]))
+    rows = np.unique(np.concatenate([tile_rows(ref), sample_rows(ref, 48), tok_rows]))
     ex = row_experts(ref.blocks, rows)
     x_rows = inputs.as_oracle_array(c.x)[ref.row_token[rows]]
     act, yp = oracle.ffn_rows(x_rows, inputs.as_oracle_array(c.W1), inputs.as_oracle_array(c.W2),
                               np.arange(len(rows), dtype=np.int32), ex.astype(np.int32))
     rows_t = torch.from_numpy(rows).to(layer.act.device)
-    e_act = rel_frob(to_f64(host(layer.act[rows_t])), to_f64(act))
-    e_yp = rel_frob(to_f64(host(layer.yp[rows_t])), to_f64(yp))
+    g_act, g_yp = to_f64(host(layer.act[rows_t])), to_f64(host(layer.yp[rows_t]))
+    e_act = rel_frob(g_act, to_f64(act))
+    e_yp = rel_frob(g_yp, to_f64(yp))
+    s_act = check_rows(g_act, to_f64(act), "act")
+    # yp: FC2's input rows (act) may already differ by a rounding flip; propagate that exactly
+    d_act = np.abs(g_act - to_f64(act))
+    prop_yp = np.zeros_like(g_yp)
+    for l in np.unique(ex):
+        m = ex == l
+        if d_act[m].any():
+            prop_yp[m] = d_act[m] @ np.abs(c.W2[int(l)].double().numpy()).T
+    s_yp = check_rows(g_yp, to_f64(yp), "yp", extra=prop_yp)
     # end to end on the sampled tokens: oracle combine over the oracle's yp rows
     remap = {int(r): j for j, r in enumerate(rows)}
     ep_t = np.array([[remap[int(p)] if p >= 0 else -1 for p in ep[t]] for t in toks], np.int32)
     out_ref = oracle.combine(yp, ref.w[toks], ep_t, len(toks), c.K)
     toks_t = torch.from_numpy(toks).to(layer.out.device)
-    e_out = rel_frob(to_f64(host(layer.out[toks_t])), to_f64(out_ref))
+    g_out = to_f64(host(layer.out[toks_t]))
+    e_out = rel_frob(g_out, to_f64(out_ref))
+    # out: the combine's inputs (yp rows) may differ by what the check above allowed
+    d_yp = np.abs(g_yp - to_f64(yp))
+    prop_out = np.zeros_like(g_out)
+    for j, t in enumerate(toks):
+        for k in range(c.K):
+            if ep_t[j, k] >= 0:
+                prop_out[j] += abs(float(ref.w[t, k])) * d_yp[ep_t[j, k]]
+    s_out = check_rows(g_out, to_f64(out_ref), "out (oracle chain)", extra=prop_out)
+    # the combine alone, element by element: the oracle's combine over the GPU's own yp rows
+    out_own = oracle.combine(host(layer.yp[rows_t]), ref.w[toks], ep_t, len(toks), c.K)
+    check_rows(g_out, to_f64(out_own), "out (combine of the GPU's yp)", rms_frac=1e-4)
     # tokens with no local entry are exactly zero
     none_local = np.nonzero(~(ep >= 0).any(1))[0][:64]
     if len(none_local):
         assert torch.count_nonzero(layer.out[torch.from_numpy(none_local).to(layer.out.device)]) == 0
-    print(f"rows={len(rows)} tokens={len(toks)} act={e_act:.2e} yp={e_yp:.2e} out={e_out:.2e}")
+    print(f"rows={len(rows)} tokens={len(toks)} act={e_act:.2e} yp={e_yp:.2e} out={e_out:.2e} "
+          f"row/elem act={s_act} yp={s_yp} out={s_out}")
     assert e_act <= c.tol and e_yp <= c.tol and e_out <= c.tol
     del layer
     torch.cuda.empty_cache()
