@@ -317,6 +317,21 @@ moe_status_t moe_expert_ffn_gather(const void* x, const int32_t* row_token, int 
                                    int max_blocks, void* act, void* yp, int64_t max_rows,
                                    int32_t* workspace, int64_t workspace_elems,
                                    hipStream_t stream);
+/* moe_expert_ffn_gather for callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): no workspace argument; the FFN's scratch is
+ * a static device array inside the library (one per GPU, held until the process ends, about
+ * 1 MB), whose address is looked up once per device.  Same arguments, results and checks as
+ * moe_expert_ffn_gather otherwise; allocates and frees nothing.  max_blocks above
+ * MOE_FFN_NOALLOC_MAX_BLOCKS returns MOE_ERR_UNSUPPORTED.  All calls on one GPU share the
+ * array: calls that overlap on one GPU (other streams, other host threads) race and must not
+ * be made; calls in sequence on one stream are fine (each rewrites what it needs).  The
+ * table's error word is that array's word MOE_FFN_WS_ERR, not visible to the caller. */
+#define MOE_FFN_NOALLOC_MAX_BLOCKS 16384
+moe_status_t moe_expert_ffn_gather_noalloc(const void* x, const int32_t* row_token, int T,
+                                           const void* w1, const void* w2, moe_dtype_t dt,
+                                           int H, int I, int E_loc, const int32_t* blocks,
+                                           const int32_t* n_blocks, int max_blocks, void* act,
+                                           void* yp, int64_t max_rows, hipStream_t stream);
 /* FC1 half of moe_expert_ffn_gather (FC2 is moe_expert_ffn_fc2, unchanged). */
 moe_status_t moe_expert_ffn_fc1_gather(const void* x, const int32_t* row_token, int T,
                                        const void* w1, moe_dtype_t dt, int H, int I, int E_loc,

@@ -46,6 +46,8 @@ _SIGNATURES = {
                                   _vp, _i64, _vp]),
     "moe_expert_ffn_gather": (_i32, [_vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp,
                                      _vp, _i32, _vp, _vp, _i64, _vp, _i64, _vp]),
+    "moe_expert_ffn_gather_noalloc": (_i32, [_vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
+                                             _vp, _vp, _i32, _vp, _vp, _i64, _vp]),
     "moe_expert_ffn_fc1_gather": (_i32, [_vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp, _vp,
                                          _i32, _vp, _i64, _vp, _i64, _vp]),
     "moe_expert_ffn_tile_schedule": (_i32, [_vp, _vp, _i32, _i32, _i64, _vp, _i64, _vp]),
@@ -257,6 +259,32 @@ def moe_expert_ffn_tile_schedule(blocks, n_blocks, E_loc, max_rows, workspace, s
 # workspace word holding the FFN's table error bits (MOE_FFN_WS_ERR and MOE_FFN_ERR_* in moe.h)
 FFN_WS_ERR = 1
 FFN_ERR_EXPERT, FFN_ERR_ROWS, FFN_ERR_RANGE, FFN_ERR_COUNT = 1, 2, 4, 8
+
+
+# largest block table moe_expert_ffn_gather_noalloc takes (MOE_FFN_NOALLOC_MAX_BLOCKS in moe.h)
+FFN_NOALLOC_MAX_BLOCKS = 16384
+
+
+def moe_expert_ffn_gather_noalloc(x, row_token, w1, w2, blocks, n_blocks, act, yp, stream=None):
+    """moe_expert_ffn_gather with the library's static per-GPU scratch instead of a workspace
+    (allocates nothing; calls that overlap on one GPU race)."""
+    T, H = x.shape
+    E_loc, two_I, _ = w1.shape
+    I = two_I // 2
+    rows = row_token.shape[0]
+    if w1.shape[2] != H or w2.shape != (E_loc, H, I) or act.shape[1] != I or yp.shape[1] != H:
+        raise MoeError("moe_expert_ffn_gather_noalloc: inconsistent shapes")
+    if act.shape[0] < rows or yp.shape[0] < rows:
+        raise MoeError("moe_expert_ffn_gather_noalloc: act/yp have fewer rows than row_token")
+    _check(lib().moe_expert_ffn_gather_noalloc(_ptr(x, x.dtype, "x"),
+                                               _ptr(row_token, torch.int32, "row_token"), T,
+                                               _ptr(w1, x.dtype, "w1"), _ptr(w2, x.dtype, "w2"),
+                                               _dt(x), H, I, E_loc,
+                                               _ptr(blocks, torch.int32, "blocks"),
+                                               _ptr(n_blocks, torch.int32, "n_blocks"),
+                                               blocks.shape[0], _ptr(act, x.dtype, "act"),
+                                               _ptr(yp, x.dtype, "yp"), rows, _stream(stream)),
+           "moe_expert_ffn_gather_noalloc")
 
 
 def moe_expert_ffn_gather(x, row_token, w1, w2, blocks, n_blocks, act, yp, workspace,
