@@ -227,6 +227,32 @@ def ffn_source_sha256(precision: str = "bf16") -> str:
     return h.hexdigest()
 
 
+def hbm_reference(torch, dev, mib=1024, reps=20):
+    """The box's practical HBM rates, measured live: a device-to-device copy of `mib` MiB
+    (bytes read + written per second) and a read-only pass over the same buffer (an int64
+    sum), each the median of `reps` event-timed launches."""
+    n = mib << 20
+    a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    out = {}
+    for name, fn, bytes_ in (("copy", lambda: b.copy_(a), 2 * n),
+                             ("read", lambda: a.view(torch.int64).sum(), n)):
+        for _ in range(3):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for e0, e1 in ev:
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        t = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e-3
+        out[name + "_gbs"] = round(bytes_ / t / 1e9, 1)
+    del a, b
+    torch.cuda.empty_cache()
+    return out
+
+
 def plan_comparison(layer, w, steps, torch):
     """Both planners on the layer's current expert counts: plan kernel time (HIP events over
     back-to-back calls), blocks in the table, the busiest rank's blocks and rows, partial
@@ -521,6 +547,12 @@ def main():
         torch.cuda.empty_cache()
     if w.n_local // w.P <= 64 and w.n_local * w.P <= 4096:
         line["plan_comparison"] = plan_comparison(layer, w, max(20, args.steps // 4), torch)
+    # the practical HBM rates of this machine (after the timed steps), beside the 8 TB/s spec
+    ref = hbm_reference(torch, dev)
+    line["hbm_measured"] = {**ref, "what": "1 GiB device copy (read + written bytes) and a 1 GiB "
+                                           "read-only sum, median of 20 event-timed launches"}
+    line["combine_frac_of_measured_copy"] = round(combine_bytes / (per["combine"] * 1e-6) / 1e9
+                                                  / ref["copy_gbs"], 4)
     if not args.no_all_skews:
         by = []
         for sk in w.skews:
