@@ -89,6 +89,13 @@ def test_tiny_f32_full():
     ("three_pass", dict(seed=17, T=16385, H=64, E=256, K=4, I=64, P=8, block_m=16)),
     # the two-pass form with the largest top-k (16 entries per token in one place pass)
     ("two_pass_k16", dict(seed=18, T=16384, H=64, E=64, K=16, I=64, P=8, block_m=16)),
+    # decode-sized layers (a handful of rows per expert): experts of 1..32 rows, of 33..64
+    # rows, exactly 64 rows (4 experts taking every token), 65 rows, and wider H and I
+    ("decode_small", dict(seed=19, T=64, H=256, E=32, K=4, I=192, P=4, block_m=16)),
+    ("decode_two_blocks", dict(seed=20, T=64, H=128, E=6, K=4, I=128, P=2, block_m=32)),
+    ("decode_64_rows", dict(seed=21, T=64, H=128, E=4, K=4, I=64, P=2, block_m=64)),
+    ("decode_65_rows", dict(seed=22, T=65, H=128, E=4, K=4, I=64, P=2, block_m=64)),
+    ("decode_wide", dict(seed=23, T=16, H=320, E=16, K=4, I=448, P=4, block_m=16)),
 ])
 def test_small_layers_full(name, kw):
     c = random_case(**kw)
@@ -167,6 +174,9 @@ def test_graph_replay_matches_eager():
 @pytest.mark.parametrize("name,kw,drop", [
     # every other block: each expert's blocks no longer cover one row range (table in LDS)
     ("every_other", dict(seed=1, T=600, H=128, E=12, K=3, I=192, P=4, block_m=32), 2),
+    # a decode-sized layer (experts of about 48 rows in 16-row blocks) with every third block
+    # left out: experts of two row runs, paired into tiles of two halves
+    ("decode_runs", dict(seed=24, T=64, H=128, E=4, K=3, I=128, P=2, block_m=16), 3),
     # a quarter of 4130 blocks dropped: 3098 blocks, walked in global memory
     ("many_blocks", dict(seed=15, T=8192, H=64, E=64, K=8, I=64, P=8, block_m=16), 4),
 ])
