@@ -460,6 +460,9 @@ def main():
                   if args.materialize else
                   "ffn_bf16_kernel<true, true>, the FC1 GEMM of moe_expert_ffn_fc1_gather (gate/up + SwiGLU, "
                   "rows gathered from x)")
+    if dt == torch.float32:
+        fc1_kernel = ("ffn_f32_kernel<true>, the FC1 of moe_expert_ffn_fc1_gather on the float32 layer "
+                      "(gate/up + SwiGLU, fp32 FMAs, rows gathered from x)")
     peak_mfma = PEAK_BF16_TFLOPS
     if mx:
         fc1_kernel = ("ffn_mx_kernel<true>, the FC1 GEMM of moe_expert_ffn_mx_fc1 (MXFP4 gate/up "
@@ -506,7 +509,7 @@ def main():
                    "K": w.K, "I": w.I, "P": w.P, "block_m": w.beta,
                    "skew": w.skew_label(skew), "local_entries": N, "blocks": nb,
                    "maxvio": round(maxvio, 3), "planner": args.planner,
-                   "precision": args.precision,
+                   "precision": "f32" if dt == torch.float32 else args.precision,
                    "parallelism": "single GPU",
                    "launch": "hip graph replay" if args.graph else "eager",
                    "dispatch": "materialised xp" if args.materialize else

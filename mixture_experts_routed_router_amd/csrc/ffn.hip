@@ -43,7 +43,6 @@ constexpr int kWaves = 8;    // two waves per SIMD
 constexpr int kThreads = kWaves * MOE_WAVE;
 constexpr int ROW_BYTES = BK * 2;           // 128
 constexpr int SEG_ROWS = 1024 / ROW_BYTES;  // 8 rows per 1 KB copy
-constexpr int B_REGION = BN * ROW_BYTES;    // 32 KB of B rows per stage
 
 // An item stages kRowsA rows of A per K slice: 256 (two 128-row halves, a 2-deep ring of
 // 64 KB stages), 128 or 64 (one half of at most that many rows, a 3-deep ring of 48 or 40 KB
@@ -53,9 +52,10 @@ template <int kRowsA>
 struct Mode {
     static constexpr int kStages = kRowsA == 256 ? 2 : 3;
     static constexpr int kARegion = kRowsA * ROW_BYTES;
-    static constexpr int kStageBytes = kARegion + B_REGION;
+    static constexpr int kStageBytes = kARegion + BN * ROW_BYTES;
     static constexpr int kACopies = kRowsA / 64;  // 1 KB A copies per wave per stage
-    static constexpr int kCopies = kACopies + 4;  // + 4 B copies
+    static constexpr int kBCopies = BN / 64;      // 1 KB B copies per wave per stage
+    static constexpr int kCopies = kACopies + kBCopies;
     static constexpr int kRowBlocks = kRowsA / 64;  // 32-row MFMA blocks per wave
 };
 constexpr int SMEM_BYTES = Mode<128>::kStages * Mode<128>::kStageBytes;  // 144 KB
@@ -74,10 +74,11 @@ static_assert(Mode<64>::kStages * Mode<64>::kStageBytes <= SMEM_BYTES, "ring siz
 // segment bases are multiples of 256 bytes).
 template <int kRowsA>
 __device__ __forceinline__ uint32_t stage_row_offset(int row, bool b_side) {
+    using M = Mode<kRowsA>;
     const int g = row >> 3;  // segment of the row on its side
     const uint32_t in_seg = (uint32_t)(row & 7) * ROW_BYTES;
-    if (b_side) return (uint32_t)(Mode<kRowsA>::kARegion + (g & 7) * 4096 + (g >> 3) * 1024) + in_seg;
-    return (uint32_t)((g & 7) * (Mode<kRowsA>::kACopies * 1024) + (g >> 3) * 1024) + in_seg;
+    if (b_side) return (uint32_t)(M::kARegion + (g & 7) * (M::kBCopies * 1024) + (g >> 3) * 1024) + in_seg;
+    return (uint32_t)((g & 7) * (M::kACopies * 1024) + (g >> 3) * 1024) + in_seg;
 }
 
 template <int kRowsA>
@@ -386,7 +387,13 @@ struct GemmArgs {
     int b_rows;
     uint16_t* C;             // [rows, ldc]
     int ldc, n_cols, I, NT;
-    const int32_t* tiles;    // the schedule's tile records
+    // the schedule's tile records, read with scalar loads: the schedule kernel wrote them
+    // before this launch, and a scalar load is tracked by lgkmcnt, so waiting for it never
+    // waits for the slice copies in flight (a vector load's wait would: the copies are
+    // invisible to the compiler's vmcnt bookkeeping, which then waits for vmcnt(0))
+    const __attribute__((address_space(4))) int32_t* tiles;
+    int32_t* gidx;           // LDS: the gathered token rows of the item being decoded
+    uint32_t gidx_lds;       // its LDS byte address
     int32_t* ctr;            // this GEMM's per-XCD item counters
     int total, per_xcd_items, xcd;
     const int32_t* gather;   // row_token (gather-on-load) or nullptr
@@ -460,29 +467,43 @@ __device__ __forceinline__ void decode_step(int s, Item& n, const GemmArgs& g, Q
                                             int* item_s, int tid, int wave, int seg_row,
                                             int seg_lchunk) {
     switch (s) {
+        // The counter increment is the kernel's only vector-memory read the compiler sees (the
+        // slice copies are inline asm, invisible to its bookkeeping).  Every lane of wave 0 takes
+        // its result in step 1, so that the compiler's wait for it sits on every path that
+        // issued it: a wait left pending on some path would make the compiler drain all copies
+        // in flight (vmcnt(0)) before later writes to that register, e.g. every MFMA.
         case 0:
-            if (tid == 0 && qs.q < kXcds) qs.raw = atomicAdd(&g.ctr[(g.xcd + qs.q) % kXcds], 1);
+            if (wave == 0) {
+                if (tid == 0 && qs.q < kXcds) qs.raw = atomicAdd(&g.ctr[(g.xcd + qs.q) % kXcds], 1);
+            }
             break;
         case 1:
-            if (tid == 0) {
-                int got = -1;
-                while (qs.q < kXcds) {
-                    const int x = (g.xcd + qs.q) % kXcds;
-                    const int it = x * g.per_xcd_items + qs.raw;
-                    if (qs.raw < g.per_xcd_items && it < g.total) {
-                        got = it;
-                        break;
+            if (wave == 0) {
+                qs.raw = __builtin_amdgcn_readfirstlane(qs.raw);
+                if (tid == 0) {
+                    int got = -1;
+                    while (qs.q < kXcds) {
+                        const int x = (g.xcd + qs.q) % kXcds;
+                        const int it = x * g.per_xcd_items + qs.raw;
+                        if (qs.raw < g.per_xcd_items && it < g.total) {
+                            got = it;
+                            break;
+                        }
+                        if (++qs.q < kXcds) qs.raw = atomicAdd(&g.ctr[(g.xcd + qs.q) % kXcds], 1);
                     }
-                    if (++qs.q < kXcds) qs.raw = atomicAdd(&g.ctr[(g.xcd + qs.q) % kXcds], 1);
+                    asm volatile("" ::"v"(qs.raw));  // the last increment is taken on every path
+                    *item_s = got;
                 }
-                *item_s = got;
             }
             break;
         case 2: {
             n.it = __builtin_amdgcn_readfirstlane(*item_s);
             n.rows_a = 0;
             if (n.it >= 0) {
-                const int32_t* tg = g.tiles + TILE_INTS * (n.it / g.NT);
+                // wave-uniform operands (readfirstlane) keep the address in scalar registers,
+                // so the record is read with scalar loads
+                const int it = __builtin_amdgcn_readfirstlane(n.it);
+                const auto tg = g.tiles + TILE_INTS * (it / g.NT);
                 n.ts = __builtin_amdgcn_readfirstlane(tg[5]);
                 n.cnt = __builtin_amdgcn_readfirstlane(tg[6]);
             }
@@ -492,14 +513,17 @@ __device__ __forceinline__ void decode_step(int s, Item& n, const GemmArgs& g, Q
             if (n.it >= 0) {
                 // item -> (tile, column tile): the expert's items [ts * NT, (ts + cnt) * NT) in
                 // groups of kGroupTiles tiles, column-tile-major inside a group
-                const int local = n.it - n.ts * g.NT;
+                const int it = __builtin_amdgcn_readfirstlane(n.it);
+                const int ts = __builtin_amdgcn_readfirstlane(n.ts);
+                const int cnt = __builtin_amdgcn_readfirstlane(n.cnt);
+                const int local = it - ts * g.NT;
                 const int grp = local / (kGroupTiles * g.NT);
                 const int r = local - grp * (kGroupTiles * g.NT);
-                const int rest = n.cnt - grp * kGroupTiles;
+                const int rest = cnt - grp * kGroupTiles;
                 const int ct = rest < kGroupTiles ? rest : kGroupTiles;
                 n.nt = r / ct;
-                const int t = n.ts + grp * kGroupTiles + (r - n.nt * ct);
-                const int32_t* tl = g.tiles + TILE_INTS * t;
+                const int t = ts + grp * kGroupTiles + (r - n.nt * ct);
+                const auto tl = g.tiles + TILE_INTS * t;
                 n.l = __builtin_amdgcn_readfirstlane(tl[0]);
                 n.h_row0[0] = __builtin_amdgcn_readfirstlane(tl[1]);
                 n.h_rows[0] = __builtin_amdgcn_readfirstlane(tl[2]);
@@ -511,6 +535,10 @@ __device__ __forceinline__ void decode_step(int s, Item& n, const GemmArgs& g, Q
             if (n.it >= 0) {
                 n.rows_a = rows_mode(n.h_rows[1], n.h_rows[0]);
                 if (kGather) {
+                    // the token row of each of this lane's A copies, copied straight into LDS
+                    // (lane l's word lands at gidx[(wave * 4 + q) * 64 + l]); the slice wait at
+                    // the next boundary covers the copy, as it was issued before that
+                    // boundary's newest slice copies
                     const int copies = n.rows_a / 64;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
@@ -519,7 +547,9 @@ __device__ __forceinline__ void decode_step(int s, Item& n, const GemmArgs& g, Q
                             int rr = ((q & 1) * 8 + wave) * SEG_ROWS + seg_row;
                             const int hr = h ? n.h_rows[1] : n.h_rows[0];
                             if (rr > hr - 1) rr = hr - 1;  // read, unused
-                            n.offa[q] = (uint32_t)g.gather[(h ? n.h_row0[1] : n.h_row0[0]) + rr];
+                            const int row = (h ? n.h_row0[1] : n.h_row0[0]) + rr;
+                            one_copy_dword(g.gidx_lds + (uint32_t)(wave * 4 + q) * (MOE_WAVE * 4), g.gather,
+                                           (uint32_t)row * 4u);
                         }
                     }
                 }
@@ -531,7 +561,7 @@ __device__ __forceinline__ void decode_step(int s, Item& n, const GemmArgs& g, Q
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     // row_token -1 (padding) or out of range: read row 0, never stored
-                    const int t = (int)n.offa[q];
+                    const int t = q < copies ? g.gidx[(wave * 4 + q) * MOE_WAVE + moe_lane_id()] : 0;
                     const int tok = q < copies && t >= 0 && t < g.a_rows ? t : 0;
                     n.offa[q] = (uint32_t)tok * (uint32_t)g.Kdim * 2u + seg_lchunk * 16u;
                 }
@@ -568,6 +598,15 @@ __device__ __forceinline__ uint32_t a_offset(const GemmArgs& g, const Item& it, 
     return (uint32_t)rr * (uint32_t)g.Kdim * 2u + lane_chunk;
 }
 
+// 64-row items (at most 64 valid rows, decode-sized experts): wave w stages A rows
+// 8w .. 8w + 7 only when some of them are valid.  Rows past the valid ones feed only MFMA
+// rows that are never stored, so their LDS rows may hold anything; a tile of a few rows then
+// stages 1 KB of A per slice instead of 8 KB, which a weight-streaming CU spends on weights.
+template <int kRowsA>
+__device__ __forceinline__ bool a_copy_needed(const Item& it, int wave) {
+    return kRowsA != 64 || wave * SEG_ROWS < it.h_rows[0];
+}
+
 template <bool kSwiGLU, bool kGather, int kRowsA>
 __device__ __forceinline__ void issue_slice(const GemmArgs& g, const Item& it, int kt,
                                             uint32_t smem_base, int wave, int seg_row,
@@ -587,7 +626,7 @@ __device__ __forceinline__ void issue_slice(const GemmArgs& g, const Item& it, i
         four_copies(ma, a0, a0 - 1024, a1 - 2048, a1 - 3072, oa[0], oa[1], oa[2], oa[3], true);
     } else if constexpr (kRowsA == 128) {
         four_copies(ma, a0, a0 - 1024, a0, a0, oa[0], oa[1], 0, 0, false);
-    } else {
+    } else if (a_copy_needed<kRowsA>(it, wave)) {
         one_copy(ma, a0, oa[0]);
     }
     four_copies(st + M::kARegion + wave * 4096, bx, bx - 1024, bx - 2048, bx - 3072,
@@ -601,10 +640,27 @@ template <bool kSwiGLU, bool kGather, int kRowsA>
 __device__ __forceinline__ void issue_prologue_m(const GemmArgs& g, const Item& it,
                                                  uint32_t smem_base, int wave, int seg_row,
                                                  uint32_t lane_chunk) {
+    constexpr int kStages = Mode<kRowsA>::kStages;
     const int nk = g.Kdim / BK;
-    const int pre = nk < Mode<kRowsA>::kStages ? nk : Mode<kRowsA>::kStages;
+    const int pre = nk < kStages ? nk : kStages;
     for (int s = 0; s < pre; ++s)
         issue_slice<kSwiGLU, kGather, kRowsA>(g, it, s, smem_base, wave, seg_row, lane_chunk);
+}
+
+// Wait until this wave's copies of all but the last `pending` issued slices have landed, then
+// meet the workgroup.  64-row items: a wave issues kCopies copies per slice, or one fewer
+// when it stages no A rows (a_copy_needed).
+template <int kRowsA>
+__device__ __forceinline__ void wait_slices(int pending, bool a_copy) {
+    using M = Mode<kRowsA>;
+    if constexpr (kRowsA == 64) {
+        if (a_copy)
+            wait_pending_stages<M::kCopies, M::kStages - 1>(pending);
+        else
+            wait_pending_stages<M::kCopies - 1, M::kStages - 1>(pending);
+    } else {
+        wait_copies_and_barrier(pending * M::kCopies);
+    }
 }
 
 // The first kStages slices of an item (the ring must be free).
@@ -667,7 +723,8 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& g, const Item& cur_in,
     };
 
     // slice 0 in LDS everywhere (stores of the previous item may still be counted: stricter)
-    wait_copies_and_barrier((pre - 1) * M::kCopies);
+    const bool a_copy = a_copy_needed<kRowsA>(cur, wave);
+    wait_slices<kRowsA>(pre - 1, a_copy);
     if (active) load_frags(0, 0, 0);
 
     int step = 0;
@@ -697,7 +754,7 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& g, const Item& cur_in,
                 // out before the next copies); slice kt's slot then takes slice kt+kStages;
                 // first fragments of slice kt+1
                 const int issued = kt + M::kStages - 1 < nk ? kt + M::kStages - 1 : nk - 1;
-                wait_copies_and_barrier((issued - (kt + 1)) * M::kCopies);
+                wait_slices<kRowsA>(issued - (kt + 1), a_copy);
                 if (kt >= first_step && step < kDecodeSteps)
                     decode_step<kSwiGLU, kGather>(step++, nxt, g, qs, item_s, tid, wave, seg_row, seg_lchunk);
                 if (kt + M::kStages < nk)
@@ -716,8 +773,12 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& g, const Item& cur_in,
         __syncthreads();
         step = 2;
     }
-    for (; step < kDecodeSteps; ++step)
+    for (; step < kDecodeSteps; ++step) {
+        // steps 4 and 5 back to back: the gathered rows must be in LDS first (only that copy
+        // is in flight here)
+        if (kGather && step == 5) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         decode_step<kSwiGLU, kGather>(step, nxt, g, qs, item_s, tid, wave, seg_row, seg_lchunk);
+    }
     issue_prologue<kSwiGLU, kGather>(g, nxt, smem_base, wave, seg_row, seg_lchunk * 16u);
 
     // epilogue: acc[i][j][4c + e] = C[tile row wrow + i*32 + lane%32][col + 8c + 4(lane/32) + e].
@@ -807,14 +868,17 @@ ffn_bf16_kernel(const uint16_t* __restrict__ A, int64_t a_rows, int Kdim,
                 int max_blocks, int32_t* __restrict__ ws, const int32_t* __restrict__ gather) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM_BYTES];
     __shared__ int item_s;
+    __shared__ __attribute__((aligned(256))) int32_t gidx[kWaves * 4 * MOE_WAVE];
 
     GemmArgs g;
     g.A = A; g.a_rows = a_rows; g.Kdim = Kdim;
     g.B = B; g.b_expert_stride = b_expert_stride; g.b_rows = b_rows;
     g.C = C; g.ldc = ldc; g.n_cols = n_cols; g.I = I; g.NT = NT;
-    g.tiles = ws + WS_HEAD + max_blocks;
+    g.tiles = (const __attribute__((address_space(4))) int32_t*)(ws + WS_HEAD + max_blocks);
+    g.gidx = gidx;
+    g.gidx_lds = (uint32_t)(uintptr_t)(lds_u8_t*)reinterpret_cast<uint8_t*>(gidx);
     g.ctr = ws + (kSwiGLU ? WS_CTR_FC1 : WS_CTR_FC2);
-    g.total = ws[WS_NTILES] * NT;
+    g.total = ws[WS_NTILES] * g.NT;
     g.per_xcd_items = (g.total + kXcds - 1) / kXcds;
     g.xcd = blockIdx.x % kXcds;
     g.gather = gather;
@@ -834,7 +898,10 @@ ffn_bf16_kernel(const uint16_t* __restrict__ A, int64_t a_rows, int Kdim,
     decode_step<kSwiGLU, kGather>(0, cur, g, qs, &item_s, tid, wave, seg_row, seg_lchunk);
     decode_step<kSwiGLU, kGather>(1, cur, g, qs, &item_s, tid, wave, seg_row, seg_lchunk);
     __syncthreads();
-    for (int s = 2; s < 6; ++s) decode_step<kSwiGLU, kGather>(s, cur, g, qs, &item_s, tid, wave, seg_row, seg_lchunk);
+    for (int s = 2; s < 6; ++s) {
+        if (kGather && s == 5) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        decode_step<kSwiGLU, kGather>(s, cur, g, qs, &item_s, tid, wave, seg_row, seg_lchunk);
+    }
     issue_prologue<kSwiGLU, kGather>(g, cur, smem_base, wave, seg_row, seg_lchunk * 16u);
 
     for (;;) {
