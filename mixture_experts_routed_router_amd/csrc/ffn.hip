@@ -410,11 +410,9 @@ struct Item {
     uint32_t offa[4];  // with gather (decode step 4 leaves the token rows here, step 5 the offsets)
 };
 
-// Thread 0's queue state: the queue being tried (own XCD first, then the others in turn) and
-// the value of its last counter increment.
+// Thread 0's queue state: the queue being tried (own XCD first, then the others in turn).
 struct Queue {
     int q;
-    int raw;
 };
 
 // Two floats -> packed bf16x2 (low half = a), nearest even (v_cvt_pk_bf16_f32).
@@ -423,6 +421,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     typedef float f32x2_t __attribute__((ext_vector_type(2)));
     const f32x2_t v = {a, b};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// v, in a form the compiler cannot see through: what is derived from it is computed where it
+// is used, instead of being hoisted to the kernel's start and kept live (or spilled) across the
+// item loop.  A spilled value's reload is a vector-memory read, and the compiler's wait for it
+// would also wait for the slice copies in flight.
+__device__ __forceinline__ int opaque(int v) {
+    asm volatile("" : "+v"(v));
+    return v;
 }
 
 __device__ __forceinline__ int rows_mode(int h_rows1, int h_rows0) {
@@ -468,36 +475,34 @@ __device__ __forceinline__ void decode_step(int s, Item& n, const GemmArgs& g, Q
                                             int seg_lchunk) {
     switch (s) {
         // The counter increment is the kernel's only vector-memory read the compiler sees (the
-        // slice copies are inline asm, invisible to its bookkeeping).  Every lane of wave 0 takes
-        // its result in step 1, so that the compiler's wait for it sits on every path that
-        // issued it: a wait left pending on some path would make the compiler drain all copies
-        // in flight (vmcnt(0)) before later writes to that register, e.g. every MFMA.
+        // slice copies are inline asm, invisible to its bookkeeping, so its wait for the
+        // increment is vmcnt(0)).  Its result goes to LDS at once, in wave 0: no register holds
+        // it across slice boundaries, where a pending read would make the compiler drain all
+        // copies in flight before later uses or writes of that register (e.g. every MFMA).
         case 0:
             if (wave == 0) {
-                if (tid == 0 && qs.q < kXcds) qs.raw = atomicAdd(&g.ctr[(g.xcd + qs.q) % kXcds], 1);
+                if (tid == 0 && qs.q < kXcds) item_s[1] = atomicAdd(&g.ctr[(g.xcd + qs.q) % kXcds], 1);
             }
             break;
         case 1:
-            if (wave == 0) {
-                qs.raw = __builtin_amdgcn_readfirstlane(qs.raw);
-                if (tid == 0) {
-                    int got = -1;
-                    while (qs.q < kXcds) {
-                        const int x = (g.xcd + qs.q) % kXcds;
-                        const int it = x * g.per_xcd_items + qs.raw;
-                        if (qs.raw < g.per_xcd_items && it < g.total) {
-                            got = it;
-                            break;
-                        }
-                        if (++qs.q < kXcds) qs.raw = atomicAdd(&g.ctr[(g.xcd + qs.q) % kXcds], 1);
+            if (tid == 0) {
+                int raw = item_s[1];
+                int got = -1;
+                while (qs.q < kXcds) {
+                    const int x = (g.xcd + qs.q) % kXcds;
+                    const int it = x * g.per_xcd_items + raw;
+                    if (raw < g.per_xcd_items && it < g.total) {
+                        got = it;
+                        break;
                     }
-                    asm volatile("" ::"v"(qs.raw));  // the last increment is taken on every path
-                    *item_s = got;
+                    if (++qs.q < kXcds) raw = atomicAdd(&g.ctr[(g.xcd + qs.q) % kXcds], 1);
                 }
+                asm volatile("" ::"v"(raw));  // the last increment is taken on every path
+                item_s[0] = got;
             }
             break;
         case 2: {
-            n.it = __builtin_amdgcn_readfirstlane(*item_s);
+            n.it = __builtin_amdgcn_readfirstlane(item_s[0]);
             n.rows_a = 0;
             if (n.it >= 0) {
                 // wave-uniform operands (readfirstlane) keep the address in scalar registers,
@@ -779,17 +784,18 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& g, const Item& cur_in,
         if (kGather && step == 5) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         decode_step<kSwiGLU, kGather>(step, nxt, g, qs, item_s, tid, wave, seg_row, seg_lchunk);
     }
-    issue_prologue<kSwiGLU, kGather>(g, nxt, smem_base, wave, seg_row, seg_lchunk * 16u);
+    issue_prologue<kSwiGLU, kGather>(g, nxt, smem_base, wave, opaque(seg_row), opaque(seg_lchunk) * 16u);
 
     // epilogue: acc[i][j][4c + e] = C[tile row wrow + i*32 + lane%32][col + 8c + 4(lane/32) + e].
     // Lanes l and l + 32 hold one row.  One v_permlane32_swap per pair of packed registers
     // (groups c and c + 2) leaves lane l with columns 0..15 and lane l + 32 with columns
     // 16..31 of each 32-column block, each as two 16-byte pieces in column order.
     if (active) {
-        const int hi16 = lane >= 32 ? 16 : 0;
+        const int le = opaque(lane);
+        const int hi16 = le >= 32 ? 16 : 0;
 #pragma unroll
         for (int i = 0; i < RB; ++i) {
-            const int tr = wrow + i * 32 + (lane & 31);
+            const int tr = wrow + i * 32 + (le & 31);
             const int rl = tr & (HALF - 1);
             // selects, not an indexed load: the item stays in registers
             const bool h1 = tr >= HALF;
@@ -867,7 +873,7 @@ ffn_bf16_kernel(const uint16_t* __restrict__ A, int64_t a_rows, int Kdim,
                 uint16_t* __restrict__ C, int ldc, int n_cols, int I, int NT,
                 int max_blocks, int32_t* __restrict__ ws, const int32_t* __restrict__ gather) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM_BYTES];
-    __shared__ int item_s;
+    __shared__ int item_s[2];  // [0] the next item, [1] thread 0's last counter increment
     __shared__ __attribute__((aligned(256))) int32_t gidx[kWaves * 4 * MOE_WAVE];
 
     GemmArgs g;
@@ -893,14 +899,14 @@ ffn_bf16_kernel(const uint16_t* __restrict__ A, int64_t a_rows, int Kdim,
     const int seg_row = lane >> 3;
     const int seg_lchunk = swz_chunk((wave & 1) * 8 + seg_row, lane & 7);
 
-    Queue qs{0, 0};
+    Queue qs{0};
     Item cur;
-    decode_step<kSwiGLU, kGather>(0, cur, g, qs, &item_s, tid, wave, seg_row, seg_lchunk);
-    decode_step<kSwiGLU, kGather>(1, cur, g, qs, &item_s, tid, wave, seg_row, seg_lchunk);
+    decode_step<kSwiGLU, kGather>(0, cur, g, qs, item_s, tid, wave, seg_row, seg_lchunk);
+    decode_step<kSwiGLU, kGather>(1, cur, g, qs, item_s, tid, wave, seg_row, seg_lchunk);
     __syncthreads();
     for (int s = 2; s < 6; ++s) {
         if (kGather && s == 5) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        decode_step<kSwiGLU, kGather>(s, cur, g, qs, &item_s, tid, wave, seg_row, seg_lchunk);
+        decode_step<kSwiGLU, kGather>(s, cur, g, qs, item_s, tid, wave, seg_row, seg_lchunk);
     }
     issue_prologue<kSwiGLU, kGather>(g, cur, smem_base, wave, seg_row, seg_lchunk * 16u);
 
@@ -909,13 +915,13 @@ ffn_bf16_kernel(const uint16_t* __restrict__ A, int64_t a_rows, int Kdim,
         if (rows_a == 0) break;
         Item nxt;
         if (rows_a == 256)
-            gemm_item<kSwiGLU, kGather, 256>(g, cur, nxt, qs, &item_s, smem, smem_base, tid, wave, lane,
+            gemm_item<kSwiGLU, kGather, 256>(g, cur, nxt, qs, item_s, smem, smem_base, tid, wave, lane,
                                     seg_row, seg_lchunk);
         else if (rows_a == 128)
-            gemm_item<kSwiGLU, kGather, 128>(g, cur, nxt, qs, &item_s, smem, smem_base, tid, wave, lane,
+            gemm_item<kSwiGLU, kGather, 128>(g, cur, nxt, qs, item_s, smem, smem_base, tid, wave, lane,
                                     seg_row, seg_lchunk);
         else
-            gemm_item<kSwiGLU, kGather, 64>(g, cur, nxt, qs, &item_s, smem, smem_base, tid, wave, lane,
+            gemm_item<kSwiGLU, kGather, 64>(g, cur, nxt, qs, item_s, smem, smem_base, tid, wave, lane,
                                    seg_row, seg_lchunk);
         cur = nxt;
     }
