@@ -612,33 +612,68 @@ __device__ __forceinline__ bool a_copy_needed(const Item& it, int wave) {
     return kRowsA != 64 || wave * SEG_ROWS < it.h_rows[0];
 }
 
+// issue_slice parts: the A rows' copies, and the B rows' first two and last two copies.
+constexpr int kPartA = 1, kPartB01 = 2, kPartB23 = 4, kPartB = kPartB01 | kPartB23;
+// Where the copies of the slice that a slice boundary makes room for go out: at the boundary
+// itself (-1), with the wait, or before the MFMAs of K step k (0..3) of the next slice.  Issued
+// all at the boundary, the 64 copies of the workgroup queue in the address unit (one 1 KB copy
+// every ~18 cycles) while every wave waits there for its turn, before its first MFMA of the
+// slice; spread into the K steps, a wave that waits on a copy leaves the MFMA pipe to the other
+// wave of its SIMD.  Measured per GEMM (lab copies in one process, all bit-identical):
+// FC1 B copies before step 1 (−1 to −3.5%), FC2 A copies before step 0 and B before step 1
+// (−3 to −7%), against all at the boundary.
+#ifndef FFN_DEFER_FC1
+#define FFN_DEFER_FC1 -1, 1, 1
+#endif
+#ifndef FFN_DEFER_FC2
+#define FFN_DEFER_FC2 0, 1, 1
+#endif
+struct Defer {
+    int a, b01, b23;  // the K step of the A copies, B copies 0-1, B copies 2-3
+};
+template <bool kSwiGLU>
+__device__ constexpr Defer defer_of() {
+    return kSwiGLU ? Defer{FFN_DEFER_FC1} : Defer{FFN_DEFER_FC2};
+}
+
 template <bool kSwiGLU, bool kGather, int kRowsA>
 __device__ __forceinline__ void issue_slice(const GemmArgs& g, const Item& it, int kt,
                                             uint32_t smem_base, int wave, int seg_row,
-                                            uint32_t lane_chunk) {
+                                            uint32_t lane_chunk, int parts = kPartA | kPartB) {
     using M = Mode<kRowsA>;
     const uint32_t st = smem_base + (kt % M::kStages) * M::kStageBytes;
     const uint32_t koff = (uint32_t)kt * (BK * 2);
     const uint32_t ma = st + wave * (M::kACopies * 1024);
     const uint8_t* a0 = base_a(g, it, 0);
     const uint8_t* bx = base_b(g, it);
-    uint32_t oa[4];
+    if (parts & kPartA) {
+        uint32_t oa[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-        oa[q] = (kGather ? it.offa[q] : a_offset(g, it, q, wave, seg_row, lane_chunk)) + koff;
-    if constexpr (kRowsA == 256) {
-        const uint8_t* a1 = base_a(g, it, 1);
-        four_copies(ma, a0, a0 - 1024, a1 - 2048, a1 - 3072, oa[0], oa[1], oa[2], oa[3], true);
-    } else if constexpr (kRowsA == 128) {
-        four_copies(ma, a0, a0 - 1024, a0, a0, oa[0], oa[1], 0, 0, false);
-    } else if (a_copy_needed<kRowsA>(it, wave)) {
-        one_copy(ma, a0, oa[0]);
+        for (int q = 0; q < 4; ++q)
+            oa[q] = (kGather ? it.offa[q] : a_offset(g, it, q, wave, seg_row, lane_chunk)) + koff;
+        if constexpr (kRowsA == 256) {
+            const uint8_t* a1 = base_a(g, it, 1);
+            four_copies(ma, a0, a0 - 1024, a1 - 2048, a1 - 3072, oa[0], oa[1], oa[2], oa[3], true);
+        } else if constexpr (kRowsA == 128) {
+            four_copies(ma, a0, a0 - 1024, a0, a0, oa[0], oa[1], 0, 0, false);
+        } else if (a_copy_needed<kRowsA>(it, wave)) {
+            one_copy(ma, a0, oa[0]);
+        }
     }
-    four_copies(st + M::kARegion + wave * 4096, bx, bx - 1024, bx - 2048, bx - 3072,
-                b_offset<kSwiGLU>(g, it.nt, 0, wave, seg_row, lane_chunk) + koff,
-                b_offset<kSwiGLU>(g, it.nt, 1, wave, seg_row, lane_chunk) + koff,
-                b_offset<kSwiGLU>(g, it.nt, 2, wave, seg_row, lane_chunk) + koff,
-                b_offset<kSwiGLU>(g, it.nt, 3, wave, seg_row, lane_chunk) + koff, true);
+    if ((parts & kPartB) == kPartB)
+        four_copies(st + M::kARegion + wave * 4096, bx, bx - 1024, bx - 2048, bx - 3072,
+                    b_offset<kSwiGLU>(g, it.nt, 0, wave, seg_row, lane_chunk) + koff,
+                    b_offset<kSwiGLU>(g, it.nt, 1, wave, seg_row, lane_chunk) + koff,
+                    b_offset<kSwiGLU>(g, it.nt, 2, wave, seg_row, lane_chunk) + koff,
+                    b_offset<kSwiGLU>(g, it.nt, 3, wave, seg_row, lane_chunk) + koff, true);
+    else if (parts & kPartB01)
+        four_copies(st + M::kARegion + wave * 4096, bx, bx - 1024, bx, bx,
+                    b_offset<kSwiGLU>(g, it.nt, 0, wave, seg_row, lane_chunk) + koff,
+                    b_offset<kSwiGLU>(g, it.nt, 1, wave, seg_row, lane_chunk) + koff, 0, 0, false);
+    else if (parts & kPartB23)
+        four_copies(st + M::kARegion + wave * 4096 + 2048, bx, bx - 1024, bx, bx,
+                    b_offset<kSwiGLU>(g, it.nt, 2, wave, seg_row, lane_chunk) + koff,
+                    b_offset<kSwiGLU>(g, it.nt, 3, wave, seg_row, lane_chunk) + koff, 0, 0, false);
 }
 
 template <bool kSwiGLU, bool kGather, int kRowsA>
@@ -733,10 +768,22 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& g, const Item& cur_in,
     if (active) load_frags(0, 0, 0);
 
     int step = 0;
+    constexpr Defer kDefer = defer_of<kSwiGLU>();
+    static_assert(kDefer.a < BK / 16 && kDefer.b01 < BK / 16 && kDefer.b23 < BK / 16,
+                  "copies go out within the next slice");
+    // the parts of a slice's copies that go out at step k of the next slice (k = -1: at the boundary)
+    auto parts_at = [&](int k) {
+        return (kDefer.a == k ? kPartA : 0) | (kDefer.b01 == k ? kPartB01 : 0) |
+               (kDefer.b23 == k ? kPartB23 : 0);
+    };
+    int deferred = -1;  // the slice whose deferred copies go out in this slice's K steps
     for (int kt = 0; kt < nk; ++kt) {
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
             const int cur_buf = kk & 1;
+            if (parts_at(kk) != 0 && deferred >= 0)
+                issue_slice<kSwiGLU, kGather, kRowsA>(g, cur, deferred, smem_base, wave, seg_row,
+                                                      seg_lchunk * 16u, parts_at(kk));
             if (active) {
                 if (kk + 1 < BK / 16) load_frags(kt, kk + 1, cur_buf ^ 1);
                 // FC1: the wave issuing MFMAs goes first while the other wave of its SIMD
@@ -762,9 +809,13 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& g, const Item& cur_in,
                 wait_slices<kRowsA>(issued - (kt + 1), a_copy);
                 if (kt >= first_step && step < kDecodeSteps)
                     decode_step<kSwiGLU, kGather>(step++, nxt, g, qs, item_s, tid, wave, seg_row, seg_lchunk);
-                if (kt + M::kStages < nk)
-                    issue_slice<kSwiGLU, kGather, kRowsA>(g, cur, kt + M::kStages, smem_base, wave, seg_row,
-                                                 seg_lchunk * 16u);
+                deferred = -1;
+                if (kt + M::kStages < nk) {
+                    if (parts_at(-1) != 0)
+                        issue_slice<kSwiGLU, kGather, kRowsA>(g, cur, kt + M::kStages, smem_base, wave,
+                                                              seg_row, seg_lchunk * 16u, parts_at(-1));
+                    if (parts_at(-1) != (kPartA | kPartB)) deferred = kt + M::kStages;
+                }
                 if (active) load_frags(kt + 1, 0, cur_buf ^ 1);
             }
         }

@@ -424,6 +424,14 @@ __device__ __forceinline__ void epilogue_fc2(const MxArgs& g, const MxItem& it,
 // slice s + 1, one decode step of the next item, the copies of slice s + 3 into slice s's
 // stage, and slice s + 1's first fragments); then the next item's first slices are issued
 // and this item's results leave from registers while they land.
+// The copies of the slice that a slice boundary makes room for go out after the next slice's
+// first MFMA step instead of at the boundary, where every wave would wait in the address unit's
+// queue before its first MFMA of the slice.
+#ifndef FFN_MX_DEFER
+#define FFN_MX_DEFER 0
+#endif
+constexpr bool kMxDeferCopies = FFN_MX_DEFER != 0;
+
 template <bool kFC1>
 __device__ __forceinline__ void mx_item(const MxArgs& g, const MxCtx& c, const MxItem& cur_in,
                                         MxItem& nxt, uint8_t* smem) {
@@ -451,10 +459,12 @@ __device__ __forceinline__ void mx_item(const MxArgs& g, const MxCtx& c, const M
     load_frags(f[0], smem, fh, tq, c.lane, 0);
 
     int step = 0;
+    int deferred = -1;  // the slice whose copies go out after this slice's first MFMA step
     for (int s = 0; s < nk; ++s) {
         const uint8_t* stage = smem + (s % kStages) * STAGE;
         const bool half = c.k_half && s == nk - 1;
         mfma_step(acc, f[0], sc, 0);
+        if (kMxDeferCopies && deferred >= 0) issue_slice(g, c, cur, deferred);
         if (!half) {
             load_frags(f[1], stage, fh, tq, c.lane, 1);
             mfma_step(acc, f[1], sc, 1);
@@ -465,7 +475,13 @@ __device__ __forceinline__ void mx_item(const MxArgs& g, const MxCtx& c, const M
             const int issued = s + kStages - 1 < nk ? s + kStages - 1 : nk - 1;
             wait_pending_stages<kCopies, kStages - 2>(issued - (s + 1));
             if (s >= first_step && step < kDecodeSteps) decode_step<kFC1>(step++, nxt, g, c);
-            if (s + kStages < nk) issue_slice(g, c, cur, s + kStages);
+            deferred = -1;
+            if (s + kStages < nk) {
+                if (kMxDeferCopies)
+                    deferred = s + kStages;
+                else
+                    issue_slice(g, c, cur, s + kStages);
+            }
             const uint8_t* nst = smem + ((s + 1) % kStages) * STAGE;
             load_scales(sc, nst, fh, tq, c.lane);
             load_frags(f[0], nst, fh, tq, c.lane, 0);
