@@ -641,6 +641,7 @@ __device__ __forceinline__ void issue_slice(const GemmArgs& g, const Item& it, i
                                             uint32_t smem_base, int wave, int seg_row,
                                             uint32_t lane_chunk, int parts = kPartA | kPartB) {
     using M = Mode<kRowsA>;
+    kt = __builtin_amdgcn_readfirstlane(kt);  // wave-uniform: M0 and the copy bases are scalars
     const uint32_t st = smem_base + (kt % M::kStages) * M::kStageBytes;
     const uint32_t koff = (uint32_t)kt * (BK * 2);
     const uint32_t ma = st + wave * (M::kACopies * 1024);
