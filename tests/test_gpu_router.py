@@ -140,6 +140,41 @@ def test_router_topk_full_size(name):
     assert int(host(counts).sum()) == wl.T * wl.K
 
 
+SCAN_FORMS = [
+    # T, E, K, k_ref, offset (floats the rows start past a 16-byte boundary)
+    (16400, 256, 8, 8, 0),     # 4 lanes per token, 16-byte chunks
+    (16400, 256, 8, 8, 1),     # rows not 16-byte aligned: float-by-float scan
+    (16400, 130, 8, 130, 0),   # E = 2 mod 4: float-by-float, plain softmax denominator
+    (3000, 64, 6, 64, 0),      # 16 lanes per token, chunks, plain softmax denominator
+    (3000, 61, 5, 7, 0),       # E odd, k_ref = K + 2
+    (2000, 128, 16, 16, 3),    # K = 16, rows 12 bytes off
+    (1, 256, 8, 8, 0),         # one token
+]
+
+
+@pytest.mark.parametrize("T,E,K,k_ref,offset", SCAN_FORMS)
+def test_route_ref_scan_forms(T, E, K, k_ref, offset):
+    """moe_route_ref reads a row in 16-byte chunks when E is a multiple of 4 and the rows are
+    16-byte aligned, else float by float: both forms against the oracle, with exact ties,
+    +0 / -0 pairs (equal logits) and subnormal logits planted in some rows."""
+    _announce(f"scan T={T} E={E} K={K} k_ref={k_ref} offset={offset}")
+    rng = np.random.default_rng(zlib.crc32(f"scan {T} {E} {offset}".encode()))
+    logits = rng.standard_normal((T, E), dtype=np.float32)
+    logits[::7, ::3] = 0.5                                    # ties at the top
+    logits[1::11, :] = 0.0
+    logits[1::11, 1::2] = -0.0                                # rows of +0 / -0 only
+    logits[2::13, : E // 2] = np.float32(1e-40)               # subnormals either sign
+    logits[2::13, E // 2:] = np.float32(-1e-40)
+    logits[3::17, E - 1] = 3e38                               # the last expert wins
+    buf = torch.full((T * E + offset,), float("nan"), dtype=torch.float32, device="cuda")
+    d_logits = buf[offset:].view(T, E)
+    d_logits.copy_(torch.from_numpy(logits))
+    ids, w, counts = _outputs(T, E, K)
+    binding.moe_route_ref(d_logits, K, k_ref, ids, w, counts)
+    torch.cuda.synchronize()
+    _check_topk(logits, ids, w, counts, K, k_ref)
+
+
 @pytest.mark.parametrize("name,skew", [("olmoe_shaped", 1.2), ("qwen3_30b_a3b_shaped", "hot4")])
 def test_route_ref_workload_logits(name, skew):
     """moe_route_ref on the workload's precomputed logits for k_ref = K, K + 1, 16 and E."""
