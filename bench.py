@@ -253,6 +253,29 @@ def hbm_reference(torch, dev, mib=1024, reps=20):
     return out
 
 
+def read_rate_at(torch, dev, nbytes, reps=20):
+    """The box's read rate for a working set of `nbytes` read again pass after pass, as the
+    weight-bound FFN re-reads its touched experts' weights every step: a read-only int64 sum over
+    a buffer of that size, median of `reps` event-timed launches after 3 warm-ups (GB/s).  The
+    rate depends on the size: sets that fit the last-level cache read faster than 8 TB/s allows
+    for HBM alone, sets of a few times its size slower than very large ones."""
+    n = max(1, int(nbytes) // 8)
+    a = torch.ones(n, dtype=torch.int64, device=dev)
+    for _ in range(3):
+        a.sum()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record()
+        a.sum()
+        e1.record()
+    torch.cuda.synchronize()
+    t = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e-3
+    del a
+    torch.cuda.empty_cache()
+    return n * 8 / t / 1e9
+
+
 def plan_comparison(layer, w, steps, torch):
     """Both planners on the layer's current expert counts: plan kernel time (HIP events over
     back-to-back calls), blocks in the table, the busiest rank's blocks and rows, partial
@@ -565,13 +588,20 @@ def main():
             f = 6.0 * w.H * w.I * n_
             ffn_t = (pr["fc1"] + pr["fc2"]) * 1e-6
             loc_ = cnt_[w.expert_begin::w.expert_stride][: w.n_local].tolist()
-            tr, tch, wb, _ = ffn_roofline(w, loc_, eb, peak_mfma)
-            by.append({"skew": w.skew_label(sk), "tokens_per_s": round(w.T / wl, 1),
-                       "ms_per_step": round(wl * 1e3, 4),
-                       "gemm_tflops": round(f / ffn_t / 1e12, 1),
-                       "ffn_frac_of_t_roof": round(tr / ffn_t, 4),
-                       "touched_experts": tch,
-                       "ffn_weight_gbs": round(wb / ffn_t / 1e9, 1)})
+            tr, tch, wb, bound_ = ffn_roofline(w, loc_, eb, peak_mfma)
+            entry = {"skew": w.skew_label(sk), "tokens_per_s": round(w.T / wl, 1),
+                     "ms_per_step": round(wl * 1e3, 4),
+                     "gemm_tflops": round(f / ffn_t / 1e12, 1),
+                     "ffn_frac_of_t_roof": round(tr / ffn_t, 4),
+                     "touched_experts": tch,
+                     "ffn_weight_gbs": round(wb / ffn_t / 1e9, 1)}
+            if bound_ == "hbm":
+                # the same weight stream against what this machine reads for a working set of
+                # that size (re-read pass after pass), beside the 8 TB/s of t_roof
+                rr = read_rate_at(torch, dev, wb)
+                entry["read_ref_gbs"] = round(rr, 1)
+                entry["ffn_frac_of_read_ref"] = round(wb / ffn_t / 1e9 / rr, 4)
+            by.append(entry)
         line["by_skew"] = by
     if not args.no_cpu_baseline:
         T_s = args.cpu_tokens or {"tiny_f32": 64, "olmoe_shaped": 256,
