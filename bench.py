@@ -253,6 +253,39 @@ def hbm_reference(torch, dev, mib=1024, reps=20):
     return out
 
 
+def gemm_reference(torch, dev, w, n_loc, reps=20):
+    """The vendor library's rate (torch.bmm, hipBLASLt) on a batched GEMM of the same
+    per-expert shape as the two expert GEMMs: one batch entry per touched expert with the
+    mean of their rows (FC1: [m, H] x [H, 2I]; FC2: [m, I] x [I, H]), bf16, operands
+    contiguous; median of `reps` event-timed launches after 3 warm-ups.  Neither fuses the
+    gather or the SwiGLU.  Returns TFLOP/s per GEMM."""
+    touched = [int(n) for n in n_loc if n > 0]
+    if not touched:
+        return {}
+    b, m = len(touched), max(1, round(sum(touched) / len(touched)))
+    out = {}
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    for name, k, n in (("fc1", w.H, 2 * w.I), ("fc2", w.I, w.H)):
+        a = torch.randn(b, m, k, device=dev, dtype=torch.bfloat16, generator=g)
+        bm = torch.randn(b, k, n, device=dev, dtype=torch.bfloat16, generator=g)
+        for _ in range(3):
+            torch.bmm(a, bm)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for e0, e1 in ev:
+            e0.record()
+            torch.bmm(a, bm)
+            e1.record()
+        torch.cuda.synchronize()
+        t = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e-3
+        out[name + "_tflops"] = round(2.0 * b * m * k * n / t / 1e12, 1)
+        del a, bm
+    out["shape"] = f"{b} x [{m} x K] x [K x N] (experts x mean rows)"
+    torch.cuda.empty_cache()
+    return out
+
+
 def read_rate_at(torch, dev, nbytes, reps=20):
     """The box's read rate for a working set of `nbytes` read again pass after pass, as the
     weight-bound FFN re-reads its touched experts' weights every step: a read-only int64 sum over
@@ -579,6 +612,14 @@ def main():
                                            "read-only sum, median of 20 event-timed launches"}
     line["combine_frac_of_measured_copy"] = round(combine_bytes / (per["combine"] * 1e-6) / 1e9
                                                   / ref["copy_gbs"], 4)
+    if bound == "mfma" and dt == torch.bfloat16 and not mx:
+        # the vendor library on the same per-expert shapes, beside the 2.5 PFLOP/s peak
+        gref = gemm_reference(torch, dev, w, loc.tolist())
+        fc2_s = per["fc2"] * 1e-6
+        gref["fc1_frac"] = round(achieved / gref["fc1_tflops"], 4)
+        gref["fc2_frac"] = round(2.0 * w.H * w.I * N / fc2_s / 1e12 / gref["fc2_tflops"], 4)
+        line["gemm_measured"] = {**gref, "what": "torch.bmm (hipBLASLt) bf16 on the same per-expert "
+                                                 "shapes; *_frac = this path's GEMM kernel rate over it"}
     if not args.no_all_skews:
         by = []
         for sk in w.skews:
