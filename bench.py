@@ -575,6 +575,10 @@ def main():
         "per_call_us": {k: round(v, 2) for k, v in per.items()},
         "permute_gbs": (round(permute_bytes / (per["permute"] * 1e-6) / 1e9, 1)
                         if args.materialize else None),
+        # gather-on-load: the permute is index work only (topk_ids read, entry_pos and row_token
+        # written); a few MB over three small kernels, so its rate is launch- and latency-bound
+        "permute_index_bytes": 4 * (2 * w.T * w.K + rows_pad),
+        "permute_index_gbs": round(4 * (2 * w.T * w.K + rows_pad) / (per["permute"] * 1e-6) / 1e9, 1),
         "combine_gbs": round(combine_bytes / (per["combine"] * 1e-6) / 1e9, 1),
         "ffn_t_roof_us": round(t_roof * 1e6, 2),
         "ffn_frac_of_t_roof": round(t_roof / ffn_s, 4),
