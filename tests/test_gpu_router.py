@@ -142,21 +142,28 @@ def test_router_topk_full_size(name):
 
 SCAN_FORMS = [
     # T, E, K, k_ref, offset (floats the rows start past a 16-byte boundary)
-    (16400, 256, 8, 8, 0),     # 4 lanes per token, 16-byte chunks
+    (16400, 256, 8, 8, 0),     # 4 lanes per token, staged slices
     (16400, 256, 8, 8, 1),     # rows not 16-byte aligned: float-by-float scan
-    (16400, 130, 8, 130, 0),   # E = 2 mod 4: float-by-float, plain softmax denominator
-    (3000, 64, 6, 64, 0),      # 16 lanes per token, chunks, plain softmax denominator
+    (16400, 130, 8, 130, 0),   # E not a power of two: float-by-float, plain softmax denominator
+    (3000, 64, 6, 64, 0),      # 16 lanes per token, staged, plain softmax denominator
     (3000, 61, 5, 7, 0),       # E odd, k_ref = K + 2
     (2000, 128, 16, 16, 3),    # K = 16, rows 12 bytes off
     (1, 256, 8, 8, 0),         # one token
+    # staged reads (4 lanes per token from T = 16369) across the slice counts of the scan:
+    (16400, 256, 4, 4, 0),     # KM 4: groups of 4, four slices
+    (16400, 256, 16, 16, 0),   # KM 16 over 64 experts per lane
+    (16400, 256, 8, 256, 0),   # plain softmax denominator from the staged values
+    (16400, 64, 8, 8, 0),      # 16 experts per lane: two slices
+    (16401, 128, 4, 4, 0),     # a last wave with one token
 ]
 
 
 @pytest.mark.parametrize("T,E,K,k_ref,offset", SCAN_FORMS)
 def test_route_ref_scan_forms(T, E, K, k_ref, offset):
-    """moe_route_ref reads a row in 16-byte chunks when E is a multiple of 4 and the rows are
-    16-byte aligned, else float by float: both forms against the oracle, with exact ties,
-    +0 / -0 pairs (equal logits) and subnormal logits planted in some rows."""
+    """moe_route_ref reads a wave's rows as staged 16-byte column slices when the rows fill the
+    lanes exactly (E a power of two) and the logits are 16-byte aligned, else each lane reads its
+    row float by float: both forms against the oracle, over the scan's group and slice layouts,
+    with exact ties, +0 / -0 pairs (equal logits) and subnormal logits planted in some rows."""
     _announce(f"scan T={T} E={E} K={K} k_ref={k_ref} offset={offset}")
     rng = np.random.default_rng(zlib.crc32(f"scan {T} {E} {offset}".encode()))
     logits = rng.standard_normal((T, E), dtype=np.float32)
