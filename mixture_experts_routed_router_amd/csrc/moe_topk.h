@@ -273,9 +273,6 @@ __device__ __forceinline__ void topk_token(const float* row, int t, bool valid, 
 // lane_expert<LPT, true>(q, j), that is 16-byte chunks q, q + LPT, ... of the row, and the row
 // is whole (E = LPT * NE).  scan_values<J0, J1> takes groups [J0, J1) of the lane's values into
 // list (J0 = 0 first); finish_values then merges the lanes and writes the token.
-template <int KM, int NE>
-constexpr int values_group() { return group_size<KM, NE>(); }
-
 template <int LPT, int NE, int KM, int J0, int J1>
 __device__ __forceinline__ void scan_values(const float (&v)[NE], bool valid, int q,
                                             double (&list)[KM]) {

@@ -9,7 +9,9 @@
 // bf16: one workgroup (4 waves) per tile of TM tokens against all E router rows, E <= 32 NB.
 // K (= H) is staged in 64-wide slices (128-byte rows) through an LDS ring of up to 8 stages
 // filled by gfx950 direct-to-LDS copies (a stage holds the TM token rows and the 32 NB router
-// rows); v_mfma_f32_32x32x16_bf16 accumulates the [TM, 32 NB] scores in float32.  The score
+// rows); v_mfma_f32_32x32x16_bf16 accumulates the [TM, 32 NB] scores in float32, each wave
+// taking all TM rows against a quarter of the 32-row router blocks (a k-step reads TM/32 + NB/4
+// fragments per wave, not 1 + TM NB / 128 as with one row block per wave).  The score
 // tile is then written to LDS (and to `logits` if asked) and each token's top-k is taken from
 // it by 256 / TM lanes.  float32: the same tile flow with scalar FMAs.  The histogram is kept
 // in LDS and flushed with one atomic per nonzero bin; at most 256 workgroups.
@@ -21,7 +23,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxBlocks = 256;
-constexpr int kRingBytes = 120 * 1024;
+constexpr int kRingBytes = 144 * 1024;
 
 template <int TM, int NB>
 struct Geom {
@@ -32,7 +34,7 @@ struct Geom {
     static constexpr int kStagesFit = kRingBytes / kStageBytes;
     static constexpr int kStages = kStagesFit < 8 ? kStagesFit : 8;
     static constexpr int kRB = TM / 32;                       // 32-row blocks
-    static constexpr int kTPW = (kRB * NB + 3) / 4;           // MFMA tiles per wave
+    static constexpr int kCBW = (NB + 3) / 4;                 // column blocks per wave
     static constexpr int kLPT = kThreads / TM;                // top-k lanes per token
     static constexpr int kNE = kRowsB / kLPT;                 // experts per top-k lane
     static constexpr int kLdS = kRowsB + 1;                   // score tile row stride (floats)
@@ -42,8 +44,7 @@ struct Geom {
                                                                      : kScoreBytes;
     static_assert(kSegs % 4 == 0, "whole copies per wave");
     static_assert(kStages >= 2, "ring depth");
-    static_assert(kSmem <= 136 * 1024, "LDS");
-    static_assert(4 % kRB == 0, "every tile of a wave shares its row block");
+    static_assert(kSmem <= 144 * 1024, "LDS");
 };
 
 // Stage layout: segment g (8 rows of 128 bytes) at g KB; segments 0 .. TM/8 - 1 hold token
@@ -103,22 +104,27 @@ router_bf16_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
                          off[q] + koff);
         };
 
-        f32x16_t acc[G::kTPW];
+        // wave w: every row block, column blocks w, w + 4, ...  Blocks past NB read router
+        // block 0 and are never stored; their MFMAs run anyway, since a branch around an MFMA
+        // makes the compiler move its accumulators between register files at every slice
+        f32x16_t acc[G::kRB][G::kCBW];
 #pragma unroll
-        for (int j = 0; j < G::kTPW; ++j)
+        for (int i = 0; i < G::kRB; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
-        // tiles i = wave + 4j: row block i % kRB (the same for every j), column block i / kRB
-        const int rb = wave % G::kRB;
-        bf16x8_t fa[2], fb[2][G::kTPW];
+            for (int c = 0; c < G::kCBW; ++c)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][c][r] = 0.f;
+        bf16x8_t fa[2][G::kRB], fb[2][G::kCBW];
         auto load_frags = [&](int kt, int kk, int buf) {
             const uint8_t* st = smem + (kt % G::kStages) * G::kStageBytes;
             const int ch = kk * 2 + (lane >> 5);
-            fa[buf] = stage_frag<TM>(st, rb * 32 + (lane & 31), false, ch);
 #pragma unroll
-            for (int j = 0; j < G::kTPW; ++j) {
-                const int cb = (wave + 4 * j) / G::kRB;
-                fb[buf][j] = stage_frag<TM>(st, (cb < NB ? cb : 0) * 32 + (lane & 31), true, ch);
+            for (int i = 0; i < G::kRB; ++i)
+                fa[buf][i] = stage_frag<TM>(st, i * 32 + (lane & 31), false, ch);
+#pragma unroll
+            for (int c = 0; c < G::kCBW; ++c) {
+                const int cb = wave + 4 * c;
+                fb[buf][c] = stage_frag<TM>(st, (cb < NB ? cb : 0) * 32 + (lane & 31), true, ch);
             }
         };
 
@@ -133,10 +139,11 @@ router_bf16_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
                 const int cur = kk & 1;
                 if (kk + 1 < 4) load_frags(kt, kk + 1, cur ^ 1);
 #pragma unroll
-                for (int j = 0; j < G::kTPW; ++j)
-                    if (wave + 4 * j < G::kRB * NB)
-                        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur], fb[cur][j],
-                                                                         acc[j], 0, 0, 0);
+                for (int c = 0; c < G::kCBW; ++c)
+#pragma unroll
+                    for (int i = 0; i < G::kRB; ++i)
+                        acc[i][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][c],
+                                                                            acc[i][c], 0, 0, 0);
                 if (kk == 3 && kt + 1 < nk) {
                     const int issued = kt + G::kStages - 1 < nk ? kt + G::kStages - 1 : nk - 1;
                     wait_pending_stages<G::kCPW, G::kStages - 1>(issued - (kt + 1));
@@ -146,20 +153,21 @@ router_bf16_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
             }
         }
 
-        // scores: acc[j][r] = S[row rb*32 + 8(r/4) + 4(lane/32) + r%4][col cb*32 + lane%32]
+        // scores: acc[i][c][r] = S[row 32 i + 8(r/4) + 4(lane/32) + r%4][col 32 (wave + 4c) + lane%32]
         __syncthreads();  // every wave is done with the ring
         float* sc = reinterpret_cast<float*>(smem);
 #pragma unroll
-        for (int j = 0; j < G::kTPW; ++j) {
-            if (wave + 4 * j >= G::kRB * NB) continue;
-            const int cb = (wave + 4 * j) / G::kRB;
-            const int col = cb * 32 + (lane & 31);
+        for (int c = 0; c < G::kCBW; ++c) {
+            if (wave + 4 * c >= NB) continue;
+            const int col = (wave + 4 * c) * 32 + (lane & 31);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = rb * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r & 3);
-                sc[row * G::kLdS + col] = acc[j][r];
-                if (logits && col < E && t0 + row < T) logits[(int64_t)(t0 + row) * E + col] = acc[j][r];
-            }
+            for (int i = 0; i < G::kRB; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r & 3);
+                    sc[row * G::kLdS + col] = acc[i][c][r];
+                    if (logits && col < E && t0 + row < T) logits[(int64_t)(t0 + row) * E + col] = acc[i][c][r];
+                }
         }
         __syncthreads();
         const int slot = tid / G::kLPT, q = tid % G::kLPT;
