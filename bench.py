@@ -64,6 +64,8 @@ def parse():
     ap.add_argument("--precision", choices=("bf16", "mx"), default="bf16",
                     help="bf16 expert GEMMs (the default) or the MX path: MXFP4 weights, MXFP8 "
                          "activations (x quantized inside the step)")
+    ap.add_argument("--no-router", action="store_true",
+                    help="skip timing moe_router_topk (router scores + top-k) beside the step")
     ap.add_argument("--no-mx-summary", action="store_true",
                     help="skip the MX path's summary (mx_path) in a bf16 run")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -307,6 +309,32 @@ def read_rate_at(torch, dev, nbytes, reps=20):
     del a
     torch.cuda.empty_cache()
     return n * 8 / t / 1e9
+
+
+def router_measured(torch, dev, w, x, binding, inputs, reps=200):
+    """moe_router_topk (router scores x . W_r^T with the top-k fused) on the batch's x and a
+    seeded router matrix, apart from the measured step (which starts from given logits): the
+    mean of `reps` back-to-back calls between two events, after as many warm-ups (a pair of
+    events around each call would add the launch gap to calls of a few microseconds).  Bytes: x
+    and W_r read once, the ids and weights written (T H b + E H b + 8 T K)."""
+    wr = inputs.make_router_weights(w).to(dev)
+    ids = torch.empty((w.T, w.K), dtype=torch.int32, device=dev)
+    tw = torch.empty((w.T, w.K), dtype=torch.float32, device=dev)
+    cnt = torch.empty((w.E,), dtype=torch.int32, device=dev)
+    for _ in range(reps):
+        binding.moe_router_topk(x, wr, w.K, w.K, ids, tw, cnt)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        binding.moe_router_topk(x, wr, w.K, w.K, ids, tw, cnt)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / reps
+    b = x.element_size()
+    nbytes = w.T * w.H * b + w.E * w.H * b + 8 * w.T * w.K
+    return {"us": round(t * 1e6, 2), "bytes": nbytes, "gbs": round(nbytes / t / 1e9, 1),
+            "frac_of_hbm_peak": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4),
+            "calls": reps}
 
 
 def plan_comparison(layer, w, steps, torch):
@@ -610,6 +638,10 @@ def main():
         torch.cuda.empty_cache()
     if w.n_local // w.P <= 64 and w.n_local * w.P <= 4096:
         line["plan_comparison"] = plan_comparison(layer, w, max(20, args.steps // 4), torch)
+    if not args.no_router:
+        line["router_topk"] = {**router_measured(torch, dev, w, x, binding, inputs),
+                               "what": "moe_router_topk (scores and top-k in one kernel) on the batch's x and "
+                                       "a seeded W_r, outside the measured step; mean of back-to-back calls"}
     # the practical HBM rates of this machine (after the timed steps), beside the 8 TB/s spec
     ref = hbm_reference(torch, dev)
     line["hbm_measured"] = {**ref, "what": "1 GiB device copy (read + written bytes) and a 1 GiB "
