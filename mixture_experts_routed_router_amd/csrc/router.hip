@@ -14,17 +14,17 @@
 // taking all TM rows against every W-th 32-row router block for W waves (with 4 waves a k-step
 // reads TM/32 + NB/4 fragments per wave, not 1 + TM NB / 128 as with one row block per wave).
 // At 128 tokens x 256 experts the staging bounds the kernel; 8 waves, two per SIMD, keep more
-// copies in flight than 4 and were 7.5% faster there.  The score
-// tile is then written to LDS (and to `logits` if asked) and each token's top-k is taken from
-// it by 256 / TM lanes.  float32: the same tile flow with scalar FMAs.  The histogram is kept
-// in LDS and flushed with one atomic per nonzero bin; at most 256 workgroups.
+// copies in flight than 4 and were 7.5% faster there.  The score tile is then written to LDS
+// (and to `logits` if asked) and each token's top-k is taken from it by 64 W / TM lanes.
+// float32: the same tile flow with scalar FMAs (256 threads).  The histogram is kept in LDS and
+// flushed with one atomic per nonzero bin; at most 256 workgroups.
 #include "moe_launch.h"
 #include "moe_lds.h"
 #include "moe_topk.h"
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kF32Threads = 256;  // the float32 kernel's workgroup
 constexpr int kMaxBlocks = 256;
 constexpr int kRingBytes = 144 * 1024;
 
@@ -188,7 +188,7 @@ router_bf16_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
 // float32 router: the same tile flow; the score tile [TM = 64, 32 NB] is accumulated from K
 // slices of 32 staged in LDS, thread (token row tid / 4, experts tid % 4 + 4 m).
 template <int NB, int KM>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kF32Threads)
 router_f32_kernel(const float* __restrict__ x, const float* __restrict__ wr, int T, int H, int E,
                   int K, int k_ref, float* __restrict__ logits, int32_t* __restrict__ topk_ids,
                   float* __restrict__ topk_w, int32_t* __restrict__ counts) {
@@ -198,7 +198,7 @@ router_f32_kernel(const float* __restrict__ x, const float* __restrict__ wr, int
     __shared__ float sc[TM * LDS_];
     __shared__ int hist[256];
     const int tid = threadIdx.x;
-    for (int e = tid; e < E; e += kThreads) hist[e] = 0;
+    for (int e = tid; e < E; e += kF32Threads) hist[e] = 0;
     const int ntiles = (T + TM - 1) / TM;
     const int r = tid / 4, eq = tid % 4;
     for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
@@ -208,11 +208,11 @@ router_f32_kernel(const float* __restrict__ x, const float* __restrict__ wr, int
         for (int m = 0; m < NPT; ++m) acc[m] = 0.f;
         for (int k0 = 0; k0 < H; k0 += TK) {
             __syncthreads();
-            for (int i = tid; i < TM * TK; i += kThreads) {
+            for (int i = tid; i < TM * TK; i += kF32Threads) {
                 const int rr = i / TK, kk = i % TK;
                 xs[rr][kk] = (t0 + rr < T && k0 + kk < H) ? x[(int64_t)(t0 + rr) * H + k0 + kk] : 0.f;
             }
-            for (int i = tid; i < RB * TK; i += kThreads) {
+            for (int i = tid; i < RB * TK; i += kF32Threads) {
                 const int e = i / TK, kk = i % TK;
                 ws[e][kk] = (e < E && k0 + kk < H) ? wr[(int64_t)e * H + k0 + kk] : 0.f;
             }
@@ -235,7 +235,7 @@ router_f32_kernel(const float* __restrict__ x, const float* __restrict__ wr, int
                                             topk_ids, topk_w, hist);
         __syncthreads();
     }
-    for (int e = tid; e < E; e += kThreads) {
+    for (int e = tid; e < E; e += kF32Threads) {
         const int c = hist[e];
         if (c) atomicAdd(&counts[e], c);
     }
@@ -286,13 +286,13 @@ hipError_t launch_f32(int km, const float* x, const float* wr, int T, int H, int
     const int tiles = (T + 63) / 64;
     const int grid = tiles < kMaxBlocks ? tiles : kMaxBlocks;
     if (km <= 4)
-        router_f32_kernel<NB, 4><<<grid, kThreads, 0, stream>>>(x, wr, T, H, E, K, k_ref, logits,
+        router_f32_kernel<NB, 4><<<grid, kF32Threads, 0, stream>>>(x, wr, T, H, E, K, k_ref, logits,
                                                                ids, w, counts);
     else if (km <= 8)
-        router_f32_kernel<NB, 8><<<grid, kThreads, 0, stream>>>(x, wr, T, H, E, K, k_ref, logits,
+        router_f32_kernel<NB, 8><<<grid, kF32Threads, 0, stream>>>(x, wr, T, H, E, K, k_ref, logits,
                                                                ids, w, counts);
     else
-        router_f32_kernel<NB, 16><<<grid, kThreads, 0, stream>>>(x, wr, T, H, E, K, k_ref, logits,
+        router_f32_kernel<NB, 16><<<grid, kF32Threads, 0, stream>>>(x, wr, T, H, E, K, k_ref, logits,
                                                                 ids, w, counts);
     return hipGetLastError();
 }
