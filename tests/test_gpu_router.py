@@ -122,7 +122,8 @@ def test_router_topk_tiny_f32_workload():
         _check_topk(g, ids, w, counts, wl.K, k_ref)
 
 
-@pytest.mark.parametrize("name", ["olmoe_shaped", "gpt_oss_120b_shaped", "deepseek_v3_share"])
+@pytest.mark.parametrize("name", ["olmoe_shaped", "qwen3_30b_a3b_shaped", "gpt_oss_120b_shaped",
+                                  "gpt_oss_120b_decode", "deepseek_v3_share"])
 def test_router_topk_full_size(name):
     """Full layer sizes: every score row for OLMoE's shape, 1024 sampled token rows for the
     larger ones; the top-k on every token."""
