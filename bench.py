@@ -68,6 +68,10 @@ def parse():
                     help="skip timing moe_router_topk (router scores + top-k) beside the step")
     ap.add_argument("--no-mx-summary", action="store_true",
                     help="skip the MX path's summary (mx_path) in a bf16 run")
+    ap.add_argument("--no-direct", action="store_true",
+                    help="down GEMM stores every row to yp and the combine sums every token "
+                         "(default: the rows of one-entry tokens go to out from the down GEMM's "
+                         "epilogue, moe_expert_ffn_fc2_direct + moe_combine_multi)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a reference for "
                          "hardware byte counters)")
@@ -497,10 +501,11 @@ def main():
         wmx = binding.mx_quantize_weights(W1, W2)  # MXFP4 weights, prepared once
     if mx:
         W1, W2 = wmx
+    direct = not (args.no_direct or mx)
     layer = binding.RoutedExperts(w.T, w.H, w.E, w.K, w.I, w.P, dtype=dt, E_loc=w.n_local,
                                   expert_begin=w.expert_begin, expert_stride=w.expert_stride,
                                   block_m=w.beta, gather=not args.materialize,
-                                  planner=args.planner, precision=args.precision)
+                                  planner=args.planner, precision=args.precision, direct=direct)
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
@@ -537,7 +542,12 @@ def main():
     rows_pad = int(layer.offsets[-1].item())
     eb = 2 if dt == torch.bfloat16 else 4
     permute_bytes = (w.T + N) * w.H * eb + 4 * (w.T * w.K + rows_pad)
+    # tokens with exactly one local entry: with direct rows the down GEMM stores their out rows
+    # and the combine neither reads their expert row nor writes their out row
+    n_one = int(((layer.entry_pos.view(w.T, w.K) >= 0).sum(dim=1) == 1).sum().item())
     combine_bytes = (N + w.T) * w.H * eb + 8 * w.T * w.K
+    if direct:
+        combine_bytes -= 2 * n_one * w.H * eb
     traffic = ffn_traffic(w.name, args.precision)
     t_roof, touched, wbytes, bound = ffn_roofline(w, loc.tolist(), eb)
     fc1_kernel = ("ffn_bf16_kernel<true, false>, the FC1 GEMM of moe_expert_ffn_fc1 (gate/up + SwiGLU)"
@@ -597,7 +607,11 @@ def main():
                    "parallelism": "single GPU",
                    "launch": "hip graph replay" if args.graph else "eager",
                    "dispatch": "materialised xp" if args.materialize else
-                               "gather-on-load (FC1 reads x rows through row_token)"},
+                               "gather-on-load (FC1 reads x rows through row_token)",
+                   "combine": ("direct rows: the down GEMM stores the weighted out rows of the "
+                               f"{n_one} one-entry tokens, the combine sums the other "
+                               f"{w.T - n_one}" if direct else
+                               "every token summed by the combine")},
         "gemm_tflops": round(flops_ffn / ffn_s / 1e12, 1),
         "gemm_frac_of_peak": round(flops_ffn / ffn_s / 1e12 / peak_mfma, 4),
         "per_call_us": {k: round(v, 2) for k, v in per.items()},
@@ -608,6 +622,7 @@ def main():
         "permute_index_bytes": 4 * (2 * w.T * w.K + rows_pad),
         "permute_index_gbs": round(4 * (2 * w.T * w.K + rows_pad) / (per["permute"] * 1e-6) / 1e9, 1),
         "combine_gbs": round(combine_bytes / (per["combine"] * 1e-6) / 1e9, 1),
+        "combine_bytes": combine_bytes,
         "ffn_t_roof_us": round(t_roof * 1e6, 2),
         "ffn_frac_of_t_roof": round(t_roof / ffn_s, 4),
         "touched_experts": touched,

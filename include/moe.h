@@ -11,7 +11,9 @@
  *                   moe_plan_blocks: the block-granular replica plan instead, same outputs
  *   moe_expert_ffn  SwiGLU expert FFN over the block table (grouped GEMMs on bf16 MFMA);
  *                   moe_expert_ffn_gather reads the token rows of x directly
- *   moe_combine     routing-weight combine of each token's expert outputs
+ *   moe_combine     routing-weight combine of each token's expert outputs;
+ *                   moe_expert_ffn_fc2_direct + moe_combine_multi: the same with the rows of
+ *                   one-entry tokens weighted and stored by the down GEMM itself
  *   moe_mx_quantize MXFP8 / MXFP4 quantization (the low-precision expert path's inputs)
  *   moe_expert_ffn_mx  the expert FFN with MXFP4 weights and MXFP8 activations (block-scaled
  *                   MFMA)
@@ -277,6 +279,33 @@ moe_status_t moe_expert_ffn_fc2(const void* act, const void* w2, moe_dtype_t dt,
                                 int32_t* workspace, int64_t workspace_elems,
                                 hipStream_t stream);
 
+/* moe_expert_ffn_fc2 with the routing weight of one-entry tokens applied in its epilogue
+ * ([MF §2.1]: FC2 and the final top-k sum belong to one pipeline; the TritonMoE abstract, Daily
+ * Papers listing: the routing weight is applied inside the fused pass).  A token t whose
+ * entries include exactly one local entry, at row p (entry_pos[t*K + k] = p, row_token[p] = t),
+ * has out[t] = bf16(w[t][k] * yp[p]) in moe_combine (float32 product, as the combine forms
+ * it).  This call stores exactly that value into out[t] when it computes row p, instead of
+ * storing yp[p]; every other row is stored to yp as moe_expert_ffn_fc2 does.  Followed by
+ * moe_combine_multi, which computes the other tokens, `out` is bit-identical to
+ * moe_expert_ffn_fc2 followed by moe_combine, with one read of yp and one write of out less
+ * per such token.
+ *   row_token, entry_pos  from the moe_permute call that laid out `act`'s rows.
+ *   topk_w      [T, K] routing weights (float32), as given to moe_combine.
+ *   out         [T, H] (dtype dt) out: the rows of one-entry tokens whose row a block covers.
+ *   row_direct  [2 * max_rows] int32 scratch, written first: entry p = the token row p writes
+ *               directly (-1: none), entry max_rows + p = its weight's bits.
+ * Other arguments as for moe_expert_ffn_fc2 (same schedule in `workspace`, so it follows an
+ * fc1 call with the same blocks).  yp rows of one-entry tokens are not written.  Returns
+ * MOE_ERR_UNSUPPORTED for K > 16 or max_rows >= 2^27. */
+moe_status_t moe_expert_ffn_fc2_direct(const void* act, const void* w2, moe_dtype_t dt, int H,
+                                       int I, int E_loc, const int32_t* blocks,
+                                       const int32_t* n_blocks, int max_blocks, void* yp,
+                                       int64_t max_rows, const int32_t* row_token,
+                                       const int32_t* entry_pos, const float* topk_w, int T,
+                                       int K, void* out, int32_t* row_direct,
+                                       int32_t* workspace, int64_t workspace_elems,
+                                       hipStream_t stream);
+
 /* Every FC1 call starts with this: the GEMM tile schedule of the block table, written to
  * `workspace` (each expert's row-contiguous blocks cut into 128-row pieces, paired into
  * 256-row tiles; the GEMMs' work counters cleared), and the table's error word (below).
@@ -395,6 +424,13 @@ moe_status_t moe_expert_ffn_mx_fc2(const uint8_t* actq, const uint8_t* acts, con
 moe_status_t moe_combine(const void* yp, moe_dtype_t dt, const float* topk_w,
                          const int32_t* entry_pos, int T, int H, int K, void* out,
                          hipStream_t stream);
+
+/* moe_combine for every token except those with exactly one local entry, whose out rows
+ * moe_expert_ffn_fc2_direct has written (they are neither read nor written here).  Same
+ * arguments and checks as moe_combine. */
+moe_status_t moe_combine_multi(const void* yp, moe_dtype_t dt, const float* topk_w,
+                               const int32_t* entry_pos, int T, int H, int K, void* out,
+                               hipStream_t stream);
 
 #ifdef __cplusplus
 }

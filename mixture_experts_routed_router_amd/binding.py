@@ -65,6 +65,10 @@ _SIGNATURES = {
     "moe_router_topk": (_i32, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
                                _vp]),
     "moe_combine": (_i32, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
+    "moe_combine_multi": (_i32, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
+    "moe_expert_ffn_fc2_direct": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp,
+                                         _i64, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _i64,
+                                         _vp]),
 }
 
 
@@ -354,6 +358,27 @@ def moe_expert_ffn_fc2(act, w2, blocks, n_blocks, yp, workspace, stream=None):
            "moe_expert_ffn_fc2")
 
 
+def moe_expert_ffn_fc2_direct(act, w2, blocks, n_blocks, yp, row_token, entry_pos, topk_w, out,
+                              row_direct, workspace, stream=None):
+    E_loc, H, I = w2.shape
+    T, K = topk_w.shape
+    if act.shape[1] != I or yp.shape[1] != H or yp.shape[0] < act.shape[0]:
+        raise MoeError("moe_expert_ffn_fc2_direct: inconsistent shapes")
+    if out.shape != (T, H) or entry_pos.numel() != T * K or row_token.numel() < act.shape[0]:
+        raise MoeError("moe_expert_ffn_fc2_direct: inconsistent shapes")
+    if row_direct.numel() < 2 * act.shape[0]:
+        raise MoeError("moe_expert_ffn_fc2_direct: row_direct needs 2 * max_rows entries")
+    _check(lib().moe_expert_ffn_fc2_direct(
+        _ptr(act, act.dtype, "act"), _ptr(w2, act.dtype, "w2"), _dt(act), H, I, E_loc,
+        _ptr(blocks, torch.int32, "blocks"), _ptr(n_blocks, torch.int32, "n_blocks"),
+        blocks.shape[0], _ptr(yp, act.dtype, "yp"), act.shape[0],
+        _ptr(row_token, torch.int32, "row_token"), _ptr(entry_pos, torch.int32, "entry_pos"),
+        _ptr(topk_w, torch.float32, "topk_w"), T, K, _ptr(out, act.dtype, "out"),
+        _ptr(row_direct, torch.int32, "row_direct"), _ptr(workspace, torch.int32, "workspace"),
+        workspace.numel(), _stream(stream)),
+        "moe_expert_ffn_fc2_direct")
+
+
 MOE_MX_FP8, MOE_MX_FP4 = 0, 1
 
 
@@ -480,6 +505,18 @@ def moe_combine(yp, topk_w, entry_pos, out, stream=None):
            "moe_combine")
 
 
+def moe_combine_multi(yp, topk_w, entry_pos, out, stream=None):
+    T, K = topk_w.shape
+    H = yp.shape[1]
+    if out.shape != (T, H) or entry_pos.numel() != T * K:
+        raise MoeError("moe_combine_multi: inconsistent shapes")
+    _check(lib().moe_combine_multi(_ptr(yp, None, "yp"), _dt(yp),
+                                   _ptr(topk_w, torch.float32, "topk_w"),
+                                   _ptr(entry_pos, torch.int32, "entry_pos"), T, H, K,
+                                   _ptr(out, yp.dtype, "out"), _stream(stream)),
+           "moe_combine_multi")
+
+
 # ------------------------------------------------------------- whole layer path ---
 
 class RoutedExperts:
@@ -493,7 +530,7 @@ class RoutedExperts:
 
     def __init__(self, T, H, E, K, I, P, dtype=torch.bfloat16, E_loc=None, expert_begin=0,
                  expert_stride=1, block_m=128, renormalize=True, device="cuda", gather=False,
-                 planner="moonep", replica_budget=None, precision="bf16"):
+                 planner="moonep", replica_budget=None, precision="bf16", direct=False):
         self.T, self.H, self.E, self.K, self.I, self.P = T, H, E, K, I, P
         if precision not in ("bf16", "mx"):
             raise MoeError(f"unknown precision {precision!r} (bf16 or mx)")
@@ -512,6 +549,11 @@ class RoutedExperts:
         self.replica_budget = (replica_budget if replica_budget is not None
                                else (E_loc or E) // (4 * P))
         self.gather = gather  # FC1 reads x rows through row_token; xp is never written
+        # direct: FC2 writes the weighted out rows of one-entry tokens and the combine skips
+        # them (moe_expert_ffn_fc2_direct + moe_combine_multi; not on the MX path)
+        if direct and precision == "mx":
+            raise MoeError("direct rows are a bf16 / float32 down-GEMM epilogue")
+        self.direct = direct
         self.E_loc = E_loc or E
         self.begin, self.stride, self.block_m = expert_begin, expert_stride, block_m
         self.renormalize = renormalize
@@ -548,6 +590,7 @@ class RoutedExperts:
             self.act = torch.empty((self.max_rows, I), dtype=dtype, device=device)
         self.yp = torch.empty((self.max_rows, H), dtype=dtype, device=device)
         self.out = torch.empty((T, H), dtype=dtype, device=device)
+        self.row_direct = torch.empty((2 * self.max_rows,), **i32) if direct else None
 
     def route(self, logits, stream=None):
         moe_route(logits, self.K, self.topk_ids, self.topk_w, self.counts, self.renormalize, stream)
@@ -579,6 +622,10 @@ class RoutedExperts:
                               self.n_blocks, self.actq, self.acts, self.yp, self.ffn_workspace,
                               stream)
             return
+        if self.direct:
+            self.expert_ffn_fc1(w1, stream)
+            self.expert_ffn_fc2(w2, stream)
+            return
         if self.gather:
             moe_expert_ffn_gather(self._x, self.row_token, w1, w2, self.blocks, self.n_blocks,
                                   self.act, self.yp, self.ffn_workspace, stream)
@@ -603,6 +650,11 @@ class RoutedExperts:
             moe_expert_ffn_mx_fc2(self.actq, self.acts, w2[0], w2[1], self.blocks, self.n_blocks,
                                   self.yp, self.ffn_workspace, stream)
             return
+        if self.direct:
+            moe_expert_ffn_fc2_direct(self.act, w2, self.blocks, self.n_blocks, self.yp,
+                                      self.row_token, self.entry_pos, self.topk_w, self.out,
+                                      self.row_direct, self.ffn_workspace, stream)
+            return
         moe_expert_ffn_fc2(self.act, w2, self.blocks, self.n_blocks, self.yp, self.ffn_workspace,
                            stream)
 
@@ -616,6 +668,9 @@ class RoutedExperts:
         return int(self.ffn_workspace[FFN_WS_ERR].item())
 
     def combine(self, stream=None):
+        if self.direct:
+            moe_combine_multi(self.yp, self.topk_w, self.entry_pos, self.out, stream)
+            return
         moe_combine(self.yp, self.topk_w, self.entry_pos, self.out, stream)
 
     def forward(self, logits, x, w1, w2, stream=None):

@@ -238,6 +238,33 @@ moe_status_t moe_expert_ffn_fc2(const void* act, const void* w2, moe_dtype_t dt,
                                        workspace, yp, max_rows, stream));
 }
 
+moe_status_t moe_expert_ffn_fc2_direct(const void* act, const void* w2, moe_dtype_t dt, int H,
+                                       int I, int E_loc, const int32_t* blocks,
+                                       const int32_t* n_blocks, int max_blocks, void* yp,
+                                       int64_t max_rows, const int32_t* row_token,
+                                       const int32_t* entry_pos, const float* topk_w, int T,
+                                       int K, void* out, int32_t* row_direct,
+                                       int32_t* workspace, int64_t workspace_elems,
+                                       hipStream_t stream) {
+    if (!act || !w2 || !blocks || !n_blocks || !yp || !workspace || !row_token || !entry_pos ||
+        !topk_w || !out || !row_direct)
+        return MOE_ERR_INVALID;
+    if (!aligned16(act) || !aligned16(w2) || !aligned16(yp) || !aligned16(out))
+        return MOE_ERR_INVALID;
+    if (T < 1 || K < 1) return MOE_ERR_INVALID;
+    moe_status_t st = check_ffn_shape(dt, H, I, E_loc, max_blocks, max_rows);
+    if (st != MOE_OK) return st;
+    if (workspace_elems < moe_ffn_workspace_elems(max_blocks)) return MOE_ERR_INVALID;
+    if (E_loc > 256 || K > MOE_MAX_K) return MOE_ERR_UNSUPPORTED;
+    // the bf16 GEMM addresses the row table with 32-bit byte offsets
+    if (max_rows > 0x7FFFFFFLL) return MOE_ERR_UNSUPPORTED;
+    st = launched(moe_launch_direct_rows(row_token, entry_pos, topk_w, T, K, max_rows, row_direct,
+                                         stream));
+    if (st != MOE_OK) return st;
+    return launched(moe_launch_ffn_fc2(act, w2, dt, H, I, E_loc, blocks, n_blocks, max_blocks,
+                                       workspace, yp, max_rows, stream, row_direct, out, T));
+}
+
 moe_status_t moe_expert_ffn(const void* xp, const void* w1, const void* w2, moe_dtype_t dt,
                             int H, int I, int E_loc, const int32_t* blocks,
                             const int32_t* n_blocks, int max_blocks, void* act, void* yp,
@@ -363,6 +390,18 @@ moe_status_t moe_combine(const void* yp, moe_dtype_t dt, const float* topk_w,
     const int64_t row_bytes = (int64_t)H * (dt == MOE_BF16 ? 2 : 4);
     if (row_bytes % 16 != 0 || !aligned16(yp) || !aligned16(out)) return MOE_ERR_INVALID;
     return launched(moe_launch_combine(yp, dt, topk_w, entry_pos, T, H, K, out, stream));
+}
+
+moe_status_t moe_combine_multi(const void* yp, moe_dtype_t dt, const float* topk_w,
+                               const int32_t* entry_pos, int T, int H, int K, void* out,
+                               hipStream_t stream) {
+    if (!yp || !topk_w || !entry_pos || !out) return MOE_ERR_INVALID;
+    if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID;
+    if (T < 1 || H < 1 || K < 1) return MOE_ERR_INVALID;
+    if (K > MOE_MAX_K) return MOE_ERR_UNSUPPORTED;
+    const int64_t row_bytes = (int64_t)H * (dt == MOE_BF16 ? 2 : 4);
+    if (row_bytes % 16 != 0 || !aligned16(yp) || !aligned16(out)) return MOE_ERR_INVALID;
+    return launched(moe_launch_combine(yp, dt, topk_w, entry_pos, T, H, K, out, stream, true));
 }
 
 }  // extern "C"

@@ -13,6 +13,13 @@
 // their FMAs; with fewer it takes 4 chunks per lane at once, entry by entry, so either way a wave
 // has several KB of loads in flight.  Rows of yp and out are read / written in coalesced 1 KB
 // runs per wave instruction; the sum runs over k in ascending order in both paths.
+//
+// Direct rows (moe_expert_ffn_fc2_direct + moe_combine_multi): a token with exactly one local
+// entry sums one weighted row, bf16(fmaf(w, y, 0)), which the down GEMM's epilogue can store
+// itself, bit for bit, into the token's output row.  That removes the reading of its expert
+// row and the second writing of its output row from this pass: on one GPU's 32-expert share of
+// a 256-expert top-8 layer about half the tokens are such tokens.  direct_rows_kernel marks the
+// rows; the combine then skips those tokens (skip_one).
 #include "moe_launch.h"
 
 namespace {
@@ -71,8 +78,9 @@ constexpr int kSparseChunks = 4;
 // no faster on the large-H shapes and slower on the DeepSeek-V3 share).
 constexpr int kDenseChunks = 2;
 
-// KM: the top-k bound the kernel is unrolled for (4, 8 or 16 >= K).
-template <bool kBF16, int KM>
+// KM: the top-k bound the kernel is unrolled for (4, 8 or 16 >= K).  kSkipOne: tokens with
+// exactly one local entry are left alone (their rows were written by the down GEMM).
+template <bool kBF16, int KM, bool kSkipOne>
 __global__ void __launch_bounds__(kThreads)
 combine_kernel(const uint8_t* __restrict__ yp, const float* __restrict__ w,
                const int32_t* __restrict__ entry_pos, int T, int H, int K,
@@ -90,6 +98,7 @@ combine_kernel(const uint8_t* __restrict__ yp, const float* __restrict__ w,
         }
         uint4* orow = reinterpret_cast<uint4*>(out + (int64_t)t * row_bytes);
         const int n_local = __popcll(__ballot(my_p >= 0));
+        if (kSkipOne && n_local == 1) continue;  // wave-uniform
         if (n_local >= 4) {
             // many entries: kDenseChunks chunks per lane, the loads of all entries before the FMAs
             for (int c0 = lane; c0 < n16; c0 += MOE_WAVE * kDenseChunks) {
@@ -155,22 +164,66 @@ combine_kernel(const uint8_t* __restrict__ yp, const float* __restrict__ w,
     }
 }
 
-template <bool kBF16>
+template <bool kBF16, bool kSkipOne>
 void launch_km(int grid, hipStream_t stream, const uint8_t* yp, const float* w,
                const int32_t* entry_pos, int T, int H, int K, uint8_t* out) {
     if (K <= 4)
-        combine_kernel<kBF16, 4><<<grid, kThreads, 0, stream>>>(yp, w, entry_pos, T, H, K, out);
+        combine_kernel<kBF16, 4, kSkipOne><<<grid, kThreads, 0, stream>>>(yp, w, entry_pos, T, H, K, out);
     else if (K <= 8)
-        combine_kernel<kBF16, 8><<<grid, kThreads, 0, stream>>>(yp, w, entry_pos, T, H, K, out);
+        combine_kernel<kBF16, 8, kSkipOne><<<grid, kThreads, 0, stream>>>(yp, w, entry_pos, T, H, K, out);
     else
-        combine_kernel<kBF16, 16><<<grid, kThreads, 0, stream>>>(yp, w, entry_pos, T, H, K, out);
+        combine_kernel<kBF16, 16, kSkipOne><<<grid, kThreads, 0, stream>>>(yp, w, entry_pos, T, H, K, out);
+}
+
+// dir[p] = t and dir[max_rows + p] = the bits of w[t][k] when row p is the only local entry
+// (slot k) of its token t = row_token[p]; dir[p] = -1 (weight word 0) for every other row,
+// padding and rows past the permutation included, so that the table describes all max_rows
+// rows whatever a block table covers.  One thread per row; the token's K entry_pos words are
+// read to count its local entries, as the combine counts them.
+__global__ void __launch_bounds__(kThreads)
+direct_rows_kernel(const int32_t* __restrict__ row_token, const int32_t* __restrict__ entry_pos,
+                   const float* __restrict__ w, int T, int K, int64_t max_rows,
+                   int32_t* __restrict__ dir) {
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t p = (int64_t)blockIdx.x * kThreads + threadIdx.x; p < max_rows; p += stride) {
+        const int t = row_token[p];
+        int tok = -1;
+        int wbits = 0;
+        if (t >= 0 && t < T) {
+            int n = 0, kk = -1;
+            for (int k = 0; k < K; ++k) {
+                const int e = entry_pos[(int64_t)t * K + k];
+                if (e >= 0) {
+                    ++n;
+                    if (e == p) kk = k;
+                }
+            }
+            if (n == 1 && kk >= 0) {
+                tok = t;
+                wbits = __float_as_int(w[(int64_t)t * K + kk]);
+            }
+        }
+        dir[p] = tok;
+        dir[max_rows + p] = wbits;
+    }
 }
 
 }  // namespace
 
+hipError_t moe_launch_direct_rows(const int32_t* row_token, const int32_t* entry_pos,
+                                  const float* w, int T, int K, int64_t max_rows, int32_t* dir,
+                                  hipStream_t stream) {
+    int64_t grid = (max_rows + kThreads - 1) / kThreads;
+    if (grid > 4096) grid = 4096;
+    if (grid < 1) grid = 1;
+    direct_rows_kernel<<<(int)grid, kThreads, 0, stream>>>(row_token, entry_pos, w, T, K,
+                                                           max_rows, dir);
+    return hipGetLastError();
+}
+
 hipError_t moe_launch_combine(const void* yp, moe_dtype_t dt, const float* w,
                               const int32_t* entry_pos, int T, int H, int K, void* out,
-                              hipStream_t stream) {
+                              hipStream_t stream, bool skip_one) {
     const int waves_per_block = kThreads / MOE_WAVE;
     int64_t grid = ((int64_t)T + waves_per_block - 1) / waves_per_block;
     // grid-stride beyond 32K waves (3% faster than 16K on the 32-expert share of a 256-expert
@@ -178,9 +231,16 @@ hipError_t moe_launch_combine(const void* yp, moe_dtype_t dt, const float* w,
     if (grid > 8192) grid = 8192;
     const uint8_t* y = static_cast<const uint8_t*>(yp);
     uint8_t* o = static_cast<uint8_t*>(out);
-    if (dt == MOE_BF16)
-        launch_km<true>((int)grid, stream, y, w, entry_pos, T, H, K, o);
-    else
-        launch_km<false>((int)grid, stream, y, w, entry_pos, T, H, K, o);
+    if (dt == MOE_BF16) {
+        if (skip_one)
+            launch_km<true, true>((int)grid, stream, y, w, entry_pos, T, H, K, o);
+        else
+            launch_km<true, false>((int)grid, stream, y, w, entry_pos, T, H, K, o);
+    } else {
+        if (skip_one)
+            launch_km<false, true>((int)grid, stream, y, w, entry_pos, T, H, K, o);
+        else
+            launch_km<false, false>((int)grid, stream, y, w, entry_pos, T, H, K, o);
+    }
     return hipGetLastError();
 }

@@ -397,6 +397,11 @@ struct GemmArgs {
     int32_t* ctr;            // this GEMM's per-XCD item counters
     int total, per_xcd_items, xcd;
     const int32_t* gather;   // row_token (gather-on-load) or nullptr
+    // FC2 with direct rows: dir[p] = the token whose only local entry is row p (else -1) and
+    // dir[a_rows + p] its routing weight's bits; such a row goes to out[token], weighted
+    const int32_t* dir;
+    uint16_t* out;
+    int T;
 };
 
 // One item (tile, column tile): its wave-uniform description and this lane's A copy offsets
@@ -718,14 +723,40 @@ __device__ __forceinline__ void issue_prologue(const GemmArgs& g, const Item& it
         issue_prologue_m<kSwiGLU, kGather, 64>(g, it, smem_base, wave, seg_row, lane_chunk);
 }
 
+// FC2 with direct rows: an item's 256 dir entries and their 256 weights, copied straight into
+// buffer `buf` (512 words) of the gidx area of LDS (unused by FC2): lane l of wave w moves word
+// e = 64 w + l, i.e. entry (e & 255) of side e >> 8, for tile row e & 255 (clamped to the
+// item's first row where the row is past its half, read and unused).  Issued with the item's
+// first slices, one item ahead, into the buffer the item before last used (every wave has
+// passed a barrier since that item's epilogue read it); the waits that follow only become
+// stricter, and the item's last wait covers it before its epilogue reads it.
+__device__ __forceinline__ void issue_dir_copy(const GemmArgs& g, const Item& it, int wave,
+                                               int buf) {
+    const int e = wave * MOE_WAVE + moe_lane_id();
+    const int side = e >> 8, r = e & 255, h = r >> 7, rl = r & (HALF - 1);
+    const int hr = h ? it.h_rows[1] : it.h_rows[0];
+    const int row = rl < hr ? (h ? it.h_row0[1] : it.h_row0[0]) + rl : it.h_row0[0];
+    buf = __builtin_amdgcn_readfirstlane(buf);  // wave-uniform: the M0 base is a scalar
+    one_copy_dword(g.gidx_lds + (uint32_t)(buf * 512 + wave * MOE_WAVE) * 4u, g.dir,
+                   ((uint32_t)side * (uint32_t)g.a_rows + (uint32_t)row) * 4u);
+}
+
+// bf16 pair u reweighted as a one-entry combine does it: bf16(fmaf(w, y, 0)) per half, rounded
+// to nearest even by the hardware conversion (the combine's software rounding gives the same
+// bits for every finite value; one instruction per pair instead of about a dozen).
+__device__ __forceinline__ uint32_t weight_bf16x2(uint32_t u, float w) {
+    return pack_bf16x2(fmaf(w, __uint_as_float(u << 16), 0.f),
+                       fmaf(w, __uint_as_float(u & 0xFFFF0000u), 0.f));
+}
+
 // One item whose first slices are already issued: the K loop; meanwhile the next item is
 // decoded (decode_step, over the last slice boundaries); then the next item's first slices
 // are issued, and this item's results are written from registers while they land.
-template <bool kSwiGLU, bool kGather, int kRowsA>
+template <bool kSwiGLU, bool kGather, int kRowsA, bool kDirect = false>
 __device__ __forceinline__ void gemm_item(const GemmArgs& g, const Item& cur_in, Item& nxt,
                                           Queue& qs, int* item_s, uint8_t* smem,
                                           uint32_t smem_base, int tid, int wave, int lane,
-                                          int seg_row, int seg_lchunk) {
+                                          int seg_row, int seg_lchunk, int dbuf) {
     using M = Mode<kRowsA>;
     const Item cur = uniform_item(cur_in);
     constexpr int RB = M::kRowBlocks;
@@ -837,6 +868,10 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& g, const Item& cur_in,
         decode_step<kSwiGLU, kGather>(step, nxt, g, qs, item_s, tid, wave, seg_row, seg_lchunk);
     }
     issue_prologue<kSwiGLU, kGather>(g, nxt, smem_base, wave, opaque(seg_row), opaque(seg_lchunk) * 16u);
+    if constexpr (kDirect) {
+        const Item nu = uniform_item(nxt);
+        if (nu.rows_a != 0) issue_dir_copy(g, nu, wave, dbuf ^ 1);
+    }
 
     // epilogue: acc[i][j][4c + e] = C[tile row wrow + i*32 + lane%32][col + 8c + 4(lane/32) + e].
     // Lanes l and l + 32 hold one row.  One v_permlane32_swap per pair of packed registers
@@ -853,6 +888,18 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& g, const Item& cur_in,
             const bool h1 = tr >= HALF;
             const bool row_ok = rl < (h1 ? cur.h_rows[1] : cur.h_rows[0]);
             uint16_t* crow = g.C + (int64_t)((h1 ? cur.h_row0[1] : cur.h_row0[0]) + rl) * g.ldc;
+            // direct rows: out[token] instead of the expert-output row (tokens checked: a
+            // table over rows the dir entries do not describe still stores inside out)
+            int dtok = -1;
+            float dw = 0.f;
+            if constexpr (kDirect) {
+                const int tk = g.gidx[dbuf * 512 + tr];
+                if (tk >= 0 && tk < g.T) {
+                    dtok = tk;
+                    dw = __int_as_float(g.gidx[dbuf * 512 + 256 + tr]);
+                    crow = g.out + (int64_t)tk * g.ldc;
+                }
+            }
             constexpr int NJ = kSwiGLU ? 1 : 2;
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
@@ -874,6 +921,12 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& g, const Item& cur_in,
                     }
                     pk[c][0] = pack_bf16x2(v[0], v[1]);
                     pk[c][1] = pack_bf16x2(v[2], v[3]);
+                    if constexpr (kDirect) {
+                        if (dtok >= 0) {
+                            pk[c][0] = weight_bf16x2(pk[c][0], dw);
+                            pk[c][1] = weight_bf16x2(pk[c][1], dw);
+                        }
+                    }
                 }
                 // swap(x, y) exchanges lanes 32..63 of x with lanes 0..31 of y: afterwards x
                 // holds (lane l: own group c; lane l + 32: lane l's group c + 2) and y holds
@@ -918,12 +971,15 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& g, const Item& cur_in,
 // self-balancing); a workgroup whose range is drained helps the others.  Items are
 // pipelined: the next one is claimed and decoded during the current one's last K slices and
 // its first slices are in flight while the current one's results are written.
-template <bool kSwiGLU, bool kGather>
+template <bool kSwiGLU, bool kGather, bool kDirect = false>
 __global__ void __launch_bounds__(kThreads, 1)
 ffn_bf16_kernel(const uint16_t* __restrict__ A, int64_t a_rows, int Kdim,
                 const uint16_t* __restrict__ B, int64_t b_expert_stride, int b_rows,
                 uint16_t* __restrict__ C, int ldc, int n_cols, int I, int NT,
-                int max_blocks, int32_t* __restrict__ ws, const int32_t* __restrict__ gather) {
+                int max_blocks, int32_t* __restrict__ ws, const int32_t* __restrict__ gather,
+                const int32_t* __restrict__ dir = nullptr, uint16_t* __restrict__ out = nullptr,
+                int T = 0) {
+    static_assert(!kDirect || (!kSwiGLU && !kGather), "direct rows are an FC2 epilogue");
     __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM_BYTES];
     __shared__ int item_s[2];  // [0] the next item, [1] thread 0's last counter increment
     __shared__ __attribute__((aligned(256))) int32_t gidx[kWaves * 4 * MOE_WAVE];
@@ -940,6 +996,9 @@ ffn_bf16_kernel(const uint16_t* __restrict__ A, int64_t a_rows, int Kdim,
     g.per_xcd_items = (g.total + kXcds - 1) / kXcds;
     g.xcd = blockIdx.x % kXcds;
     g.gather = gather;
+    g.dir = dir;
+    g.out = out;
+    g.T = T;
 
     const int tid = threadIdx.x;
     const int lane = moe_lane_id();
@@ -961,20 +1020,26 @@ ffn_bf16_kernel(const uint16_t* __restrict__ A, int64_t a_rows, int Kdim,
         decode_step<kSwiGLU, kGather>(s, cur, g, qs, item_s, tid, wave, seg_row, seg_lchunk);
     }
     issue_prologue<kSwiGLU, kGather>(g, cur, smem_base, wave, seg_row, seg_lchunk * 16u);
+    int dbuf = 0;  // direct rows: the gidx buffer of the current item's row table
+    if constexpr (kDirect) {
+        const Item u = uniform_item(cur);
+        if (u.rows_a != 0) issue_dir_copy(g, u, wave, 0);
+    }
 
     for (;;) {
         const int rows_a = __builtin_amdgcn_readfirstlane(cur.rows_a);
         if (rows_a == 0) break;
         Item nxt;
         if (rows_a == 256)
-            gemm_item<kSwiGLU, kGather, 256>(g, cur, nxt, qs, item_s, smem, smem_base, tid, wave, lane,
-                                    seg_row, seg_lchunk);
+            gemm_item<kSwiGLU, kGather, 256, kDirect>(g, cur, nxt, qs, item_s, smem, smem_base, tid, wave, lane,
+                                    seg_row, seg_lchunk, dbuf);
         else if (rows_a == 128)
-            gemm_item<kSwiGLU, kGather, 128>(g, cur, nxt, qs, item_s, smem, smem_base, tid, wave, lane,
-                                    seg_row, seg_lchunk);
+            gemm_item<kSwiGLU, kGather, 128, kDirect>(g, cur, nxt, qs, item_s, smem, smem_base, tid, wave, lane,
+                                    seg_row, seg_lchunk, dbuf);
         else
-            gemm_item<kSwiGLU, kGather, 64>(g, cur, nxt, qs, item_s, smem, smem_base, tid, wave, lane,
-                                   seg_row, seg_lchunk);
+            gemm_item<kSwiGLU, kGather, 64, kDirect>(g, cur, nxt, qs, item_s, smem, smem_base, tid, wave, lane,
+                                   seg_row, seg_lchunk, dbuf);
+        dbuf ^= 1;
         cur = nxt;
     }
     // the last workgroup out clears this GEMM's counters so the kernel can run again
@@ -1002,7 +1067,8 @@ ffn_f32_kernel(const float* __restrict__ A, const int32_t* __restrict__ gather, 
                int Kdim, const float* __restrict__ B, int64_t b_expert_stride, int I,
                float* __restrict__ C, int ldc, int n_cols, const int32_t* __restrict__ blocks,
                const int32_t* __restrict__ n_blocks_ptr, int max_blocks, int E_loc,
-               int64_t max_rows) {
+               int64_t max_rows, const int32_t* __restrict__ dir = nullptr,
+               float* __restrict__ out = nullptr, int T = 0) {
     constexpr int TC = 64, TK = 64, TR = 64, RPT = TR / 4;
     __shared__ float a_s[TR][TK + 1];
     __shared__ float g_s[TC][TK + 1];
@@ -1057,7 +1123,17 @@ ffn_f32_kernel(const float* __restrict__ A, const int32_t* __restrict__ gather, 
                     const int r = r0 + rg + 4 * j;
                     if (r < m) {
                         const float g = ag[j];
-                        C[(int64_t)(row0 + r) * ldc + col] = kSwiGLU ? g / (1.f + expf(-g)) * au[j] : g;
+                        float* dst = C + (int64_t)(row0 + r) * ldc + col;
+                        float v = kSwiGLU ? g / (1.f + expf(-g)) * au[j] : g;
+                        if (!kSwiGLU && dir) {
+                            // direct row: out[token] = fmaf(w, y, 0), as a one-entry combine
+                            const int tk = dir[row0 + r];
+                            if (tk >= 0 && tk < T) {
+                                dst = out + (int64_t)tk * ldc + col;
+                                v = fmaf(__int_as_float(dir[max_rows + row0 + r]), g, 0.f);
+                            }
+                        }
+                        *dst = v;
                     }
                 }
             }
@@ -1116,19 +1192,25 @@ hipError_t moe_launch_ffn_fc1(const void* a, const void* w1, moe_dtype_t dt, int
 hipError_t moe_launch_ffn_fc2(const void* act, const void* w2, moe_dtype_t dt, int H, int I,
                               int E_loc, const int32_t* blocks, const int32_t* n_blocks,
                               int max_blocks, int32_t* ws, void* yp, int64_t max_rows,
-                              hipStream_t stream) {
+                              hipStream_t stream, const int32_t* dir, void* out, int T) {
     if (dt == MOE_F32) {
         const int64_t items = (int64_t)max_blocks * ((H + 63) / 64);
         const int grid = items < 2048 ? (int)items : 2048;
         ffn_f32_kernel<false><<<grid, 256, 0, stream>>>(
             static_cast<const float*>(act), nullptr, max_rows, I, static_cast<const float*>(w2),
             (int64_t)H * I, I, static_cast<float*>(yp), H, H, blocks, n_blocks, max_blocks,
-            E_loc, max_rows);
+            E_loc, max_rows, dir, static_cast<float*>(out), T);
         return hipGetLastError();
     }
-    ffn_bf16_kernel<false, false><<<persistent_grid(), kThreads, 0, stream>>>(
-        static_cast<const uint16_t*>(act), max_rows, I, static_cast<const uint16_t*>(w2),
-        (int64_t)H * I, H, static_cast<uint16_t*>(yp), H, H, I, (H + BN - 1) / BN, max_blocks,
-        ws, nullptr);
+    if (dir)
+        ffn_bf16_kernel<false, false, true><<<persistent_grid(), kThreads, 0, stream>>>(
+            static_cast<const uint16_t*>(act), max_rows, I, static_cast<const uint16_t*>(w2),
+            (int64_t)H * I, H, static_cast<uint16_t*>(yp), H, H, I, (H + BN - 1) / BN,
+            max_blocks, ws, nullptr, dir, static_cast<uint16_t*>(out), T);
+    else
+        ffn_bf16_kernel<false, false><<<persistent_grid(), kThreads, 0, stream>>>(
+            static_cast<const uint16_t*>(act), max_rows, I, static_cast<const uint16_t*>(w2),
+            (int64_t)H * I, H, static_cast<uint16_t*>(yp), H, H, I, (H + BN - 1) / BN,
+            max_blocks, ws, nullptr);
     return hipGetLastError();
 }

@@ -44,7 +44,8 @@ hipError_t moe_launch_ffn_fc1(const void* a, const void* w1, moe_dtype_t dt, int
 hipError_t moe_launch_ffn_fc2(const void* act, const void* w2, moe_dtype_t dt, int H, int I,
                               int E_loc, const int32_t* blocks, const int32_t* n_blocks,
                               int max_blocks, int32_t* ws, void* yp, int64_t max_rows,
-                              hipStream_t stream);
+                              hipStream_t stream, const int32_t* dir = nullptr,
+                              void* out = nullptr, int T = 0);
 
 hipError_t moe_launch_ffn_mx_fc1(const uint8_t* xq, const uint8_t* xs, const int32_t* gather,
                                  int64_t x_rows, const uint8_t* w1q, const uint8_t* w1s, int H,
@@ -57,6 +58,11 @@ hipError_t moe_launch_ffn_mx_fc2(const uint8_t* actq, const uint8_t* acts, const
 inline int64_t moe_mx_scale_pitch_impl(int64_t cols) { return (cols / 32 + 3) / 4 * 4; }
 hipError_t moe_launch_mx_quantize(const void* src, moe_dtype_t dt, int64_t rows, int64_t cols,
                                   int fmt, uint8_t* codes, uint8_t* scales, hipStream_t stream);
+// skip_one: leave out the tokens with exactly one local entry (moe_combine_multi)
 hipError_t moe_launch_combine(const void* yp, moe_dtype_t dt, const float* w,
                               const int32_t* entry_pos, int T, int H, int K, void* out,
-                              hipStream_t stream);
+                              hipStream_t stream, bool skip_one = false);
+// dir[p] / dir[max_rows + p] for p < max_rows (moe_expert_ffn_fc2_direct)
+hipError_t moe_launch_direct_rows(const int32_t* row_token, const int32_t* entry_pos,
+                                  const float* w, int T, int K, int64_t max_rows, int32_t* dir,
+                                  hipStream_t stream);

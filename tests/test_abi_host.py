@@ -201,6 +201,29 @@ def test_ffn_and_combine_reject(lib):
     assert lib.moe_combine(P[0], 1, P[1], P[2], 4, 128, 17, P[3], NULL) == UNSUPPORTED  # K > 16
 
 
+def test_direct_rows_reject(lib):
+    def fc2d(act=P[0], row_token=P[7], entry_pos=P[8], topk_w=P[9], out=P[10], row_direct=P[11],
+             dt=1, H=128, I=256, T=64, K=8, max_rows=1024, ws_elems=272, E_loc=8):
+        return lib.moe_expert_ffn_fc2_direct(act, P[1], dt, H, I, E_loc, P[2], P[3], 16, P[4],
+                                             max_rows, row_token, entry_pos, topk_w, T, K, out,
+                                             row_direct, P[5], ws_elems, NULL)
+    for arg in ("act", "row_token", "entry_pos", "topk_w", "out", "row_direct"):
+        assert fc2d(**{arg: NULL}) == INVALID, arg
+    assert fc2d(out=ctypes.c_void_p(0x1008)) == INVALID    # 16-byte aligned rows
+    assert fc2d(T=0) == INVALID
+    assert fc2d(K=0) == INVALID
+    assert fc2d(K=17) == UNSUPPORTED                        # the combine's top-k bound
+    assert fc2d(ws_elems=271) == INVALID
+    assert fc2d(H=2880, I=100) == UNSUPPORTED               # bf16 needs multiples of 64
+    assert fc2d(E_loc=300) == UNSUPPORTED
+    assert fc2d(max_rows=1 << 27) == UNSUPPORTED            # 32-bit offsets into row_direct
+    multi = lib.moe_combine_multi
+    assert multi(P[0], 1, P[1], P[2], 4, 100, 2, P[3], NULL) == INVALID  # 200-B rows
+    assert multi(P[0], 1, P[1], NULL, 4, 128, 2, P[3], NULL) == INVALID
+    assert multi(P[0], 3, P[1], P[2], 4, 128, 2, P[3], NULL) == INVALID
+    assert multi(P[0], 1, P[1], P[2], 4, 128, 17, P[3], NULL) == UNSUPPORTED
+
+
 def test_binding_fails_loudly_without_a_gpu_tensor(lib):
     import torch
     from mixture_experts_routed_router_amd import binding
