@@ -68,10 +68,11 @@ def parse():
                     help="skip timing moe_router_topk (router scores + top-k) beside the step")
     ap.add_argument("--no-mx-summary", action="store_true",
                     help="skip the MX path's summary (mx_path) in a bf16 run")
-    ap.add_argument("--no-direct", action="store_true",
-                    help="down GEMM stores every row to yp and the combine sums every token "
-                         "(default: the rows of one-entry tokens go to out from the down GEMM's "
-                         "epilogue, moe_expert_ffn_fc2_direct + moe_combine_multi)")
+    ap.add_argument("--direct", choices=("auto", "on", "off"), default="auto",
+                    help="on: the rows of one-entry tokens go to out from the down GEMM's epilogue "
+                         "(moe_expert_ffn_fc2_direct + moe_combine_multi); off: the down GEMM stores "
+                         "every row to yp and the combine sums every token; auto (default): on where "
+                         "a token can have exactly one local entry (a share of the experts, or top-1)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a reference for "
                          "hardware byte counters)")
@@ -501,7 +502,8 @@ def main():
         wmx = binding.mx_quantize_weights(W1, W2)  # MXFP4 weights, prepared once
     if mx:
         W1, W2 = wmx
-    direct = not (args.no_direct or mx)
+    direct = not mx and (args.direct == "on" or
+                         (args.direct == "auto" and (w.n_local < w.E or w.K == 1)))
     layer = binding.RoutedExperts(w.T, w.H, w.E, w.K, w.I, w.P, dtype=dt, E_loc=w.n_local,
                                   expert_begin=w.expert_begin, expert_stride=w.expert_stride,
                                   block_m=w.beta, gather=not args.materialize,
