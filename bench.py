@@ -502,8 +502,7 @@ def main():
         wmx = binding.mx_quantize_weights(W1, W2)  # MXFP4 weights, prepared once
     if mx:
         W1, W2 = wmx
-    direct = not mx and (args.direct == "on" or
-                         (args.direct == "auto" and (w.n_local < w.E or w.K == 1)))
+    direct = args.direct == "on" or (args.direct == "auto" and (w.n_local < w.E or w.K == 1))
     layer = binding.RoutedExperts(w.T, w.H, w.E, w.K, w.I, w.P, dtype=dt, E_loc=w.n_local,
                                   expert_begin=w.expert_begin, expert_stride=w.expert_stride,
                                   block_m=w.beta, gather=not args.materialize,
@@ -638,7 +637,7 @@ def main():
         lay_mx = binding.RoutedExperts(w.T, w.H, w.E, w.K, w.I, w.P, dtype=dt, E_loc=w.n_local,
                                        expert_begin=w.expert_begin,
                                        expert_stride=w.expert_stride, block_m=w.beta,
-                                       planner=args.planner, precision="mx")
+                                       planner=args.planner, precision="mx", direct=direct)
         st = max(20, min(args.steps, 100))
         tm_mx, n_mx, _, _ = measure(skew, st, st, lay_mx, wmx[0], wmx[1], settle_s=0.5)
         wl_mx, pr_mx = tm_mx["median_s"], tm_mx["per"]
@@ -646,6 +645,8 @@ def main():
         line["mx_path"] = {
             "tokens_per_s": round(w.T / wl_mx, 1), "ms_per_step": round(wl_mx * 1e3, 4),
             "fc1_kernel": "ffn_mx_kernel<true>",
+            "combine": "direct rows (one-entry tokens stored by the MX down GEMM)" if direct else
+                       "every token summed by the combine",
             "fc1_tflops": round(4.0 * w.H * w.I * n_mx / f1 / 1e12, 1),
             "fc1_frac_of_fp8_peak": round(4.0 * w.H * w.I * n_mx / f1 / 1e12 / PEAK_FP8_TFLOPS, 4),
             "gemm_tflops": round(6.0 * w.H * w.I * n_mx / ((pr_mx["fc1"] + pr_mx["fc2"]) * 1e-6) / 1e12, 1),

@@ -412,6 +412,22 @@ moe_status_t moe_expert_ffn_mx_fc2(const uint8_t* actq, const uint8_t* acts, con
                                    void* yp, int64_t max_rows, int32_t* workspace,
                                    int64_t workspace_elems, hipStream_t stream);
 
+/* moe_expert_ffn_mx_fc2 with direct rows, as moe_expert_ffn_fc2_direct is to
+ * moe_expert_ffn_fc2: rows whose token has exactly one local entry are stored into out[t] as
+ * bf16(w[t][k] * yp[p]) (float32 product) instead of into yp; followed by moe_combine_multi,
+ * `out` is bit-identical to moe_expert_ffn_mx_fc2 followed by moe_combine.  Arguments as for
+ * moe_expert_ffn_mx_fc2 plus row_token, entry_pos, topk_w, T, K, out and row_direct as for
+ * moe_expert_ffn_fc2_direct (same checks). */
+moe_status_t moe_expert_ffn_mx_fc2_direct(const uint8_t* actq, const uint8_t* acts,
+                                          const uint8_t* w2q, const uint8_t* w2s, int H, int I,
+                                          int E_loc, const int32_t* blocks,
+                                          const int32_t* n_blocks, int max_blocks, void* yp,
+                                          int64_t max_rows, const int32_t* row_token,
+                                          const int32_t* entry_pos, const float* topk_w, int T,
+                                          int K, void* out, int32_t* row_direct,
+                                          int32_t* workspace, int64_t workspace_elems,
+                                          hipStream_t stream);
+
 /* ---------------------------------------------------------------------- combine --- */
 
 /* Routing-weight combine ([MF §1]; [MF §2.1]: the top-k sum is its own step; [MF App. A.2]:

@@ -66,6 +66,9 @@ _SIGNATURES = {
                                _vp]),
     "moe_combine": (_i32, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
     "moe_combine_multi": (_i32, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
+    "moe_expert_ffn_mx_fc2_direct": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _i32,
+                                            _vp, _i64, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp,
+                                            _i64, _vp]),
     "moe_expert_ffn_fc2_direct": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp,
                                          _i64, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _i64,
                                          _vp]),
@@ -459,6 +462,30 @@ def moe_expert_ffn_mx_fc2(actq, acts, w2q, w2s, blocks, n_blocks, yp, workspace,
         _ptr(workspace, torch.int32, "workspace"), workspace.numel(), _stream(stream)), call)
 
 
+def moe_expert_ffn_mx_fc2_direct(actq, acts, w2q, w2s, blocks, n_blocks, yp, row_token, entry_pos,
+                                 topk_w, out, row_direct, workspace, stream=None):
+    call = "moe_expert_ffn_mx_fc2_direct"
+    E_loc, H, I2 = w2q.shape
+    I = 2 * I2
+    rows = actq.shape[0]
+    T, K = topk_w.shape
+    if actq.shape[1] != I or yp.shape != (rows, H) or yp.dtype != torch.bfloat16:
+        raise MoeError(f"{call}: inconsistent shapes")
+    if out.shape != (T, H) or entry_pos.numel() != T * K or row_token.numel() < rows:
+        raise MoeError(f"{call}: inconsistent shapes")
+    if row_direct.numel() < 2 * rows:
+        raise MoeError(f"{call}: row_direct needs 2 * max_rows entries")
+    _check(lib().moe_expert_ffn_mx_fc2_direct(
+        _ptr(actq, torch.uint8, "actq"), _mx_scales(call, acts, actq.shape[:1], I, "acts"),
+        _ptr(w2q, torch.uint8, "w2q"), _mx_scales(call, w2s, w2q.shape[:2], I, "w2s"), H, I,
+        E_loc, _ptr(blocks, torch.int32, "blocks"), _ptr(n_blocks, torch.int32, "n_blocks"),
+        blocks.shape[0], _ptr(yp, torch.bfloat16, "yp"), rows,
+        _ptr(row_token, torch.int32, "row_token"), _ptr(entry_pos, torch.int32, "entry_pos"),
+        _ptr(topk_w, torch.float32, "topk_w"), T, K, _ptr(out, torch.bfloat16, "out"),
+        _ptr(row_direct, torch.int32, "row_direct"), _ptr(workspace, torch.int32, "workspace"),
+        workspace.numel(), _stream(stream)), call)
+
+
 def moe_expert_ffn_mx(xq, xs, row_token, w1q, w1s, w2q, w2s, blocks, n_blocks, actq, acts, yp,
                       workspace, stream=None):
     """The SwiGLU expert FFN with MXFP4 weights and MXFP8 activations (FC1 then FC2)."""
@@ -550,9 +577,7 @@ class RoutedExperts:
                                else (E_loc or E) // (4 * P))
         self.gather = gather  # FC1 reads x rows through row_token; xp is never written
         # direct: FC2 writes the weighted out rows of one-entry tokens and the combine skips
-        # them (moe_expert_ffn_fc2_direct + moe_combine_multi; not on the MX path)
-        if direct and precision == "mx":
-            raise MoeError("direct rows are a bf16 / float32 down-GEMM epilogue")
+        # them (moe_expert_ffn_fc2_direct / moe_expert_ffn_mx_fc2_direct + moe_combine_multi)
         self.direct = direct
         self.E_loc = E_loc or E
         self.begin, self.stride, self.block_m = expert_begin, expert_stride, block_m
@@ -616,6 +641,10 @@ class RoutedExperts:
         moe_mx_quantize(x, MOE_MX_FP8, self.xq, self.xs, stream)
 
     def expert_ffn(self, w1, w2, stream=None):
+        if self.precision == "mx" and self.direct:
+            self.expert_ffn_fc1(w1, stream)
+            self.expert_ffn_fc2(w2, stream)
+            return
         if self.precision == "mx":
             (w1q, w1s), (w2q, w2s) = w1, w2
             moe_expert_ffn_mx(self.xq, self.xs, self.row_token, w1q, w1s, w2q, w2s, self.blocks,
@@ -646,6 +675,12 @@ class RoutedExperts:
                                self.ffn_workspace, stream)
 
     def expert_ffn_fc2(self, w2, stream=None):
+        if self.precision == "mx" and self.direct:
+            moe_expert_ffn_mx_fc2_direct(self.actq, self.acts, w2[0], w2[1], self.blocks,
+                                         self.n_blocks, self.yp, self.row_token, self.entry_pos,
+                                         self.topk_w, self.out, self.row_direct,
+                                         self.ffn_workspace, stream)
+            return
         if self.precision == "mx":
             moe_expert_ffn_mx_fc2(self.actq, self.acts, w2[0], w2[1], self.blocks, self.n_blocks,
                                   self.yp, self.ffn_workspace, stream)

@@ -364,6 +364,34 @@ moe_status_t moe_expert_ffn_mx_fc2(const uint8_t* actq, const uint8_t* acts, con
                                           static_cast<uint16_t*>(yp), max_rows, stream));
 }
 
+moe_status_t moe_expert_ffn_mx_fc2_direct(const uint8_t* actq, const uint8_t* acts,
+                                          const uint8_t* w2q, const uint8_t* w2s, int H, int I,
+                                          int E_loc, const int32_t* blocks,
+                                          const int32_t* n_blocks, int max_blocks, void* yp,
+                                          int64_t max_rows, const int32_t* row_token,
+                                          const int32_t* entry_pos, const float* topk_w, int T,
+                                          int K, void* out, int32_t* row_direct,
+                                          int32_t* workspace, int64_t workspace_elems,
+                                          hipStream_t stream) {
+    if (!actq || !acts || !w2q || !w2s || !yp || !row_token || !entry_pos || !topk_w || !out ||
+        !row_direct)
+        return MOE_ERR_INVALID;
+    if (!aligned16(actq) || !aligned16(w2q) || !aligned16(yp) || !aligned16(out))
+        return MOE_ERR_INVALID;
+    if (!aligned4(acts) || !aligned4(w2s)) return MOE_ERR_INVALID;
+    if (T < 1 || K < 1) return MOE_ERR_INVALID;
+    moe_status_t st = check_ffn_mx_shape(H, I, E_loc, max_blocks, max_rows, blocks, n_blocks,
+                                         workspace, workspace_elems);
+    if (st != MOE_OK) return st;
+    if (K > MOE_MAX_K || max_rows > 0x7FFFFFFLL) return MOE_ERR_UNSUPPORTED;
+    st = launched(moe_launch_direct_rows(row_token, entry_pos, topk_w, T, K, max_rows, row_direct,
+                                         stream));
+    if (st != MOE_OK) return st;
+    return launched(moe_launch_ffn_mx_fc2(actq, acts, w2q, w2s, H, I, max_blocks, workspace,
+                                          static_cast<uint16_t*>(yp), max_rows, stream, row_direct,
+                                          out, T));
+}
+
 moe_status_t moe_expert_ffn_mx(const uint8_t* xq, const uint8_t* xs, const int32_t* row_token,
                                int64_t x_rows, const uint8_t* w1q, const uint8_t* w1s,
                                const uint8_t* w2q, const uint8_t* w2s, int H, int I, int E_loc,

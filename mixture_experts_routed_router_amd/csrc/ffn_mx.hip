@@ -68,6 +68,11 @@ struct MxArgs {
     uint8_t* acts;          // FC1: [rows, act_sp] scales
     int act_sp;
     uint16_t* yp;           // FC2: [rows, H] bf16
+    // FC2 with direct rows: dir[p] = the token whose only local entry is row p (else -1),
+    // dir[a_rows + p] its weight's bits; such a row goes to out[token], weighted
+    const int32_t* dir;
+    uint16_t* out;
+    int T;
     const int32_t* tiles;
     const int32_t* ntiles;
     int NT;
@@ -143,6 +148,25 @@ typedef const __attribute__((address_space(4))) int32_t* sgpr_ptr_t;
 
 // row_token entries of the next item's 256 tile rows (gather), staged by decode step 2
 __shared__ __attribute__((aligned(16))) int32_t mx_gidx[256];
+// FC2 with direct rows: two buffers of an item's 256 dir entries and 256 weights
+__shared__ __attribute__((aligned(16))) int32_t mx_dir[1024];
+
+// Direct rows: item `it`'s dir entries and weights into buffer `buf` of mx_dir; lane l of wave w
+// moves word e = 64 w + l, entry (e & 255) of side e >> 8, for tile row e & 255 (clamped to the
+// item's first row where the row is past its half, read and unused).  Issued with the item's
+// first slice, one item ahead, into the buffer the item before last used (every wave has passed
+// a barrier since that item's epilogue read it); the item's last wait covers it.
+__device__ __forceinline__ void issue_dir_copy(const MxArgs& g, const MxCtx& c, const MxItem& it,
+                                               int buf) {
+    const int e = c.wave * MOE_WAVE + c.lane;
+    const int side = e >> 8, r = e & 255, h = r >> 7, rl = r & (HALF - 1);
+    const int hr = h ? it.h_rows[1] : it.h_rows[0];
+    const int row = rl < hr ? (h ? it.h_row0[1] : it.h_row0[0]) + rl : it.h_row0[0];
+    buf = __builtin_amdgcn_readfirstlane(buf);
+    const uint32_t base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int32_t*)mx_dir;
+    one_copy_dword(base + (uint32_t)(buf * 512 + c.wave * MOE_WAVE) * 4u, g.dir,
+                   ((uint32_t)side * (uint32_t)g.a_rows + (uint32_t)row) * 4u);
+}
 
 template <bool kFC1>
 __device__ __forceinline__ void decode_step(int step, MxItem& n, const MxArgs& g, const MxCtx& c) {
@@ -375,9 +399,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
-// FC2 epilogue: this wave's 128 columns of H x 64 token rows, bf16.
+// bf16 pair u reweighted as a one-entry combine does it: bf16(fmaf(w, y, 0)) per half, rounded
+// to nearest even by the hardware conversion (the combine's software rounding gives the same
+// bits for finite values).
+__device__ __forceinline__ uint32_t weight_bf16x2(uint32_t u, float w) {
+    return pack_bf16x2(fmaf(w, __uint_as_float(u << 16), 0.f),
+                       fmaf(w, __uint_as_float(u & 0xFFFF0000u), 0.f));
+}
+
+// FC2 epilogue: this wave's 128 columns of H x 64 token rows, bf16.  kDirect: rows whose dir
+// entry (buffer dbuf) names a token in [0, T) go to that token's out row, weighted.
+template <bool kDirect>
 __device__ __forceinline__ void epilogue_fc2(const MxArgs& g, const MxItem& it,
-                                             const v16f_t (&acc)[4][2], int fh, int tq, int lane) {
+                                             const v16f_t (&acc)[4][2], int fh, int tq, int lane,
+                                             int dbuf) {
     const int hi = lane >> 5;
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
@@ -386,6 +421,15 @@ __device__ __forceinline__ void epilogue_fc2(const MxArgs& g, const MxItem& it,
         const int rl = tr & (HALF - 1);
         const bool row_ok = rl < (h1 ? it.h_rows[1] : it.h_rows[0]);
         const int64_t p = (h1 ? it.h_row0[1] : it.h_row0[0]) + rl;
+        int dtok = -1;
+        float dw = 0.f;
+        if constexpr (kDirect) {
+            const int tk = mx_dir[dbuf * 512 + tr];
+            if (tk >= 0 && tk < g.T) {
+                dtok = tk;
+                dw = __int_as_float(mx_dir[dbuf * 512 + 256 + tr]);
+            }
+        }
 #pragma unroll
         for (int fb = 0; fb < 4; ++fb) {
             const int col0 = it.nt * 256 + 128 * fh + 32 * fb;
@@ -395,6 +439,14 @@ __device__ __forceinline__ void epilogue_fc2(const MxArgs& g, const MxItem& it,
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
                     pk[q][s] = pack_bf16x2(acc[fb][tb][4 * q + 2 * s], acc[fb][tb][4 * q + 2 * s + 1]);
+            if constexpr (kDirect) {
+                if (dtok >= 0) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+#pragma unroll
+                        for (int s = 0; s < 2; ++s) pk[q][s] = weight_bf16x2(pk[q][s], dw);
+                }
+            }
             uint32_t xs[2][2], ys[2][2];
 #pragma unroll
             for (int q = 0; q < 2; ++q)
@@ -405,7 +457,8 @@ __device__ __forceinline__ void epilogue_fc2(const MxArgs& g, const MxItem& it,
                     ys[q][s] = r[1];
                 }
             if (row_ok && col0 < g.n_out) {
-                uint16_t* dst = g.yp + p * g.n_out + col0 + 16 * hi;
+                uint16_t* dst = (kDirect && dtok >= 0 ? g.out + (int64_t)dtok * g.n_out
+                                                      : g.yp + p * g.n_out) + col0 + 16 * hi;
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
                     uint4 o;
@@ -433,9 +486,9 @@ __device__ __forceinline__ void epilogue_fc2(const MxArgs& g, const MxItem& it,
 #endif
 constexpr bool kMxDeferCopies = FFN_MX_DEFER != 0;
 
-template <bool kFC1>
+template <bool kFC1, bool kDirect = false>
 __device__ __forceinline__ void mx_item(const MxArgs& g, const MxCtx& c, const MxItem& cur_in,
-                                        MxItem& nxt, uint8_t* smem) {
+                                        MxItem& nxt, uint8_t* smem, int dbuf) {
     const MxItem cur = uniform_item(cur_in);
     constexpr int kDecodeSteps = 4;
     nxt.j = cur.j;
@@ -499,18 +552,23 @@ __device__ __forceinline__ void mx_item(const MxArgs& g, const MxCtx& c, const M
     // them: the next item's first wait (for all but the last (stages - 1) slices' copies) then
     // covers slice 0 and the stores, not the slices behind them
     issue_prologue(g, c, nxt, 0, 1);
+    if constexpr (kDirect) {
+        const MxItem nu = uniform_item(nxt);
+        if (nu.it >= 0) issue_dir_copy(g, c, nu, dbuf ^ 1);
+    }
 
     if (kFC1)
         epilogue_fc1(g, cur, acc, fh, tq, c.lane);
     else
-        epilogue_fc2(g, cur, acc, fh, tq, c.lane);
+        epilogue_fc2<kDirect>(g, cur, acc, fh, tq, c.lane, dbuf);
     issue_prologue(g, c, nxt, 1, kStages);
 }
 
 // Persistent grouped GEMM, one workgroup per CU (150 KB of LDS).
-template <bool kFC1>
+template <bool kFC1, bool kDirect = false>
 __global__ void __launch_bounds__(kThreads, 1)
 ffn_mx_kernel(MxArgs g) {
+    static_assert(!kDirect || !kFC1, "direct rows are an FC2 epilogue");
     __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM_BYTES];
     MxCtx c;
     c.tid = threadIdx.x;
@@ -537,10 +595,16 @@ ffn_mx_kernel(MxArgs g) {
         decode_step<kFC1>(s, cur, g, c);
     }
     issue_prologue(g, c, cur);
+    int dbuf = 0;  // direct rows: the mx_dir buffer of the current item
+    if constexpr (kDirect) {
+        const MxItem u = uniform_item(cur);
+        if (u.it >= 0) issue_dir_copy(g, c, u, 0);
+    }
     for (;;) {
         if (__builtin_amdgcn_readfirstlane(cur.it) < 0) break;
         MxItem nxt;
-        mx_item<kFC1>(g, c, cur, nxt, smem);
+        mx_item<kFC1, kDirect>(g, c, cur, nxt, smem, dbuf);
+        dbuf ^= 1;
         cur = nxt;
     }
 }
@@ -587,7 +651,8 @@ hipError_t moe_launch_ffn_mx_fc1(const uint8_t* xq, const uint8_t* xs, const int
 
 hipError_t moe_launch_ffn_mx_fc2(const uint8_t* actq, const uint8_t* acts, const uint8_t* w2q,
                                  const uint8_t* w2s, int H, int I, int max_blocks, int32_t* ws,
-                                 uint16_t* yp, int64_t max_rows, hipStream_t stream) {
+                                 uint16_t* yp, int64_t max_rows, hipStream_t stream,
+                                 const int32_t* dir, void* out, int T) {
     MxArgs g{};
     g.aq = actq;
     g.as = acts;
@@ -605,6 +670,12 @@ hipError_t moe_launch_ffn_mx_fc2(const uint8_t* actq, const uint8_t* acts, const
     g.tiles = ws + WS_HEAD + max_blocks;
     g.NT = (H + 255) / 256;
     g.ntiles = ws + WS_NTILES;
-    ffn_mx_kernel<false><<<mx_grid(), kThreads, 0, stream>>>(g);
+    g.dir = dir;
+    g.out = static_cast<uint16_t*>(out);
+    g.T = T;
+    if (dir)
+        ffn_mx_kernel<false, true><<<mx_grid(), kThreads, 0, stream>>>(g);
+    else
+        ffn_mx_kernel<false><<<mx_grid(), kThreads, 0, stream>>>(g);
     return hipGetLastError();
 }

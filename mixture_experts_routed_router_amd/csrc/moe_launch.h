@@ -54,7 +54,8 @@ hipError_t moe_launch_ffn_mx_fc1(const uint8_t* xq, const uint8_t* xs, const int
                                  hipStream_t stream);
 hipError_t moe_launch_ffn_mx_fc2(const uint8_t* actq, const uint8_t* acts, const uint8_t* w2q,
                                  const uint8_t* w2s, int H, int I, int max_blocks, int32_t* ws,
-                                 uint16_t* yp, int64_t max_rows, hipStream_t stream);
+                                 uint16_t* yp, int64_t max_rows, hipStream_t stream,
+                                 const int32_t* dir = nullptr, void* out = nullptr, int T = 0);
 inline int64_t moe_mx_scale_pitch_impl(int64_t cols) { return (cols / 32 + 3) / 4 * 4; }
 hipError_t moe_launch_mx_quantize(const void* src, moe_dtype_t dt, int64_t rows, int64_t cols,
                                   int fmt, uint8_t* codes, uint8_t* scales, hipStream_t stream);

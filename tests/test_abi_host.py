@@ -217,6 +217,15 @@ def test_direct_rows_reject(lib):
     assert fc2d(H=2880, I=100) == UNSUPPORTED               # bf16 needs multiples of 64
     assert fc2d(E_loc=300) == UNSUPPORTED
     assert fc2d(max_rows=1 << 27) == UNSUPPORTED            # 32-bit offsets into row_direct
+    mx = lambda actq=P[0], row_token=P[7], out=P[10], K=8, ws_elems=272: (
+        lib.moe_expert_ffn_mx_fc2_direct(actq, P[1], P[2], P[3], 128, 256, 8, P[4], P[5], 16,
+                                         P[6], 1024, row_token, P[8], P[9], 64, K, out, P[11],
+                                         P[12], ws_elems, NULL))
+    assert mx(actq=NULL) == INVALID
+    assert mx(row_token=NULL) == INVALID
+    assert mx(out=ctypes.c_void_p(0x1008)) == INVALID
+    assert mx(ws_elems=271) == INVALID
+    assert mx(K=17) == UNSUPPORTED
     multi = lib.moe_combine_multi
     assert multi(P[0], 1, P[1], P[2], 4, 100, 2, P[3], NULL) == INVALID  # 200-B rows
     assert multi(P[0], 1, P[1], NULL, 4, 128, 2, P[3], NULL) == INVALID

@@ -138,3 +138,66 @@ def test_direct_rows_graph_replay():
         torch.cuda.synchronize()
         assert torch.equal(layer.out, ref_out)
     del graph
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("share_of_64", dict(seed=31, T=1000, H=256, E=64, K=8, I=256, P=4, E_loc=8, begin=5,
+                         stride=8, block_m=32)),
+    ("k1_subset", dict(seed=32, T=700, H=128, E=32, K=1, I=128, P=2, E_loc=8, begin=0,
+                       stride=4, block_m=16)),
+    ("decode_subset", dict(seed=33, T=64, H=256, E=32, K=4, I=192, P=2, E_loc=8, begin=2,
+                           stride=4, block_m=16)),
+])
+def test_direct_rows_mx(name, kw):
+    """The MX down GEMM with direct rows (moe_expert_ffn_mx_fc2_direct) + moe_combine_multi:
+    out bit-identical to moe_expert_ffn_mx_fc2 + moe_combine on the same MXFP8 activation, the
+    row table as the host computes it, yp of the other tokens' rows unchanged."""
+    c = random_case(**kw)
+    _announce(f"mx {name} {kw}")
+    dev = "cuda"
+    layer = binding.RoutedExperts(c.T, c.H, c.E, c.K, c.I, c.P, dtype=c.dtype, E_loc=c.n_local,
+                                  expert_begin=c.begin, expert_stride=c.stride,
+                                  block_m=c.block_m, device=dev, precision="mx", direct=True)
+    logits = torch.from_numpy(c.logits).to(dev)
+    x = c.x.to(dev)
+    (w1q, w1s), (w2q, w2s) = binding.mx_quantize_weights(c.W1.to(dev), c.W2.to(dev))
+    layer.forward(logits, x, (w1q, w1s), (w2q, w2s))
+    yp2 = torch.zeros_like(layer.yp)
+    out2 = torch.zeros_like(layer.out)
+    binding.moe_expert_ffn_mx_fc2(layer.actq, layer.acts, w2q, w2s, layer.blocks, layer.n_blocks,
+                                  yp2, layer.ffn_workspace)
+    binding.moe_combine(yp2, layer.topk_w, layer.entry_pos, out2)
+    torch.cuda.synchronize()
+    assert torch.equal(layer.out, out2), "out: MX direct rows + combine_multi vs MX fc2 + combine"
+    T, K, max_rows = c.T, c.K, layer.max_rows
+    ep, rt = host(layer.entry_pos), host(layer.row_token)
+    tok, wbits, n_local = _host_direct_table(ep, rt, T, K, host(layer.topk_w), max_rows)
+    rd = host(layer.row_direct)
+    assert np.array_equal(rd[:max_rows], tok), "row table: tokens"
+    assert np.array_equal(rd[max_rows:][tok >= 0], wbits[tok >= 0]), "row table: weights"
+    rows = int(host(layer.offsets)[-1])
+    other = torch.from_numpy(np.nonzero((rt[:rows] >= 0) & (tok[:rows] < 0))[0]).to(dev)
+    assert torch.equal(layer.yp[other], yp2[other]), "yp rows of tokens with 0 or >= 2 entries"
+    print(dict(direct_tokens=int((n_local == 1).sum()), tokens=T))
+
+
+def test_direct_rows_mx_deepseek_v3_share():
+    """The MX path of the full-size DeepSeek-V3 share (skew 1) with direct rows: out bit-identical
+    to the plain MX down GEMM + combine on the same activation."""
+    c = workload_case("deepseek_v3_share", 1.0)
+    _announce("mx deepseek_v3_share s=1, full size")
+    dev = "cuda"
+    layer = binding.RoutedExperts(c.T, c.H, c.E, c.K, c.I, c.P, dtype=c.dtype, E_loc=c.n_local,
+                                  expert_begin=c.begin, expert_stride=c.stride,
+                                  block_m=c.block_m, device=dev, precision="mx", direct=True)
+    logits = torch.from_numpy(c.logits).to(dev)
+    x = c.x.to(dev)
+    (w1q, w1s), (w2q, w2s) = binding.mx_quantize_weights(c.W1.to(dev), c.W2.to(dev))
+    layer.forward(logits, x, (w1q, w1s), (w2q, w2s))
+    yp2 = torch.zeros_like(layer.yp)
+    out2 = torch.zeros_like(layer.out)
+    binding.moe_expert_ffn_mx_fc2(layer.actq, layer.acts, w2q, w2s, layer.blocks, layer.n_blocks,
+                                  yp2, layer.ffn_workspace)
+    binding.moe_combine(yp2, layer.topk_w, layer.entry_pos, out2)
+    torch.cuda.synchronize()
+    assert torch.equal(layer.out, out2)
