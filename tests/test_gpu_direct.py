@@ -201,3 +201,49 @@ def test_direct_rows_mx_deepseek_v3_share():
     binding.moe_combine(yp2, layer.topk_w, layer.entry_pos, out2)
     torch.cuda.synchronize()
     assert torch.equal(layer.out, out2)
+
+
+def test_direct_rows_partial_block_table():
+    """moe_expert_ffn_fc2_direct on a block table with every third block left out: covered rows
+    of one-entry tokens land in out (bit for bit the one-entry combine of the plain FC2's row),
+    the other covered rows in yp as the plain FC2 stores them, and nothing else is written."""
+    c = random_case(seed=31, T=1000, H=256, E=64, K=8, I=192, P=4, E_loc=8, begin=5, stride=8,
+                    block_m=32)
+    _announce("direct rows on a partial block table")
+    layer = run_gpu(c, direct=True)
+    _, _, W1, W2 = layer._inputs
+    nb = int(layer.n_blocks.item())
+    full = host(layer.blocks[:nb])
+    sub = np.ascontiguousarray(full[np.array([i % 3 != 2 for i in range(nb)])])
+    dev = layer.blocks.device
+    sub_buf = torch.zeros_like(layer.blocks)
+    sub_buf[: len(sub)] = torch.from_numpy(sub).to(dev)
+    n_sub = torch.tensor([len(sub)], dtype=torch.int32, device=dev)
+    act = torch.zeros_like(layer.act)
+    binding.moe_expert_ffn_fc1(layer.xp, W1, sub_buf, n_sub, act, layer.ffn_workspace)
+    yp_d, out_d = torch.zeros_like(layer.yp), torch.zeros_like(layer.out)
+    binding.moe_expert_ffn_fc2_direct(act, W2, sub_buf, n_sub, yp_d, layer.row_token,
+                                      layer.entry_pos, layer.topk_w, out_d, layer.row_direct,
+                                      layer.ffn_workspace)
+    yp_p = torch.zeros_like(layer.yp)
+    binding.moe_expert_ffn_fc2(act, W2, sub_buf, n_sub, yp_p, layer.ffn_workspace)
+    out_one = torch.zeros_like(layer.out)  # the one-entry combine of every plain row
+    binding.moe_combine(yp_p, layer.topk_w, layer.entry_pos, out_one)
+    torch.cuda.synchronize()
+    covered = np.zeros(layer.max_rows, bool)
+    for _, _, first, rows in sub:
+        covered[first:first + rows] = True
+    tok, _, _ = _host_direct_table(host(layer.entry_pos), host(layer.row_token), c.T, c.K,
+                                   host(layer.topk_w), layer.max_rows)
+    direct_rows = np.nonzero(covered & (tok >= 0))[0]
+    other_rows = np.nonzero(covered & (tok < 0))[0]
+    assert len(direct_rows) > 0 and len(other_rows) > 0
+    toks = torch.from_numpy(tok[direct_rows].astype(np.int64)).to(dev)
+    assert torch.equal(out_d[toks], out_one[toks]), "direct rows: out"
+    written = torch.zeros(c.T, dtype=torch.bool, device=dev)
+    written[toks] = True
+    assert not out_d[~written].any(), "out rows of other tokens untouched"
+    oth = torch.from_numpy(other_rows).to(dev)
+    assert torch.equal(yp_d[oth], yp_p[oth]), "other covered rows: yp"
+    mask = torch.from_numpy(covered & (tok < 0)).to(dev)
+    assert not yp_d[~mask].any(), "yp rows not stored by the call untouched"
